@@ -1,0 +1,116 @@
+"""Workload definitions and the seeded input generator.
+
+Recipe (one ``numpy.random.default_rng(seed)`` stream, seed = workload id
+unless given):
+
+1. for the packed varlen workload only: the sequence lengths,
+   ``integers(256, 8192, endpoint=True, size=64)``;
+2. Q ``[T, Hq, d]``, K ``[T, Hkv, d]``, V ``[T, Hkv, d]``, dO ``[T, Hq, d]``,
+   each ``standard_normal`` in float32, drawn in that order;
+3. the sink logits S ``[Hq]``, ``standard_normal`` float32.
+
+Tensors of a bf16 workload are rounded to bf16 (round to nearest even) on
+the host with torch; both the GPU and the oracle consume exactly those
+values.  The sinks always stay float32.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    wid: int
+    name: str
+    lengths: Sequence[int]
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    window: int  # 0 = unlimited (plain causal)
+    dtype: str  # "bf16" or "f32": the I/O type of q, k, v, o, dO, dQ, dK, dV
+
+    @property
+    def total_tokens(self) -> int:
+        return int(sum(self.lengths))
+
+    @property
+    def max_seqlen(self) -> int:
+        return int(max(self.lengths)) if len(self.lengths) else 0
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    def cu_seqlens(self) -> np.ndarray:
+        cu = np.zeros(len(self.lengths) + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(np.asarray(self.lengths, dtype=np.int64))
+        return cu
+
+    def visible_pairs(self) -> int:
+        """Number of (query, key) pairs with key visible, summed over q-heads."""
+        n = 0
+        for L in self.lengths:
+            L = int(L)
+            if self.window == 0 or self.window >= L:
+                n += L * (L + 1) // 2
+            else:
+                w = self.window
+                n += w * (w + 1) // 2 + (L - w) * w
+        return n * self.num_q_heads
+
+    def flops(self) -> Dict[str, float]:
+        """Algorithmic flops: 4d per visible pair forward, 10d backward."""
+        p = self.visible_pairs()
+        d = self.head_dim
+        return {"fwd": 4.0 * d * p, "bwd": 10.0 * d * p, "total": 14.0 * d * p}
+
+
+def _varlen_lengths(seed: int) -> np.ndarray:
+    return np.random.default_rng(seed).integers(256, 8192, endpoint=True, size=64)
+
+
+WORKLOADS: Dict[int, Workload] = {
+    1: Workload(1, "tiny_fp32_hq2_hkv1_d16_l64", (64,), 2, 1, 16, 0, "f32"),
+    2: Workload(2, "gptoss_hq64_hkv8_d64_l4096_causal", (4096,), 64, 8, 64, 0, "bf16"),
+    3: Workload(3, "gptoss_b2_l8192_window128", (8192, 8192), 64, 8, 64, 128, "bf16"),
+    4: Workload(4, "headshare_hq16_hkv2_d64_l65536", (65536,), 16, 2, 64, 0, "bf16"),
+    5: Workload(5, "varlen64_256to8192_hq64_hkv8_d64",
+                tuple(int(x) for x in _varlen_lengths(5)), 64, 8, 64, 0, "bf16"),
+}
+
+
+def workload(wid: int) -> Workload:
+    return WORKLOADS[wid]
+
+
+def custom_workload(lengths, hq, hkv, d, window=0, dtype="bf16", name="custom") -> Workload:
+    return Workload(0, name, tuple(int(x) for x in lengths), hq, hkv, d, window, dtype)
+
+
+def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Draw the seeded inputs of workload ``w`` as CPU torch tensors.
+
+    Returns q, k, v, dout (bf16 or float32 per ``w.dtype``), sinks (float32),
+    cu_seqlens (int32).  For the packed varlen workload the lengths drawn
+    here must equal ``w.lengths`` (they come from the same stream).
+    """
+    if seed is None:
+        seed = w.wid
+    rng = np.random.default_rng(seed)
+    if w.wid == 5:
+        lens = rng.integers(256, 8192, endpoint=True, size=64)
+        assert tuple(int(x) for x in lens) == tuple(w.lengths)
+    T, hq, hkv, d = w.total_tokens, w.num_q_heads, w.num_kv_heads, w.head_dim
+    out = {}
+    for name, shape in (("q", (T, hq, d)), ("k", (T, hkv, d)), ("v", (T, hkv, d)),
+                        ("dout", (T, hq, d))):
+        x = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32))
+        out[name] = x.to(torch.bfloat16) if w.dtype == "bf16" else x
+    out["sinks"] = torch.from_numpy(rng.standard_normal((hq,), dtype=np.float32))
+    out["cu_seqlens"] = torch.from_numpy(w.cu_seqlens())
+    return out
