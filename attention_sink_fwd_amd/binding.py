@@ -1,0 +1,138 @@
+"""Thin Python binding of the C ABI, same names as include/sink_attn.h.
+
+Argument marshalling only: torch supplies device memory and the current
+stream; every step of the computation runs in the HIP kernels of
+libsinkattn.so.  Outputs that are not passed in are allocated with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.bfloat16: _lib.SINK_ATTN_BF16, torch.float32: _lib.SINK_ATTN_F32}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def make_params(q: torch.Tensor, k: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                softmax_scale: Optional[float] = None, window: int = 0) -> _lib.SinkAttnParams:
+    """sink_attn_params for packed q [T, Hq, d], k [T, Hkv, d] and cu_seqlens."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q and k must be [total_tokens, heads, head_dim]")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    T, hq, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    p = _lib.SinkAttnParams()
+    p.cu_seqlens = cu_seqlens.data_ptr()
+    p.num_seqs = cu_seqlens.numel() - 1
+    p.max_seqlen = int(max_seqlen)
+    p.total_tokens = T
+    p.num_q_heads = hq
+    p.num_kv_heads = k.shape[1]
+    p.head_dim = d
+    p.softmax_scale = float(softmax_scale)
+    p.causal = 1
+    p.window = int(window)
+    p.dtype = _DTYPES[q.dtype]
+    return p
+
+
+def sink_attn_fwd(q, k, v, sinks, cu_seqlens, max_seqlen, softmax_scale=None, window=0,
+                  o=None, lse=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O [T, Hq, d] (dtype of q) and LSE [Hq, T] float32."""
+    lib = _lib.load()
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    _need(q, "q"); _need(k, "k", q.dtype, (T, hkv, d)); _need(v, "v", q.dtype, (T, hkv, d))
+    _need(sinks, "sinks", torch.float32, (hq,)); _need(cu_seqlens, "cu_seqlens", torch.int32)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((hq, T), dtype=torch.float32, device=q.device)
+    _need(o, "o", q.dtype, q.shape); _need(lse, "lse", torch.float32, (hq, T))
+    p = make_params(q, k, cu_seqlens, max_seqlen, softmax_scale, window)
+    _lib.check(lib.sink_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks),
+                                 _ptr(o), _ptr(lse), _stream(stream)))
+    return o, lse
+
+
+def sink_attn_bwd_workspace_size(q, k, cu_seqlens, max_seqlen, softmax_scale=None, window=0) -> int:
+    lib = _lib.load()
+    p = make_params(q, k, cu_seqlens, max_seqlen, softmax_scale, window)
+    return int(lib.sink_attn_bwd_workspace_size(ctypes.byref(p)))
+
+
+def sink_attn_bwd(q, k, v, sinks, o, lse, dout, cu_seqlens, max_seqlen, softmax_scale=None,
+                  window=0, dq=None, dk=None, dv=None, dsinks=None, workspace=None,
+                  stream=None):
+    """dQ, dK, dV (dtype of q) and dS [Hq] float32."""
+    lib = _lib.load()
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    _need(q, "q"); _need(k, "k", q.dtype, (T, hkv, d)); _need(v, "v", q.dtype, (T, hkv, d))
+    _need(o, "o", q.dtype, q.shape); _need(dout, "dout", q.dtype, q.shape)
+    _need(lse, "lse", torch.float32, (hq, T)); _need(sinks, "sinks", torch.float32, (hq,))
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dsinks = torch.empty_like(sinks) if dsinks is None else dsinks
+    _need(dq, "dq", q.dtype, q.shape); _need(dk, "dk", q.dtype, k.shape)
+    _need(dv, "dv", q.dtype, v.shape); _need(dsinks, "dsinks", torch.float32, (hq,))
+    p = make_params(q, k, cu_seqlens, max_seqlen, softmax_scale, window)
+    need = int(lib.sink_attn_bwd_workspace_size(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _lib.check(lib.sink_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(o),
+                                 _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)))
+    return dq, dk, dv, dsinks
+
+
+class _SinkAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, sinks, cu_seqlens, max_seqlen, softmax_scale, window):
+        o, lse = sink_attn_fwd(q, k, v, sinks, cu_seqlens, max_seqlen, softmax_scale, window)
+        ctx.save_for_backward(q, k, v, sinks, o, lse, cu_seqlens)
+        ctx.args = (max_seqlen, softmax_scale, window)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, sinks, o, lse, cu = ctx.saved_tensors
+        max_seqlen, scale, window = ctx.args
+        dq, dk, dv, ds = sink_attn_bwd(q, k, v, sinks, o, lse, do.contiguous(), cu, max_seqlen,
+                                       scale, window)
+        return dq, dk, dv, ds, None, None, None, None
+
+
+def sink_attention(q, k, v, sinks, cu_seqlens, max_seqlen, softmax_scale=None, window=0):
+    """Differentiable packed sink attention: O with gradients for q, k, v and sinks."""
+    return _SinkAttention.apply(q, k, v, sinks, cu_seqlens, max_seqlen, softmax_scale, window)

@@ -1,0 +1,199 @@
+// C ABI of libsinkattn.so: argument validation, workspace carving and kernel
+// dispatch.  Declarations and the full contract are in include/sink_attn.h.
+#include "sink_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+thread_local hipEvent_t g_bwd_events[4] = {nullptr, nullptr, nullptr, nullptr};
+thread_local bool g_bwd_events_on = false;
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_params(const sink_attn_params* p) {
+  if (!p) return fail(SINK_ATTN_ERR_INVALID_ARG, "params is NULL");
+  if (p->num_seqs < 1) return fail(SINK_ATTN_ERR_INVALID_ARG, "num_seqs must be >= 1 (got %d)", p->num_seqs);
+  if (p->num_seqs > 65535) return fail(SINK_ATTN_ERR_UNSUPPORTED, "num_seqs > 65535 (got %d)", p->num_seqs);
+  if (p->total_tokens < 0) return fail(SINK_ATTN_ERR_INVALID_ARG, "total_tokens < 0");
+  if (p->max_seqlen < 0) return fail(SINK_ATTN_ERR_INVALID_ARG, "max_seqlen < 0");
+  if (p->total_tokens > 0 && p->max_seqlen < 1)
+    return fail(SINK_ATTN_ERR_INVALID_ARG, "max_seqlen must be >= 1 when total_tokens > 0");
+  if (p->num_q_heads < 1 || p->num_kv_heads < 1)
+    return fail(SINK_ATTN_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return fail(SINK_ATTN_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                p->num_q_heads, p->num_kv_heads);
+  if (p->num_q_heads > 65535) return fail(SINK_ATTN_ERR_UNSUPPORTED, "num_q_heads > 65535");
+  if (p->head_dim < 8 || p->head_dim % 8 != 0)
+    return fail(SINK_ATTN_ERR_INVALID_ARG, "head_dim must be a positive multiple of 8 (got %d)", p->head_dim);
+  if (p->head_dim > 64) return fail(SINK_ATTN_ERR_UNSUPPORTED, "head_dim > 64 is not built (got %d)", p->head_dim);
+  if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.0f))
+    return fail(SINK_ATTN_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (p->causal != 1) return fail(SINK_ATTN_ERR_UNSUPPORTED, "only causal attention is built (causal must be 1)");
+  if (p->window < 0) return fail(SINK_ATTN_ERR_INVALID_ARG, "window must be >= 0 (got %d)", p->window);
+  if (p->dtype != SINK_ATTN_BF16 && p->dtype != SINK_ATTN_F32)
+    return fail(SINK_ATTN_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+  if (!p->cu_seqlens) return fail(SINK_ATTN_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  return SINK_ATTN_OK;
+}
+
+int check_tensor(const void* t, const char* name) {
+  if (!t) return fail(SINK_ATTN_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(t)) return fail(SINK_ATTN_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return SINK_ATTN_OK;
+}
+
+// Optional host-side check of cu_seqlens (SINK_ATTN_VALIDATE=1); synchronises.
+int maybe_validate_cu(const sink_attn_params* p, hipStream_t stream) {
+  const char* env = std::getenv("SINK_ATTN_VALIDATE");
+  if (!env || env[0] != '1') return SINK_ATTN_OK;
+  std::vector<int32_t> cu(p->num_seqs + 1);
+  hipError_t e = hipMemcpyAsync(cu.data(), p->cu_seqlens, cu.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "reading cu_seqlens: %s", hipGetErrorString(e));
+  if (cu[0] != 0) return fail(SINK_ATTN_ERR_INVALID_ARG, "cu_seqlens[0] = %d, must be 0", cu[0]);
+  for (int s = 0; s < p->num_seqs; ++s) {
+    const int len = cu[s + 1] - cu[s];
+    if (len < 0) return fail(SINK_ATTN_ERR_INVALID_ARG, "cu_seqlens decreases at %d", s);
+    if (len > p->max_seqlen)
+      return fail(SINK_ATTN_ERR_INVALID_ARG, "sequence %d has length %d > max_seqlen %d", s, len, p->max_seqlen);
+  }
+  if (cu[p->num_seqs] != p->total_tokens)
+    return fail(SINK_ATTN_ERR_INVALID_ARG, "cu_seqlens[num_seqs] = %d != total_tokens %d", cu[p->num_seqs],
+                p->total_tokens);
+  return SINK_ATTN_OK;
+}
+
+#define SA_CHECK(expr)             \
+  do {                             \
+    int _st = (expr);              \
+    if (_st != SINK_ATTN_OK) return _st; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int sink_attn_fwd(const sink_attn_params* p, const void* q, const void* k, const void* v, const float* sinks,
+                  void* o, float* lse, void* stream) {
+  g_last_error[0] = '\0';
+  SA_CHECK(check_params(p));
+  if (p->total_tokens == 0) return SINK_ATTN_OK;  // nothing to read or write
+  SA_CHECK(check_tensor(q, "q"));
+  SA_CHECK(check_tensor(k, "k"));
+  SA_CHECK(check_tensor(v, "v"));
+  SA_CHECK(check_tensor(o, "o"));
+  if (!sinks) return fail(SINK_ATTN_ERR_INVALID_ARG, "sinks is NULL");
+  if (!lse) return fail(SINK_ATTN_ERR_INVALID_ARG, "lse is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SA_CHECK(maybe_validate_cu(p, s));
+
+  sinkattn::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.sinks = sinks; a.o = o; a.lse = lse;
+  a.cu_seqlens = p->cu_seqlens;
+  a.num_q_heads = p->num_q_heads; a.num_kv_heads = p->num_kv_heads; a.head_dim = p->head_dim;
+  a.total_tokens = p->total_tokens; a.window = p->window;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  hipError_t e = sinkattn::launch_fwd(a, p->dtype, p->max_seqlen, p->num_seqs, s);
+  if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+  return SINK_ATTN_OK;
+}
+
+size_t sink_attn_bwd_workspace_size(const sink_attn_params* p) {
+  if (check_params(p) != SINK_ATTN_OK) return 0;
+  return sinkattn::bwd_workspace_layout(p->total_tokens, p->num_q_heads, p->num_kv_heads, p->head_dim).total;
+}
+
+int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const void* v, const float* sinks,
+                  const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, float* dsinks,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  SA_CHECK(check_params(p));
+  if (p->total_tokens > 0) {  // with no tokens only dsinks is written (zeros)
+    SA_CHECK(check_tensor(q, "q"));
+    SA_CHECK(check_tensor(k, "k"));
+    SA_CHECK(check_tensor(v, "v"));
+    SA_CHECK(check_tensor(o, "o"));
+    SA_CHECK(check_tensor(dout, "dout"));
+    SA_CHECK(check_tensor(dq, "dq"));
+    SA_CHECK(check_tensor(dk, "dk"));
+    SA_CHECK(check_tensor(dv, "dv"));
+    if (!sinks) return fail(SINK_ATTN_ERR_INVALID_ARG, "sinks is NULL");
+    if (!lse) return fail(SINK_ATTN_ERR_INVALID_ARG, "lse is NULL");
+  }
+  if (!dsinks) return fail(SINK_ATTN_ERR_INVALID_ARG, "dsinks is NULL");
+  const sinkattn::BwdWorkspace ws =
+      sinkattn::bwd_workspace_layout(p->total_tokens, p->num_q_heads, p->num_kv_heads, p->head_dim);
+  if (workspace_bytes < ws.total)
+    return fail(SINK_ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, ws.total);
+  if (ws.total > 0 && !workspace) return fail(SINK_ATTN_ERR_INVALID_ARG, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SINK_ATTN_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SA_CHECK(maybe_validate_cu(p, s));
+
+  char* wsb = static_cast<char*>(workspace);
+  sinkattn::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.sinks = sinks;
+  a.cu_seqlens = p->cu_seqlens;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dsinks = dsinks;
+  a.delta = reinterpret_cast<float*>(wsb);
+  a.dq_acc = reinterpret_cast<float*>(wsb + ws.delta);
+  a.dk_acc = reinterpret_cast<float*>(wsb + ws.delta + ws.dq_acc);
+  a.dv_acc = reinterpret_cast<float*>(wsb + ws.delta + ws.dq_acc + ws.dk_acc);
+  a.num_q_heads = p->num_q_heads; a.num_kv_heads = p->num_kv_heads; a.head_dim = p->head_dim;
+  a.total_tokens = p->total_tokens; a.window = p->window;
+  a.scale = p->softmax_scale;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  hipError_t e = sinkattn::launch_bwd(a, p->dtype, p->max_seqlen, p->num_seqs, s,
+                                       g_bwd_events_on ? g_bwd_events : nullptr);
+  if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+  return SINK_ATTN_OK;
+}
+
+int sink_attn_set_bwd_events(void* const* events) {
+  g_last_error[0] = '\0';
+  if (!events) {
+    g_bwd_events_on = false;
+    return SINK_ATTN_OK;
+  }
+  for (int i = 0; i < 4; ++i)
+    if (!events[i]) return fail(SINK_ATTN_ERR_INVALID_ARG, "events[%d] is NULL", i);
+  for (int i = 0; i < 4; ++i) g_bwd_events[i] = static_cast<hipEvent_t>(events[i]);
+  g_bwd_events_on = true;
+  return SINK_ATTN_OK;
+}
+
+const char* sink_attn_status_string(int status) {
+  switch (status) {
+    case SINK_ATTN_OK: return "ok";
+    case SINK_ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case SINK_ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SINK_ATTN_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case SINK_ATTN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* sink_attn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

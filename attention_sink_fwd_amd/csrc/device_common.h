@@ -1,0 +1,101 @@
+// Device-side helpers shared by the sink-attention kernels (gfx950 only).
+//
+// Matrix-core conventions used throughout (v_mfma_f32_32x32x16_bf16, one
+// 64-lane wavefront):
+//   A operand (M x K): lane l holds A[l % 32][8 * (l / 32) + s], s = 0..7
+//   B operand (K x N): lane l holds B[8 * (l / 32) + s][l % 32]
+//   C/D (M x N, 16 floats): lane l, register r holds
+//                           C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32]
+// So both operands carry 8 consecutive contraction indices per lane, the
+// output keeps its column index on the lane and its row index in registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sinkattn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+#define SA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8 zero8() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (bf16)0.0f;
+  return z;
+}
+
+// 8 consecutive elements from global memory as bf16 (float input is rounded
+// to nearest even).  p must be 16-byte aligned for bf16, 32-byte for float
+// rows whose offset is a multiple of 8 elements (true for head_dim % 8 == 0).
+__device__ __forceinline__ bf16x8 load8(const bf16* p) { return *(const bf16x8*)p; }
+__device__ __forceinline__ bf16x8 load8(const float* p) {
+  f32x4 a = *(const f32x4*)p;
+  f32x4 b = *(const f32x4*)(p + 4);
+  f32x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_convertvector(v, bf16x8);
+}
+
+// 8 consecutive elements as float (for row reductions over the input type).
+__device__ __forceinline__ f32x8 load8f(const bf16* p) {
+  return __builtin_convertvector(*(const bf16x8*)p, f32x8);
+}
+__device__ __forceinline__ f32x8 load8f(const float* p) {
+  f32x4 a = *(const f32x4*)p;
+  f32x4 b = *(const f32x4*)(p + 4);
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Store 4 consecutive floats in the output type.
+__device__ __forceinline__ void store4(bf16* p, f32x4 v) {
+  *(bf16x4*)p = __builtin_convertvector(v, bf16x4);
+}
+__device__ __forceinline__ void store4(float* p, f32x4 v) { *(f32x4*)p = v; }
+
+// Operand fragment (8 consecutive contraction indices k for lane index n)
+// from a row-major LDS tile X[k][n] whose n index is contiguous, row stride
+// `ld` elements: lane l receives X[k0 + 8*(l/32) + s][n0 + l%32], s = 0..7.
+// Uses two transposing LDS reads (ds_read_b64_tr_b16).  Within each group of
+// 16 lanes that instruction hands lane i element (i % 4) of the 4-element
+// row that lane 4*e + i/4 addressed, as its element e; lane j of the group
+// therefore addresses row k = 4*r + j/4 (r = read index) at column 4*(j%4).
+__device__ __forceinline__ bf16x8 frag_tr(const bf16* X, int ld, int k0, int n0, int lane) {
+  const int G = lane >> 4, j = lane & 15;
+  const bf16* p = X + (k0 + 8 * (G >> 1) + (j >> 2)) * ld + n0 + 16 * (G & 1) + 4 * (j & 3);
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS i16x4*)(p));
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS i16x4*)(p + 4 * ld));
+  i16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// Row permutation applied to the A operand rows of a score product so that
+// output register r of lane-half h holds row 16*(r/8) + 8*h + r%8: swap bits
+// 2 and 3 of the row index (an involution).
+__device__ __forceinline__ int row_perm(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+}  // namespace sinkattn

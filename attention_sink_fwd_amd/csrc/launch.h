@@ -1,0 +1,54 @@
+// Internal interface between the C-ABI host code and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sinkattn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* sinks;
+  void* o;
+  float* lse;
+  const int32_t* cu_seqlens;
+  int num_q_heads, num_kv_heads, head_dim, total_tokens, window;
+  float scale_log2;  // softmax_scale * log2(e)
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  const float* sinks;
+  const int32_t* cu_seqlens;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsinks;
+  float* delta;   // workspace: D_i = dO_i . O_i, [Hq, T]
+  float* dq_acc;  // workspace: float dQ accumulator, [T, Hq, d]
+  float* dk_acc;  // workspace: float dK accumulator, [T, Hkv, d]
+  float* dv_acc;  // workspace: float dV accumulator, [T, Hkv, d]
+  int num_q_heads, num_kv_heads, head_dim, total_tokens, window;
+  float scale;
+  float scale_log2;
+};
+
+// Workspace sections (bytes, each rounded up to 256).
+struct BwdWorkspace {
+  size_t delta, dq_acc, dk_acc, dv_acc, total;
+};
+BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d);
+
+hipError_t launch_fwd(const FwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s);
+// events: NULL, or four events recorded around the three kernels.
+hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s,
+                      const hipEvent_t* events);
+
+}  // namespace sinkattn

@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Sink-attention forward + backward throughput on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input already
+resident in HBM: host dispatch, the forward kernel (O, LSE), then the
+backward (D_i preprocess, main backward kernel, epilogue with dS_h).
+Default workload: GPT-OSS-20B-shaped attention, B=1, Hq=64, Hkv=8, d=64,
+L=4096, causal, bf16.
+
+Prints ONE JSON line.  Throughput counts algorithmic flops (14*d per visible
+query/key pair per query head: 4d forward, 10d backward).  The roofline
+object is for the dominant kernel (the main backward kernel), timed live
+with HIP events recorded around it on the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sink-attn fwd+bwd TFLOP/s + % bf16 MFMA peak, Hq64/Hkv8/d64 L=4096 causal"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_traffic.json")
+BWD_SOURCE = os.path.join(ROOT, "attention_sink_fwd_amd", "csrc", "bwd_kernels.hip")
+
+
+class Hip:
+    """The few HIP runtime calls the timing needs (same runtime torch uses)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        vp = ctypes.c_void_p
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(vp)]
+        self.lib.hipEventRecord.argtypes = [vp, vp]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        self.lib.hipEventDestroy.argtypes = [vp]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, stream) == 0
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return float(out.value)
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+def traffic_for_current_kernel():
+    """HBM bytes per launch of the main backward kernel from rocprofv3 counters.
+
+    Taken from profiles/bwd_main_traffic.json, and only while the kernel
+    source is the one the counters were measured on; otherwise None.
+    """
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(BWD_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if t.get("source_sha256") != sha:
+            return None
+        return float(t["bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(inp, w):
+    """The oracle (unchanged) on one KV group of the same workload, timed on the host."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = None
+    grp = w.num_q_heads // w.num_kv_heads
+    heads = list(range(grp))
+    t0 = time.perf_counter()
+    oracle.forward(inp["q"], inp["k"], inp["v"], inp["sinks"], inp["cu_seqlens"],
+                   w.softmax_scale, w.window, heads=heads)
+    oracle.backward(inp["q"], inp["k"], inp["v"], inp["sinks"], inp["dout"], inp["cu_seqlens"],
+                    w.softmax_scale, w.window, kv_heads=[0])
+    dt = time.perf_counter() - t0
+    flops = w.flops()["total"] * grp / w.num_q_heads
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads if threads is not None else os.cpu_count(),
+        "kind": "oracle",
+        "sample": (f"KV group 0 (query heads 0-{grp - 1}) of {w.name}: float64 forward + "
+                   f"backward, {flops / 1e9:.2f} GFLOP in {dt:.1f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="workload id 1-5 (default 2)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: --gpus {args.gpus} (WORLD_SIZE={world}) requested, but this build runs "
+              "on one GPU only: the kernel works on one GPU's head share and there is no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import attention_sink_fwd_amd as sa
+    from attention_sink_fwd_amd import _lib
+    from synthetic.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(w)
+    d = {k: v.to(dev) for k, v in inp.items()}
+    q, k, v, s, cu, do = d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens"], d["dout"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.num_q_heads, w.total_tokens), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ds = torch.empty_like(s)
+    ws_bytes = sa.sink_attn_bwd_workspace_size(q, k, cu, w.max_seqlen, w.softmax_scale, w.window)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    lib = _lib.load()
+    hip = Hip()
+
+    def step():
+        sa.sink_attn_fwd(q, k, v, s, cu, w.max_seqlen, w.softmax_scale, w.window, o=o, lse=lse,
+                         stream=stream)
+        sa.sink_attn_bwd(q, k, v, s, o, lse, do, cu, w.max_seqlen, w.softmax_scale, w.window,
+                         dq=dq, dk=dk, dv=dv, dsinks=ds, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    evs = [[hip.event() for _ in range(6)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        e = evs[i]
+        hip.record(e[0], sh)
+        sa.sink_attn_fwd(q, k, v, s, cu, w.max_seqlen, w.softmax_scale, w.window, o=o, lse=lse,
+                         stream=stream)
+        hip.record(e[1], sh)
+        arr = (ctypes.c_void_p * 4)(e[2].value, e[3].value, e[4].value, e[5].value)
+        _lib.check(lib.sink_attn_set_bwd_events(arr))
+        sa.sink_attn_bwd(q, k, v, s, o, lse, do, cu, w.max_seqlen, w.softmax_scale, w.window,
+                         dq=dq, dk=dk, dv=dv, dsinks=ds, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    _lib.check(lib.sink_attn_set_bwd_events(None))
+
+    def avg(a, b):
+        return sum(hip.ms(evs[i][a], evs[i][b]) for i in range(K)) / K
+
+    k_fwd, k_pre, k_main, k_post = avg(0, 1), avg(2, 3), avg(3, 4), avg(4, 5)
+    for row in evs:
+        for e in row:
+            hip.destroy(e)
+
+    ms = (t1 - t0) * 1000.0 / K
+    fl = w.flops()
+    tflops = fl["total"] / (ms * 1e-3) / 1e12
+    main_tflops = fl["bwd"] / (k_main * 1e-3) / 1e12
+    traffic = traffic_for_current_kernel()
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": len(w.lengths),
+            "seq_len": w.max_seqlen,
+            "total_tokens": w.total_tokens,
+            "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "window": w.window,
+            "causal": True,
+            "flops_per_step": fl["total"],
+        },
+        "pct_bf16_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "kernel_ms": {"fwd": round(k_fwd, 4), "bwd_pre": round(k_pre, 4),
+                      "bwd_main": round(k_main, 4), "bwd_post": round(k_post, 4)},
+        "roofline": {
+            "kernel": "bwd_main_kernel",
+            "bound": "mfma",
+            "achieved": round(main_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+/*
+ * sink_attn.h -- C ABI of libsinkattn.so: causal grouped-query attention with
+ * one learnable sink logit per query head, forward and backward, on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation.  "GPT-OSS Agentic RL Training: A Practical Retrospective",
+ * section "The Role of Attention Sinks": each head owns one learnable scalar
+ * S_h that acts as a virtual token inside the softmax, so a query can put
+ * attention mass on no real token.  Section "Implementation in FlashAttention
+ * v3" of the same page asks for a forward pass with sinks and a backward pass
+ * that also returns dL/dS_h.  Written out (the page prints no formula; this
+ * is the plain reading):
+ *
+ *   x_ij   = scale * q_i . k_j                 for keys j visible to query i
+ *   LSE_i  = ln( exp(S_h) + sum_j exp(x_ij) )  (natural log, includes the sink)
+ *   O_i    = sum_j exp(x_ij - LSE_i) v_j        (the sink has no value vector)
+ *   dS_h   = - sum_i exp(S_h - LSE_i) * (dO_i . O_i)   over all rows of all
+ *            sequences
+ *   dQ, dK, dV: the usual softmax-attention gradients of the same O.
+ *
+ * Key j is visible to query i (positions local to their sequence) iff
+ * j <= i and, when window > 0, i - window < j.  Query head h reads KV head
+ * h / (num_q_heads / num_kv_heads).  The sink is always visible and takes no
+ * key/value slot.
+ *
+ * Varlen packing.  Sequences are packed back to back along the token axis and
+ * described by cu_seqlens (prefix sums of the lengths), the interface style
+ * of FlashAttention's varlen functions ("Verl+FSDP Attention Sink" write-up,
+ * section 5.2).  A batch of B sequences of length L is cu_seqlens =
+ * {0, L, 2L, ..., B*L}.
+ *
+ * Layouts (all contiguous, row-major; T = total_tokens, d = head_dim):
+ *   q, o, dout, dq   [T, num_q_heads, d]
+ *   k, v, dk, dv     [T, num_kv_heads, d]
+ *   lse              float [num_q_heads, T]
+ *   sinks, dsinks    float [num_q_heads]
+ *   cu_seqlens       int32 [num_seqs + 1], device memory
+ * Every tensor pointer is a DEVICE pointer except `p` itself (host).  Tensor
+ * base addresses must be 16-byte aligned.  The element type of q, k, v, o,
+ * dout, dq, dk, dv is params.dtype; lse, sinks and dsinks are always float.
+ *
+ * Ownership.  The caller allocates and frees everything, including the
+ * backward workspace.  The library keeps no pointer after a call returns.
+ *
+ * Errors.  Every entry point returns a sink_attn_status.  An argument error
+ * is detected on the host before anything is enqueued, so nothing runs and no
+ * output is touched.  SINK_ATTN_ERR_HIP means a launch failed; the text of the
+ * failure is in sink_attn_last_error().  Faults inside a kernel surface at the
+ * caller's next synchronisation, as with any asynchronous HIP work.
+ * cu_seqlens lives on the device and is NOT read by the host: it must be
+ * non-decreasing, start at 0, end at total_tokens, and no length may exceed
+ * max_seqlen (set SINK_ATTN_VALIDATE=1 to have the host copy and check it,
+ * which synchronises the stream).
+ *
+ * Streams.  All work is enqueued on `stream` (a hipStream_t; NULL is the
+ * default stream) and is asynchronous.  Entry points are thread-safe.
+ */
+#ifndef SINK_ATTN_H
+#define SINK_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SINK_ATTN_OK = 0,
+  SINK_ATTN_ERR_INVALID_ARG = 1,       /* null pointer, bad size or shape */
+  SINK_ATTN_ERR_UNSUPPORTED = 2,       /* valid request this build does not implement */
+  SINK_ATTN_ERR_WORKSPACE_TOO_SMALL = 3,
+  SINK_ATTN_ERR_HIP = 4                /* a HIP runtime call or launch failed */
+} sink_attn_status;
+
+typedef enum {
+  SINK_ATTN_BF16 = 0, /* bfloat16 I/O; bf16 matrix-core products, float accumulation */
+  SINK_ATTN_F32 = 1   /* float I/O; operands are rounded to bf16 (nearest even) for
+                         the matrix-core products, accumulation and softmax in float */
+} sink_attn_dtype;
+
+typedef struct {
+  const int32_t *cu_seqlens; /* device, [num_seqs + 1] */
+  int32_t num_seqs;          /* >= 1 */
+  int32_t max_seqlen;        /* >= every sequence length; 0 allowed only if total_tokens == 0 */
+  int32_t total_tokens;      /* T = cu_seqlens[num_seqs] */
+  int32_t num_q_heads;       /* Hq >= 1 */
+  int32_t num_kv_heads;      /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;          /* d: a multiple of 8 in [8, 64] */
+  float softmax_scale;       /* tau > 0, finite; usually 1/sqrt(d) */
+  int32_t causal;            /* must be 1 (keys after the query are never visible) */
+  int32_t window;            /* 0 = unlimited; else key j visible iff i - window < j <= i */
+  int32_t dtype;             /* sink_attn_dtype */
+} sink_attn_params;
+
+/*
+ * Forward pass: O and LSE.
+ *   q     [T, Hq, d]  dtype     in
+ *   k, v  [T, Hkv, d] dtype     in
+ *   sinks [Hq]        float     in   S_h; -INFINITY is allowed and gives plain
+ *                                    causal attention; +INF and NaN are not.
+ *   o     [T, Hq, d]  dtype     out  overwritten
+ *   lse   [Hq, T]     float     out  overwritten, natural log, includes the sink
+ * Reference: "GPT-OSS Agentic RL Training: A Practical Retrospective",
+ * sections "The Role of Attention Sinks" and "Implementation in FlashAttention
+ * v3" (the forward pass with sinks).
+ */
+int sink_attn_fwd(const sink_attn_params *p, const void *q, const void *k, const void *v,
+                  const float *sinks, void *o, float *lse, void *stream);
+
+/*
+ * Bytes of device workspace sink_attn_bwd needs for these parameters
+ * (float row statistics and float gradient accumulators, 256-byte aligned
+ * sections).  Returns 0 when the parameters are invalid.
+ */
+size_t sink_attn_bwd_workspace_size(const sink_attn_params *p);
+
+/*
+ * Backward pass: dQ, dK, dV and dS.
+ *   q, k, v, sinks            the forward inputs
+ *   o, lse                    the forward outputs for exactly these inputs
+ *   dout  [T, Hq, d]  dtype   in   dL/dO
+ *   dq    [T, Hq, d]  dtype   out  overwritten
+ *   dk,dv [T, Hkv, d] dtype   out  overwritten (summed over each KV group)
+ *   dsinks [Hq]       float   out  overwritten: dL/dS_h summed over all rows
+ *                                  of all sequences
+ *   workspace, workspace_bytes     device scratch of at least
+ *                                  sink_attn_bwd_workspace_size(p) bytes,
+ *                                  256-byte aligned; contents on entry are
+ *                                  ignored and on exit unspecified.
+ * LSE is treated as a saved statistic, not an output: no gradient flows into
+ * it.  Float atomics accumulate dQ, dK, dV and dS, so the last bits may vary
+ * from run to run.
+ * Reference: "GPT-OSS Agentic RL Training: A Practical Retrospective",
+ * section "Implementation in FlashAttention v3" (the backward pass that
+ * computes the sink gradient dL/dS_h).
+ */
+int sink_attn_bwd(const sink_attn_params *p, const void *q, const void *k, const void *v,
+                  const float *sinks, const void *o, const float *lse, const void *dout,
+                  void *dq, void *dk, void *dv, float *dsinks, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/*
+ * Instrumentation (benchmarks and profilers).  Sets, for the calling thread,
+ * four hipEvent_t handles that every later sink_attn_bwd call on this thread
+ * records on its stream: events[0] before the preprocess kernel, events[1]
+ * before the main kernel, events[2] before the epilogue kernel and events[3]
+ * after it, so hipEventElapsedTime(events[1], events[2]) is the main
+ * kernel's duration.  The four handles are copied; the caller keeps owning
+ * the events.  Pass NULL to stop recording.  Returns SINK_ATTN_OK, or
+ * SINK_ATTN_ERR_INVALID_ARG if one of the four handles is NULL.
+ */
+int sink_attn_set_bwd_events(void *const *events);
+
+/* Static English text for a status code (never NULL). */
+const char *sink_attn_status_string(int status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char *sink_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINK_ATTN_H */

@@ -114,7 +114,7 @@ def forward(q, k, v, sinks, cu_seqlens, scale, window=0, heads=None, row_block=2
         L = e - b
         for h in heads:
             g = kv_head_of(h, hq, hkv)
-            qh, kg, vg = q[b:e, h], k[b:e, g], v[b:e, g]
+            qh, kg, vg = (np.ascontiguousarray(x) for x in (q[b:e, h], k[b:e, g], v[b:e, g]))
             for r0 in range(0, L, row_block):
                 rows = np.arange(r0, min(L, r0 + row_block))
                 p, _, l, klo = _row_probabilities(qh, kg, sinks[h], rows, scale, window)
@@ -129,12 +129,12 @@ def forward_rows(q, k, v, sinks, cu_seqlens, scale, window, seq, head, rows):
     cu = _i64(cu_seqlens)
     b, e = int(cu[seq]), int(cu[seq + 1])
     g = kv_head_of(head, q.shape[1], k.shape[1])
+    qh, kg, vg = (np.ascontiguousarray(x) for x in (q[b:e, head], k[b:e, g], v[b:e, g]))
     o = np.zeros((len(rows), q.shape[2]))
     lse = np.zeros(len(rows))
     for n, i in enumerate(rows):
-        p, _, l, klo = _row_probabilities(q[b:e, head], k[b:e, g], sinks[head],
-                                          np.array([i]), scale, window)
-        o[n] = p[0] @ v[b + klo:b + klo + p.shape[1], g]
+        p, _, l, klo = _row_probabilities(qh, kg, sinks[head], np.array([i]), scale, window)
+        o[n] = p[0] @ vg[klo:klo + p.shape[1]]
         lse[n] = l[0]
     return o, lse
 
@@ -160,9 +160,9 @@ def backward(q, k, v, sinks, dout, cu_seqlens, scale, window=0, kv_heads=None,
         b, e = int(cu[s]), int(cu[s + 1])
         L = e - b
         for g in kv_heads:
-            kg, vg = k[b:e, g], v[b:e, g]
+            kg, vg = np.ascontiguousarray(k[b:e, g]), np.ascontiguousarray(v[b:e, g])
             for h in range(g * group, (g + 1) * group):
-                qh, doh = q[b:e, h], dout[b:e, h]
+                qh, doh = np.ascontiguousarray(q[b:e, h]), np.ascontiguousarray(dout[b:e, h])
                 for r0 in range(0, L, row_block):
                     rows = np.arange(r0, min(L, r0 + row_block))
                     p, p_sink, _, klo = _row_probabilities(qh, kg, sinks[h], rows,
@@ -185,15 +185,15 @@ def backward_rows(q, k, v, sinks, dout, cu_seqlens, scale, window, seq, head, ro
     cu = _i64(cu_seqlens)
     b, e = int(cu[seq]), int(cu[seq + 1])
     g = kv_head_of(head, q.shape[1], k.shape[1])
+    qh, kg, vg = (np.ascontiguousarray(x) for x in (q[b:e, head], k[b:e, g], v[b:e, g]))
     out = np.zeros((len(rows), q.shape[2]))
     for n, i in enumerate(rows):
-        p, _, _, klo = _row_probabilities(q[b:e, head], k[b:e, g], sinks[head],
-                                          np.array([i]), scale, window)
-        kk = slice(b + klo, b + klo + p.shape[1])
-        o_i = p[0] @ v[kk, g]
+        p, _, _, klo = _row_probabilities(qh, kg, sinks[head], np.array([i]), scale, window)
+        kk = slice(klo, klo + p.shape[1])
+        o_i = p[0] @ vg[kk]
         d_i = dout[b + i, head] @ o_i
-        dx = p[0] * (v[kk, g] @ dout[b + i, head] - d_i)
-        out[n] = scale * (dx @ k[kk, g])
+        dx = p[0] * (vg[kk] @ dout[b + i, head] - d_i)
+        out[n] = scale * (dx @ kg[kk])
     return out
 
 
@@ -215,9 +215,9 @@ def backward_keys(q, k, v, sinks, dout, cu_seqlens, scale, window, seq, kv_head,
     last_row = L - 1 if window == 0 else min(L - 1, kmax + window - 1)
     dk = np.zeros((len(keys), q.shape[2]))
     dv = np.zeros((len(keys), q.shape[2]))
-    kg, vg = k[b:e, kv_head], v[b:e, kv_head]
+    kg, vg = np.ascontiguousarray(k[b:e, kv_head]), np.ascontiguousarray(v[b:e, kv_head])
     for h in range(kv_head * group, (kv_head + 1) * group):
-        qh, doh = q[b:e, h], dout[b:e, h]
+        qh, doh = np.ascontiguousarray(q[b:e, h]), np.ascontiguousarray(dout[b:e, h])
         for i in range(kmin, last_row + 1):
             p, _, _, klo = _row_probabilities(qh, kg, sinks[h], np.array([i]), scale, window)
             kk = slice(klo, klo + p.shape[1])

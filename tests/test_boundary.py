@@ -1,0 +1,162 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and rejects every bad argument before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_sink_fwd_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sink_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sink_attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib.load()
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    # the symbols are plain C names (no C++ mangling)
+    out = os.popen(f"nm -D --defined-only {_lib.LIB_PATH}").read()
+    for name in declared:
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_status_strings():
+    lib = _lib.load()
+    seen = set()
+    for st in range(5):
+        s = lib.sink_attn_status_string(st).decode()
+        assert s and s not in seen
+        seen.add(s)
+    assert lib.sink_attn_status_string(99).decode() == "unknown status"
+
+
+def _good_params(T=128, hq=8, hkv=2, d=64, window=0, dtype=0):
+    p = _lib.SinkAttnParams()
+    p.cu_seqlens = 256  # never read by the host unless SINK_ATTN_VALIDATE=1
+    p.num_seqs = 1
+    p.max_seqlen = T
+    p.total_tokens = T
+    p.num_q_heads = hq
+    p.num_kv_heads = hkv
+    p.head_dim = d
+    p.softmax_scale = 0.125
+    p.causal = 1
+    p.window = window
+    p.dtype = dtype
+    return p
+
+
+FAKE = 1 << 20  # aligned, non-null, never dereferenced by the host
+
+
+def _fwd(p, **override):
+    lib = _lib.load()
+    args = dict(q=FAKE, k=FAKE, v=FAKE, sinks=FAKE, o=FAKE, lse=FAKE)
+    args.update(override)
+    ptr = ctypes.byref(p) if p is not None else None
+    return lib.sink_attn_fwd(ptr, args["q"], args["k"], args["v"], args["sinks"], args["o"],
+                             args["lse"], None)
+
+
+def _bwd(p, ws_bytes=None, **override):
+    lib = _lib.load()
+    args = dict(q=FAKE, k=FAKE, v=FAKE, sinks=FAKE, o=FAKE, lse=FAKE, dout=FAKE, dq=FAKE,
+                dk=FAKE, dv=FAKE, dsinks=FAKE, ws=FAKE)
+    args.update(override)
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    return lib.sink_attn_bwd(ctypes.byref(p), args["q"], args["k"], args["v"], args["sinks"],
+                             args["o"], args["lse"], args["dout"], args["dq"], args["dk"],
+                             args["dv"], args["dsinks"], args["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_seqs", 0, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("num_seqs", 70000, _lib.SINK_ATTN_ERR_UNSUPPORTED),
+    ("total_tokens", -1, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("max_seqlen", 0, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("num_q_heads", 0, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("num_kv_heads", 3, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("head_dim", 12, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("head_dim", 0, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("head_dim", 128, _lib.SINK_ATTN_ERR_UNSUPPORTED),
+    ("softmax_scale", 0.0, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("softmax_scale", float("nan"), _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("softmax_scale", float("inf"), _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("causal", 0, _lib.SINK_ATTN_ERR_UNSUPPORTED),
+    ("window", -1, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("dtype", 7, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("cu_seqlens", None, _lib.SINK_ATTN_ERR_INVALID_ARG),
+])
+def test_bad_params_are_rejected_without_launch(field, value, status):
+    lib = _lib.load()
+    p = _good_params()
+    setattr(p, field, value)
+    assert _fwd(p) == status
+    assert lib.sink_attn_last_error().decode() != ""
+    assert _bwd(p) == status
+    assert lib.sink_attn_bwd_workspace_size(ctypes.byref(p)) == 0
+
+
+def test_null_params():
+    lib = _lib.load()
+    assert _fwd(None) == _lib.SINK_ATTN_ERR_INVALID_ARG
+    assert lib.sink_attn_bwd_workspace_size(None) == 0
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "sinks", "o", "lse"])
+def test_fwd_null_tensor(name):
+    assert _fwd(_good_params(), **{name: None}) == _lib.SINK_ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "sinks", "o", "lse", "dout", "dq", "dk", "dv",
+                                  "dsinks", "ws"])
+def test_bwd_null_tensor(name):
+    assert _bwd(_good_params(), **{name: None}) == _lib.SINK_ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o"])
+def test_misaligned_tensor(name):
+    assert _fwd(_good_params(), **{name: FAKE + 2}) == _lib.SINK_ATTN_ERR_INVALID_ARG
+
+
+def test_workspace_size_and_too_small():
+    lib = _lib.load()
+    T, hq, hkv, d = 1000, 8, 2, 64
+    p = _good_params(T, hq, hkv, d)
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    want = up(4 * hq * T) + up(4 * T * hq * d) + 2 * up(4 * T * hkv * d)
+    assert lib.sink_attn_bwd_workspace_size(ctypes.byref(p)) == want
+    assert _bwd(p, ws_bytes=want - 1) == _lib.SINK_ATTN_ERR_WORKSPACE_TOO_SMALL
+    assert "workspace" in lib.sink_attn_last_error().decode()
+    assert _bwd(p, ws_bytes=want, ws=FAKE + 16) == _lib.SINK_ATTN_ERR_INVALID_ARG
+
+
+def test_forward_with_no_tokens_is_a_no_op():
+    p = _good_params(T=0)
+    p.max_seqlen = 0
+    assert _fwd(p, q=None, k=None, v=None, o=None, lse=None, sinks=None) == _lib.SINK_ATTN_OK
+
+
+def test_package_raises_when_library_is_missing(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load()
+
+
+def test_set_bwd_events_validation():
+    lib = _lib.load()
+    arr = (ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)
+    assert lib.sink_attn_set_bwd_events(arr) == _lib.SINK_ATTN_ERR_INVALID_ARG
+    assert lib.sink_attn_set_bwd_events(None) == _lib.SINK_ATTN_OK

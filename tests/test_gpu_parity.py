@@ -1,0 +1,243 @@
+"""GPU (HIP, through the C ABI) against the float64 oracle on identical inputs.
+
+Small cases compare every element; the full-size workloads compare the
+outputs the oracle can compute at that size (whole KV groups, sampled rows
+and keys) and check the rest through identities that hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synthetic.workloads import WORKLOADS, custom_workload, make_inputs
+from tests.parity_util import (TOL_DS, TOL_GRAD, TOL_LSE, TOL_O, check_full, max_abs, rel_l2,
+                               run_gpu, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_full(inp, scale, window):
+    q, k, v, do, s, cu = (inp[n] for n in ("q", "k", "v", "dout", "sinks", "cu_seqlens"))
+    o, lse = oracle.forward(q, k, v, s, cu, scale, window)
+    dq, dk, dv, ds = oracle.backward(q, k, v, s, do, cu, scale, window)
+    return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "ds": ds}
+
+
+def _set_sinks(inp, mode, hq):
+    if mode == "minus_inf":
+        inp["sinks"] = torch.full((hq,), -math.inf)
+    elif mode == "plus30":
+        inp["sinks"] = torch.full((hq,), 30.0)
+    elif mode == "mixed":
+        vals = [-math.inf, 0.0, 5.0, 30.0, -3.0, 1.5, -math.inf, 2.0]
+        inp["sinks"] = torch.tensor([vals[i % len(vals)] for i in range(hq)], dtype=torch.float32)
+    return inp
+
+
+SMALL = [
+    # lengths, hq, hkv, d, window, dtype, sinks
+    ((1,), 4, 2, 64, 0, "bf16", "normal"),
+    ((2,), 4, 2, 64, 0, "bf16", "normal"),
+    ((63,), 8, 1, 64, 0, "bf16", "normal"),
+    ((65,), 8, 8, 64, 0, "bf16", "normal"),
+    ((127,), 4, 2, 32, 0, "bf16", "normal"),
+    ((129,), 4, 1, 64, 0, "bf16", "normal"),
+    ((300,), 8, 2, 64, 0, "bf16", "normal"),
+    ((0, 5, 1, 130, 0, 64, 257), 4, 2, 64, 0, "bf16", "normal"),
+    ((200,), 4, 2, 64, 1, "bf16", "normal"),
+    ((300,), 4, 2, 64, 17, "bf16", "normal"),
+    ((333, 129), 8, 1, 64, 128, "bf16", "normal"),
+    ((150,), 2, 1, 64, 1000, "bf16", "normal"),
+    ((129, 70), 4, 2, 16, 0, "bf16", "normal"),
+    ((100,), 4, 2, 64, 0, "bf16", "minus_inf"),
+    ((100,), 4, 2, 64, 0, "bf16", "plus30"),
+    ((190,), 8, 2, 64, 0, "bf16", "mixed"),
+    ((257,), 4, 2, 40, 0, "f32", "normal"),
+    ((200, 3), 4, 4, 64, 9, "f32", "mixed"),
+    ((520,), 16, 2, 64, 0, "bf16", "normal"),
+]
+
+
+@pytest.mark.parametrize("lengths,hq,hkv,d,window,dtype,sinks", SMALL)
+def test_small_cases_match_oracle(lengths, hq, hkv, d, window, dtype, sinks):
+    label = f"L={lengths} hq={hq} hkv={hkv} d={d} W={window} {dtype} sinks={sinks}"
+    say("case", label)
+    w = custom_workload(lengths, hq, hkv, d, window, dtype)
+    inp = _set_sinks(make_inputs(w, seed=sum(lengths) + 7 * hq + d), sinks, hq)
+    scale = 1.0 / math.sqrt(d)
+    gpu = run_gpu(inp, w.max_seqlen, scale, window)
+    ref = _oracle_full(inp, scale, window)
+    check_full(gpu, ref, label)
+    if sinks == "minus_inf":
+        assert np.all(gpu["ds"] == 0.0)
+
+
+def test_workload1_tiny_fp32_matches_oracle():
+    w = WORKLOADS[1]
+    say("case workload 1", w.name)
+    inp = make_inputs(w)
+    gpu = run_gpu(inp, w.max_seqlen, w.softmax_scale, w.window)
+    check_full(gpu, _oracle_full(inp, w.softmax_scale, w.window), w.name)
+
+
+def test_forward_is_deterministic_and_packing_is_invariant():
+    w = custom_workload((130, 7, 64, 1), 8, 2, 64, 0, "bf16")
+    inp = make_inputs(w, seed=99)
+    say("case packing invariance", w.lengths)
+    a = run_gpu(inp, w.max_seqlen, w.softmax_scale, 0)
+    b = run_gpu(inp, w.max_seqlen, w.softmax_scale, 0)
+    assert np.array_equal(a["o"], b["o"]) and np.array_equal(a["lse"], b["lse"])
+    cu = inp["cu_seqlens"].numpy()
+    ds_sum = np.zeros_like(a["ds"])
+    for s in range(len(cu) - 1):
+        sl = slice(int(cu[s]), int(cu[s + 1]))
+        one = {n: inp[n][sl] for n in ("q", "k", "v", "dout")}
+        one["sinks"] = inp["sinks"]
+        one["cu_seqlens"] = torch.tensor([0, cu[s + 1] - cu[s]], dtype=torch.int32)
+        r = run_gpu(one, int(cu[s + 1] - cu[s]), w.softmax_scale, 0)
+        assert np.array_equal(r["o"], a["o"][sl])
+        assert np.array_equal(r["lse"], a["lse"][:, sl])
+        for n in ("dq", "dk", "dv"):
+            assert max_abs(r[n], a[n][sl]) < 2e-2
+        ds_sum += r["ds"]
+    assert rel_l2(ds_sum, a["ds"]) < 1e-5
+
+
+def test_empty_batch_zeroes_dsinks():
+    import attention_sink_fwd_amd as sa
+    dev = "cuda:0"
+    q = torch.empty((0, 4, 64), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((0, 2, 64), dtype=torch.bfloat16, device=dev)
+    sinks = torch.randn(4, device=dev)
+    cu = torch.zeros(3, dtype=torch.int32, device=dev)
+    o, lse = sa.sink_attn_fwd(q, k, k, sinks, cu, 0)
+    dsinks = torch.full((4,), 7.0, device=dev)
+    sa.sink_attn_bwd(q, k, k, sinks, o, lse, o, cu, 0, dsinks=dsinks)
+    torch.cuda.synchronize()
+    assert torch.all(dsinks == 0).item()
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads (the shapes the benchmark times).
+
+
+def _kv_group_reference(inp, scale, window, g, seqs=None):
+    """Oracle restricted to KV group g (and optionally some sequences)."""
+    q, k, v, do, s, cu = (inp[n] for n in ("q", "k", "v", "dout", "sinks", "cu_seqlens"))
+    cu = cu.numpy()
+    hq, hkv = q.shape[1], k.shape[1]
+    grp = hq // hkv
+    heads = list(range(g * grp, (g + 1) * grp))
+    out = []
+    for sidx in (range(len(cu) - 1) if seqs is None else seqs):
+        b, e = int(cu[sidx]), int(cu[sidx + 1])
+        c1 = np.array([0, e - b])
+        sl = slice(b, e)
+        o, lse = oracle.forward(q[sl], k[sl], v[sl], s, c1, scale, window, heads=heads)
+        dq, dk, dv, ds = oracle.backward(q[sl], k[sl], v[sl], s, do[sl], c1, scale, window,
+                                         kv_heads=[g])
+        out.append((sidx, b, e, heads, o, lse, dq, dk, dv, ds))
+    return out
+
+
+def _check_group(gpu, refs, g, label):
+    errs = {"o": 0.0, "lse": 0.0}
+    num = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    den = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for (sidx, b, e, heads, o, lse, dq, dk, dv, ds) in refs:
+        errs["o"] = max(errs["o"], max_abs(gpu["o"][b:e, heads], o[:, heads]))
+        errs["lse"] = max(errs["lse"], max_abs(gpu["lse"][heads, b:e], lse[heads]))
+        for n, ref, got in (("dq", dq[:, heads], gpu["dq"][b:e, heads]),
+                            ("dk", dk[:, g], gpu["dk"][b:e, g]),
+                            ("dv", dv[:, g], gpu["dv"][b:e, g])):
+            num[n] += float(np.sum((got - ref) ** 2))
+            den[n] += float(np.sum(ref ** 2))
+    for n in num:
+        errs[n] = math.sqrt(num[n] / den[n])
+    say(f"  {label} group {g}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert errs["o"] <= TOL_O and errs["lse"] <= TOL_LSE, errs
+    assert errs["dq"] <= TOL_GRAD and errs["dk"] <= TOL_GRAD and errs["dv"] <= TOL_GRAD, errs
+    return errs
+
+
+def _ds_self_consistency(gpu, inp):
+    """dS_h == -sum_i exp(S_h - LSE_i) (dO_i . O_i) on the GPU's own O and LSE."""
+    s = inp["sinks"].double().numpy()
+    do = inp["dout"].double().numpy()
+    dvec = np.einsum("thd,thd->ht", do, gpu["o"])
+    want = -np.sum(np.exp(s[:, None] - gpu["lse"]) * dvec, axis=1)
+    return rel_l2(gpu["ds"], want)
+
+
+@pytest.mark.parametrize("wid", [2, 3])
+def test_full_workload_whole_kv_groups(wid):
+    """Workloads 2 and 3: two whole KV groups against the oracle; dS in full."""
+    w = WORKLOADS[wid]
+    say("case workload", wid, w.name)
+    inp = make_inputs(w)
+    gpu = run_gpu(inp, w.max_seqlen, w.softmax_scale, w.window)
+    hq, hkv = w.num_q_heads, w.num_kv_heads
+    ds_ref = np.zeros(hq)
+    ds_heads = []
+    for g in (0, hkv - 3):
+        refs = _kv_group_reference(inp, w.softmax_scale, w.window, g)
+        _check_group(gpu, refs, g, w.name)
+        for r in refs:
+            ds_ref[r[3]] += r[9][r[3]]
+        ds_heads += r[3]
+    e = rel_l2(gpu["ds"][ds_heads], ds_ref[ds_heads])
+    say(f"  dS over heads {ds_heads[0]}..: {e:.2e}; self-consistency {_ds_self_consistency(gpu, inp):.2e}")
+    assert e <= TOL_DS
+
+
+def test_full_workload4_long_context_sampled():
+    """L = 65536 head share: sampled rows (O, LSE, dQ) and late keys (dK, dV)."""
+    w = WORKLOADS[4]
+    say("case workload 4", w.name)
+    inp = make_inputs(w)
+    gpu = run_gpu(inp, w.max_seqlen, w.softmax_scale, 0)
+    L = w.max_seqlen
+    rng = np.random.default_rng(404)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 4095, 4096, 32767, L - 2, L - 1],
+                                     rng.integers(0, L, 13)]))
+    q, k, v, do, s, cu = (inp[n] for n in ("q", "k", "v", "dout", "sinks", "cu_seqlens"))
+    e_o = e_l = 0.0
+    num = den = 0.0
+    for h in (0, 7, 8, 15):
+        o_r, l_r = oracle.forward_rows(q, k, v, s, cu, w.softmax_scale, 0, 0, h, rows)
+        e_o = max(e_o, max_abs(gpu["o"][rows, h], o_r))
+        e_l = max(e_l, max_abs(gpu["lse"][h, rows], l_r))
+        dq_r = oracle.backward_rows(q, k, v, s, do, cu, w.softmax_scale, 0, 0, h, rows)
+        num += float(np.sum((gpu["dq"][rows, h] - dq_r) ** 2))
+        den += float(np.sum(dq_r ** 2))
+    e_dq = math.sqrt(num / den)
+    keys = np.array([L - 100, L - 64, L - 33, L - 2, L - 1])
+    numk = denk = numv = denv = 0.0
+    for g in (0, 1):
+        dk_r, dv_r = oracle.backward_keys(q, k, v, s, do, cu, w.softmax_scale, 0, 0, g, keys)
+        numk += float(np.sum((gpu["dk"][keys, g] - dk_r) ** 2)); denk += float(np.sum(dk_r ** 2))
+        numv += float(np.sum((gpu["dv"][keys, g] - dv_r) ** 2)); denv += float(np.sum(dv_r ** 2))
+    e_dk, e_dv = math.sqrt(numk / denk), math.sqrt(numv / denv)
+    e_ds = _ds_self_consistency(gpu, inp)
+    say(f"  o={e_o:.2e} lse={e_l:.2e} dq={e_dq:.2e} dk={e_dk:.2e} dv={e_dv:.2e} ds(self)={e_ds:.2e}")
+    assert e_o <= TOL_O and e_l <= TOL_LSE
+    assert e_dq <= TOL_GRAD and e_dk <= TOL_GRAD and e_dv <= TOL_GRAD
+    assert e_ds <= 1e-3
+
+
+def test_full_workload5_varlen_sampled_sequences():
+    """64 packed sequences: whole KV groups of four sequences, incl. shortest and longest."""
+    w = WORKLOADS[5]
+    say("case workload 5", w.name)
+    inp = make_inputs(w)
+    gpu = run_gpu(inp, w.max_seqlen, w.softmax_scale, 0)
+    lens = np.array(w.lengths)
+    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 2, 63})
+    for g in (1, 6):
+        refs = _kv_group_reference(inp, w.softmax_scale, 0, g, seqs=seqs)
+        _check_group(gpu, refs, g, w.name)
+    e_ds = _ds_self_consistency(gpu, inp)
+    say(f"  ds(self)={e_ds:.2e}")
+    assert e_ds <= 1e-3
