@@ -4,7 +4,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -16,7 +18,7 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
-thread_local hipEvent_t g_bwd_events[4] = {nullptr, nullptr, nullptr, nullptr};
+thread_local hipEvent_t g_bwd_events[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
 thread_local bool g_bwd_events_on = false;
 
 int fail(int status, const char* fmt, ...) {
@@ -42,10 +44,12 @@ int check_params(const sink_attn_params* p) {
   if (p->num_q_heads % p->num_kv_heads != 0)
     return fail(SINK_ATTN_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
                 p->num_q_heads, p->num_kv_heads);
-  if (p->num_q_heads > 65535) return fail(SINK_ATTN_ERR_UNSUPPORTED, "num_q_heads > 65535");
+  if (p->num_q_heads > 8192) return fail(SINK_ATTN_ERR_UNSUPPORTED, "num_q_heads > 8192");
   if (p->head_dim < 8 || p->head_dim % 8 != 0)
     return fail(SINK_ATTN_ERR_INVALID_ARG, "head_dim must be a positive multiple of 8 (got %d)", p->head_dim);
   if (p->head_dim > 64) return fail(SINK_ATTN_ERR_UNSUPPORTED, "head_dim > 64 is not built (got %d)", p->head_dim);
+  if ((int64_t)p->total_tokens * p->num_q_heads * p->head_dim > INT32_MAX)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "total_tokens * num_q_heads * head_dim must stay below 2^31");
   if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.0f))
     return fail(SINK_ATTN_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   if (p->causal != 1) return fail(SINK_ATTN_ERR_UNSUPPORTED, "only causal attention is built (causal must be 1)");
@@ -156,10 +160,13 @@ int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.sinks = sinks;
   a.cu_seqlens = p->cu_seqlens;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dsinks = dsinks;
-  a.delta = reinterpret_cast<float*>(wsb);
-  a.dq_acc = reinterpret_cast<float*>(wsb + ws.delta);
-  a.dk_acc = reinterpret_cast<float*>(wsb + ws.delta + ws.dq_acc);
-  a.dv_acc = reinterpret_cast<float*>(wsb + ws.delta + ws.dq_acc + ws.dk_acc);
+  size_t off = 0;
+  auto carve = [&](size_t bytes) { float* p = reinterpret_cast<float*>(wsb + off); off += bytes; return p; };
+  a.ndelta = carve(ws.ndelta);
+  a.nlse = carve(ws.nlse);
+  a.dk_acc = carve(ws.dk_acc);
+  a.dv_acc = carve(ws.dv_acc);
+  a.dsink_part = carve(ws.dsink_part);
   a.num_q_heads = p->num_q_heads; a.num_kv_heads = p->num_kv_heads; a.head_dim = p->head_dim;
   a.total_tokens = p->total_tokens; a.window = p->window;
   a.scale = p->softmax_scale;
@@ -176,9 +183,9 @@ int sink_attn_set_bwd_events(void* const* events) {
     g_bwd_events_on = false;
     return SINK_ATTN_OK;
   }
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 5; ++i)
     if (!events[i]) return fail(SINK_ATTN_ERR_INVALID_ARG, "events[%d] is NULL", i);
-  for (int i = 0; i < 4; ++i) g_bwd_events[i] = static_cast<hipEvent_t>(events[i]);
+  for (int i = 0; i < 5; ++i) g_bwd_events[i] = static_cast<hipEvent_t>(events[i]);
   g_bwd_events_on = true;
   return SINK_ATTN_OK;
 }

@@ -10,17 +10,33 @@
 // memory-efficient attention backward, with P recomputed from the saved LSE
 // (which already includes the sink, so P needs no other change).
 //
-//  1. bwd_pre_kernel   D_i = rowsum(dO * O) into the workspace; zeroes the
-//                      float dQ/dK/dV accumulators and dsinks.
-//  2. bwd_main_kernel  one workgroup per (sequence, query head, 128-key tile);
-//                      loops over the visible 64-row query tiles:
+//  1. bwd_pre_kernel   streams O and dO once (flat, coalesced): -D_i and
+//                      -LSE_i / scale into the workspace, the sink term
+//                      -p_sink,i D_i reduced per block (8-lane shuffles, then
+//                      LDS float atomics per head) into a per-block partial;
+//                      zeroes the float dK/dV accumulators.
+//  2. bwd_dkdv_kernel  one workgroup per (sequence, query head, 128-key tile),
+//                      looping over the visible 64-row query tiles:
 //                      S = Q K^T, dP = dO V^T, P = exp(S - LSE),
 //                      dS = P (dP - D), dV += P^T dO, dK += dS^T Q on the
-//                      matrix cores with K, V, dK, dV held in registers; dQ
-//                      tile = dS K through LDS, added with float atomics.
-//  3. bwd_post_kernel  converts the accumulators to the output type and
-//                      accumulates dS_h (wavefront reduction, then one float
-//                      atomic per wavefront).
+//                      matrix cores, K, V, dK, dV in registers; the per-head
+//                      dK, dV are added to float accumulators (float atomics,
+//                      once per key and head).
+//  3. bwd_dq_kernel    one workgroup per (sequence, query head, 128-row query
+//                      tile), looping over the visible 64-key tiles: recomputes
+//                      S and dP in transposed form and accumulates
+//                      dQ = scale * dS K in registers; writes dQ once.
+//  4. bwd_post_kernel  converts the dK/dV accumulators to the output type
+//                      (flat, coalesced) and sums the per-block dS partials of
+//                      each head in a fixed order (deterministic dS_h).
+//
+// dQ is not accumulated with float atomics across key tiles: on this chip
+// float atomics retire at about 0.3 G element-operations per microsecond,
+// which for L = 4096, 64 heads (2.7e8 additions) alone takes longer than the
+// whole backward pass.  Recomputing S and dP in the dQ kernel costs two
+// extra matrix products per visible block instead.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -28,108 +44,112 @@ namespace sinkattn {
 
 namespace {
 
-constexpr int kRowsPerBlock = 64;  // rows of one head per block in pre/post
+constexpr int kFlatThreads = 256;
+// VMEM instructions one wavefront issues per query-tile prefetch of the
+// dK/dV kernel on the direct path (2 Q + 2 dO + 1 statistics).
+constexpr int kPrefetchOps = 5;
+constexpr int kPairsPerIter = kFlatThreads / 8;  // 8 lanes per (row, head) pair
 
 template <typename TIn>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
+  extern __shared__ float bins[];  // [num_q_heads] sink-term partial per head
   const int tid = threadIdx.x;
-  const int row = blockIdx.x * kRowsPerBlock + (tid >> 2);
-  const int part = tid & 3;  // 16 columns each
-  const int h = blockIdx.y;
-  const int hd = a.head_dim, T = a.total_tokens;
-  if (blockIdx.x == 0 && blockIdx.y == 0) {
-    for (int i = tid; i < a.num_q_heads; i += 256) a.dsinks[i] = 0.0f;
-  }
-  if (row >= T) return;
-  const long qoff = (long)row * a.num_q_heads * hd + (long)h * hd;
-  const TIn* O = (const TIn*)a.o + qoff;
-  const TIn* dO = (const TIn*)a.dout + qoff;
-  float acc = 0.0f;
+  const int Hq = a.num_q_heads, hd = a.head_dim, T = a.total_tokens;
+  for (int i = tid; i < Hq; i += kFlatThreads) bins[i] = 0.0f;
+  __syncthreads();
+
+  const int part = tid & 7;  // 8-element chunk of the head dimension
+  const int npairs = T * Hq;
+  const TIn* O = (const TIn*)a.o;
+  const TIn* dO = (const TIn*)a.dout;
   const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int d = part * 16 + 8 * c;
-    if (d < hd) {
-      f32x8 x = load8f(O + d), y = load8f(dO + d);
+  for (int pr = blockIdx.x * kPairsPerIter + (tid >> 3); pr < npairs; pr += gridDim.x * kPairsPerIter) {
+    const int row = pr / Hq, h = pr - row * Hq;
+    const long off = (long)pr * hd + part * 8;
+    float acc = 0.0f;
+    if (part * 8 < hd) {
+      const f32x8 x = load8f(O + off), y = load8f(dO + off);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc += x[i] * y[i];
-      *(f32x4*)(a.dq_acc + qoff + d) = z;
-      *(f32x4*)(a.dq_acc + qoff + d + 4) = z;
     }
-  }
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  if (part == 0) a.delta[(long)h * T + row] = acc;
-  if (h < a.num_kv_heads) {
-    const long koff = (long)row * a.num_kv_heads * hd + (long)h * hd;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int d = part * 16 + 8 * c;
-      if (d < hd) {
-        *(f32x4*)(a.dk_acc + koff + d) = z;
-        *(f32x4*)(a.dk_acc + koff + d + 4) = z;
-        *(f32x4*)(a.dv_acc + koff + d) = z;
-        *(f32x4*)(a.dv_acc + koff + d + 4) = z;
-      }
-    }
-  }
-}
-
-template <typename TIn>
-__global__ __launch_bounds__(256) void bwd_post_kernel(BwdArgs a) {
-  const int tid = threadIdx.x;
-  const int row = blockIdx.x * kRowsPerBlock + (tid >> 2);
-  const int part = tid & 3;
-  const int h = blockIdx.y;
-  const int hd = a.head_dim, T = a.total_tokens;
-  float contrib = 0.0f;
-  if (row < T) {
-    const long qoff = (long)row * a.num_q_heads * hd + (long)h * hd;
-    TIn* dq = (TIn*)a.dq + qoff;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int d = part * 16 + 4 * c;
-      if (d < hd) store4(dq + d, *(const f32x4*)(a.dq_acc + qoff + d));
-    }
-    if (h < a.num_kv_heads) {
-      const long koff = (long)row * a.num_kv_heads * hd + (long)h * hd;
-      TIn* dk = (TIn*)a.dk + koff;
-      TIn* dv = (TIn*)a.dv + koff;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int d = part * 16 + 4 * c;
-        if (d < hd) {
-          store4(dk + d, *(const f32x4*)(a.dk_acc + koff + d));
-          store4(dv + d, *(const f32x4*)(a.dv_acc + koff + d));
-        }
-      }
-    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
     if (part == 0) {
       const long si = (long)h * T + row;
+      const float lse = a.lse[si];
+      a.ndelta[si] = -acc;          // -D: initial value of the dP accumulators
+      a.nlse[si] = -lse / a.scale;  // -LSE/scale: initial value of the S accumulators
       // sink's softmax-Jacobian entry: p_sink * (0 - D); exp(-inf) = 0
-      contrib = -__expf(a.sinks[h] - a.lse[si]) * a.delta[si];
+      atomicAdd(&bins[h], -__expf(a.sinks[h] - lse) * acc);
     }
   }
-  contrib = wave_sum(contrib);
-  if ((tid & 63) == 0 && contrib != 0.0f) unsafeAtomicAdd(a.dsinks + h, contrib);
+  const long kchunks = (long)T * a.num_kv_heads * hd / 8;
+  for (long c = (long)blockIdx.x * kFlatThreads + tid; c < kchunks; c += (long)gridDim.x * kFlatThreads) {
+    *(f32x4*)(a.dk_acc + 8 * c) = z;
+    *(f32x4*)(a.dk_acc + 8 * c + 4) = z;
+    *(f32x4*)(a.dv_acc + 8 * c) = z;
+    *(f32x4*)(a.dv_acc + 8 * c + 4) = z;
+  }
+  __syncthreads();
+  for (int i = tid; i < Hq; i += kFlatThreads) a.dsink_part[(long)blockIdx.x * Hq + i] = bins[i];
 }
 
-constexpr int kBN = 128;  // keys per workgroup (4 wavefronts x 32)
-constexpr int kBM = 64;   // query rows per inner step
-constexpr int kD = 64;
-constexpr int kLD = kD + 8;    // row stride of the [row][d] tiles
-constexpr int kLDT = kBM + 8;  // row stride of the dS^T tile [key][q]
+__device__ __forceinline__ void convert8(const float* src, bf16* dst) {
+  const f32x4 x = *(const f32x4*)src, y = *(const f32x4*)(src + 4);
+  const f32x8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  *(bf16x8*)dst = __builtin_convertvector(v, bf16x8);
+}
+__device__ __forceinline__ void convert8(const float* src, float* dst) {
+  *(f32x4*)dst = *(const f32x4*)src;
+  *(f32x4*)(dst + 4) = *(const f32x4*)(src + 4);
+}
 
 template <typename TIn>
-__global__ __launch_bounds__(256, 2) void bwd_main_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kBN * kLD];    // K tile [key][d]
-  __shared__ __attribute__((aligned(16))) bf16 Qs[kBM * kLD];    // Q tile [q][d]
-  __shared__ __attribute__((aligned(16))) bf16 dOs[kBM * kLD];   // dO tile [q][d]
-  __shared__ __attribute__((aligned(16))) bf16 dSt[kBN * kLDT];  // dS^T [key][q]
-  __shared__ __attribute__((aligned(16))) float lse2s[kBM];
-  __shared__ __attribute__((aligned(16))) float Dsh[kBM];
+__global__ __launch_bounds__(256) void bwd_post_kernel(BwdArgs a, int conv_blocks, int pre_blocks) {
+  const int tid = threadIdx.x;
+  const int Hq = a.num_q_heads;
+  if ((int)blockIdx.x >= conv_blocks) {
+    // dS_h = sum of the preprocess partials, one wavefront per head, fixed order.
+    const int h = (blockIdx.x - conv_blocks) * 4 + (tid >> 6);
+    if (h >= Hq) return;
+    float s = 0.0f;
+    for (int j = tid & 63; j < pre_blocks; j += 64) s += a.dsink_part[(long)j * Hq + h];
+    s = wave_sum(s);
+    if ((tid & 63) == 0) a.dsinks[h] = s;
+    return;
+  }
+  const long kchunks = (long)a.total_tokens * a.num_kv_heads * a.head_dim / 8;
+  for (long c = (long)blockIdx.x * kFlatThreads + tid; c < 2 * kchunks; c += (long)conv_blocks * kFlatThreads) {
+    if (c < kchunks)
+      convert8(a.dk_acc + 8 * c, (TIn*)a.dk + 8 * c);
+    else
+      convert8(a.dv_acc + 8 * (c - kchunks), (TIn*)a.dv + 8 * (c - kchunks));
+  }
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+constexpr int kBN = 128;  // keys per dK/dV workgroup (4 wavefronts x 32)
+constexpr int kBM = 64;   // query rows per dK/dV step
+constexpr int kD = 64;    // padded head dimension
+
+// One stage of the query-side ring buffer of the dK/dV kernel.
+struct __attribute__((aligned(16))) QStage {
+  bf16 q[kBM * kD];     // Q tile, swizzled [q][d]
+  bf16 dout[kBM * kD];  // dO tile, swizzled [q][d]
+  float nlse[kBM];      // -LSE/scale of the tile rows
+  float ndelta[kBM];    // -D of the tile rows
+  float spare[kBM];     // landing area that keeps every wavefront's load count equal
+};
+constexpr int kStages = 3;
+
+// dK and dV for one 128-key tile of one query head (partial over the heads
+// of its KV group; summed with float atomics into the workspace).
+template <typename TIn, bool kDirect>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
+  __shared__ QStage stage[kStages];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int h2 = lane >> 5, l32 = lane & 31;
   const int seq = blockIdx.z, hq = blockIdx.y;
   const int kt = blockIdx.x;  // key tile 0 sees the most query tiles: runs first
@@ -140,170 +160,162 @@ __global__ __launch_bounds__(256, 2) void bwd_main_kernel(BwdArgs a) {
 
   const int hd = a.head_dim, T = a.total_tokens, window = a.window;
   const int g = hq / (a.num_q_heads / a.num_kv_heads);
-  const TIn* __restrict__ Q = (const TIn*)a.q;
-  const TIn* __restrict__ K = (const TIn*)a.k;
-  const TIn* __restrict__ V = (const TIn*)a.v;
-  const TIn* __restrict__ dO = (const TIn*)a.dout;
-  const long qs = (long)a.num_q_heads * hd, ks = (long)a.num_kv_heads * hd;
-
-  // This wavefront's 32 keys; the lane's key is column n of S and dP.
-  const int wk_lo = k0 + 32 * w, wk_hi = wk_lo + 31;
-  const int key_n = wk_lo + l32;
-  bf16x8 kf[4], vf[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int d0 = 16 * c + 8 * h2;
-    const bool ok = key_n < L && d0 < hd;
-    const long off = (bos + key_n) * ks + (long)g * hd + d0;
-    kf[c] = ok ? load8(K + off) : zero8();
-    vf[c] = ok ? load8(V + off) : zero8();
-  }
-  // Whole K tile, row-major, for the dQ product (B operand via transposing reads).
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-    const int key = k0 + row;
-    *(bf16x8*)(Ks + row * kLD + col) =
-        (key < L && col < hd) ? load8(K + (bos + key) * ks + (long)g * hd + col) : zero8();
-  }
-
-  f32x16 dk[2], dv[2];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) { dk[0][i] = dk[1][i] = dv[0][i] = dv[1][i] = 0.0f; }
+  const int qs = a.num_q_heads * hd, ks = a.num_kv_heads * hd;  // row strides (< 2^31 elements)
+  // Base pointers of this (sequence, head): row i of the sequence is base + i * stride.
+  const TIn* __restrict__ Qh = (const TIn*)a.q + (long)bos * qs + hq * hd;
+  const TIn* __restrict__ dOh = (const TIn*)a.dout + (long)bos * qs + hq * hd;
+  const TIn* __restrict__ Kg = (const TIn*)a.k + (long)bos * ks + g * hd;
+  const TIn* __restrict__ Vg = (const TIn*)a.v + (long)bos * ks + g * hd;
+  const float* __restrict__ nlse_h = a.nlse + (long)hq * T + bos;
+  const float* __restrict__ nD_h = a.ndelta + (long)hq * T + bos;
 
   // Query rows that can see a key of this tile: k0 <= q < k0 + kBN - 1 + window.
   const int qhi = window > 0 ? min(L, k0 + kBN - 1 + window) : L;
   const int qt0 = k0 / kBM, qt1 = (qhi + kBM - 1) / kBM;
 
-  bf16x8 qreg[2], doreg[2];
-  float lreg = 0.0f, dreg = 0.0f;
-  auto gload = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      const int q = t * kBM + row;
-      const bool ok = q < L && col < hd;
-      const long off = (bos + q) * qs + (long)hq * hd + col;
-      qreg[i] = ok ? load8(Q + off) : zero8();
-      doreg[i] = ok ? load8(dO + off) : zero8();
-    }
-    if (tid < kBM) {
-      const int q = t * kBM + tid;
-      const long si = (long)hq * T + bos + q;
-      lreg = q < L ? a.lse[si] * kLog2e : 0.0f;
-      dreg = q < L ? a.delta[si] : 0.0f;
+  // Prefetch query tile t (clamped to the last visible tile) into stage buf.
+  // Direct path: exactly kPrefetchOps VMEM instructions per wavefront.
+  auto prefetch = [&](int t, int buf) {
+    const int q0 = min(t, qt1 - 1) * kBM;
+    QStage& st = stage[buf];
+    if constexpr (kDirect) {
+      stage_direct<kBM>(st.q, (const bf16*)Qh, q0, L, qs, w, lane);
+      stage_direct<kBM>(st.dout, (const bf16*)dOh, q0, L, qs, w, lane);
+      const float* src = (w == 1) ? nD_h : nlse_h;
+      float* dst = (w == 0) ? st.nlse : (w == 1 ? st.ndelta : st.spare);
+      __builtin_amdgcn_global_load_lds((const void*)(src + min(q0 + lane, L - 1)), (SA_LDS void*)dst, 4, 0, 0);
+    } else {
+      stage_regs<kBM>(st.q, Qh, q0, L, qs, hd, tid);
+      stage_regs<kBM>(st.dout, dOh, q0, L, qs, hd, tid);
+      if (tid < kBM) {
+        const int q = min(q0 + tid, L - 1);
+        st.nlse[tid] = nlse_h[q];
+        st.ndelta[tid] = nD_h[q];
+      }
     }
   };
-  auto sstore = [&]() {
+
+  // This wavefront's K and V fragments: B operands of S = Q K^T and
+  // dP = dO V^T (lane = key column, 8 consecutive d per register group).
+  const int wk_lo = k0 + 32 * w, wk_hi = wk_lo + 31;
+  const int key_n = wk_lo + l32;
+  bf16x8 kf[4], vf[4];
+  {
+    const int krow = min(key_n, L - 1);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      *(bf16x8*)(Qs + row * kLD + col) = qreg[i];
-      *(bf16x8*)(dOs + row * kLD + col) = doreg[i];
+    for (int c = 0; c < 4; ++c) {
+      const int d0 = 16 * c + 8 * h2;
+      kf[c] = d0 < hd ? load8(Kg + krow * ks + d0) : zero8();
+      vf[c] = d0 < hd ? load8(Vg + krow * ks + d0) : zero8();
     }
-    if (tid < kBM) { lse2s[tid] = lreg; Dsh[tid] = dreg; }
-  };
+  }
+  issue_fence();
+  prefetch(qt0, 0);
+  issue_fence();
+  prefetch(qt0 + 1, 1);
+  issue_fence();
+
+  f32x16 dk[2], dv[2];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { dk[0][i] = dk[1][i] = dv[0][i] = dv[1][i] = 0.0f; }
 
   const float sl2 = a.scale_log2;
   const int qrow_base = row_perm(l32);
-  bf16* dst_row = dSt + (32 * w + l32) * kLDT + 8 * h2;
 
-  if (qt0 < qt1) gload(qt0);
+  int buf = 0;
   for (int t = qt0; t < qt1; ++t) {
-    __syncthreads();  // previous dQ product is done with Qs, dOs, dSt
-    sstore();
-    __syncthreads();
-    if (t + 1 < qt1) gload(t + 1);
+    // Wait for this wavefront's part of tile t (only the next prefetch may
+    // still be in flight), then make all parts visible.
+    if constexpr (kDirect) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    static_assert(kPrefetchOps == 5, "wait count");
+    lds_barrier();  // tile t visible; stage (t+2)%3 was last read in step t-1
+    {
+      int nb = buf + 2;
+      if (nb >= kStages) nb -= kStages;
+      prefetch(t + 2, nb);
+      issue_fence();
+    }
+    const QStage& st = stage[buf];
     const int qb = t * kBM;
 
-    const bool active = wk_lo < L && wk_lo <= qb + kBM - 1 &&
-                        !(window > 0 && qb - wk_hi >= window);
+    const bool active = wk_lo < L && wk_lo <= qb + kBM - 1 && !(window > 0 && qb - wk_hi >= window);
     if (active) {
-      f32x16 s[2], dp[2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { s[mb][i] = 0.0f; dp[mb][i] = 0.0f; }
-        const int qr = qrow_base + 32 * mb;
-        const bf16* qp = Qs + qr * kLD + 8 * h2;
-        const bf16* dop = dOs + qr * kLD + 8 * h2;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          s[mb] = mfma32(*(const bf16x8*)(qp + 16 * c), kf[c], s[mb]);
-          dp[mb] = mfma32(*(const bf16x8*)(dop + 16 * c), vf[c], dp[mb]);
-        }
-      }
-      // Register r of block mb holds query row 32*mb + 16*(r/8) + 8*h2 + r%8.
       const bool need_mask = (wk_hi > qb) || (qb + kBM > L) ||
                              (window > 0 && qb + kBM - 1 - wk_lo >= window);
-      bf16x8 pf[4], df[4];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const int ql = 32 * mb + 16 * hb + 8 * h2;
-          const f32x4 la = *(const f32x4*)(lse2s + ql), lb = *(const f32x4*)(lse2s + ql + 4);
-          const f32x4 da = *(const f32x4*)(Dsh + ql), db = *(const f32x4*)(Dsh + ql + 4);
-          f32x8 pv, dv8;
+        // S and dP for query rows 32*mb .. 32*mb+31 of the tile; register r
+        // holds row 32*mb + 16*(r/8) + 8*h2 + r%8 (A rows permuted), so each
+        // half of the registers covers 8 consecutive rows.  The accumulators
+        // start from the row statistics -LSE/scale and -D, so that
+        // P = exp2(S * scale * log2 e) and dS = P * dP need one multiply each.
+        const int qr = qrow_base + 32 * mb;
+        const int ql0 = 32 * mb + 8 * h2;
+        f32x16 s, dp;
+        {
+          const f32x8 s0 = *(const f32x8*)(st.nlse + ql0), s1 = *(const f32x8*)(st.nlse + ql0 + 16);
+          const f32x8 d0 = *(const f32x8*)(st.ndelta + ql0), d1 = *(const f32x8*)(st.ndelta + ql0 + 16);
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const int r = 8 * hb + i;
-            const float lse2 = i < 4 ? la[i] : lb[i - 4];
-            const float dd = i < 4 ? da[i] : db[i - 4];
-            float p = fast_exp2(s[mb][r] * sl2 - lse2);
-            if (need_mask) {
-              const int q = qb + ql + i;
-              const bool vis = key_n <= q && q < L && (window == 0 || q - key_n < window);
-              p = vis ? p : 0.0f;
-            }
-            pv[i] = p;
-            dv8[i] = p * (dp[mb][r] - dd);
+            s[i] = s0[i];
+            s[8 + i] = s1[i];
+            dp[i] = d0[i];
+            dp[8 + i] = d1[i];
           }
-          pf[2 * mb + hb] = __builtin_convertvector(pv, bf16x8);
-          df[2 * mb + hb] = __builtin_convertvector(dv8, bf16x8);
         }
-      }
-      // dV += P^T dO and dK += dS^T Q (scale applied at the end).
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          dv[db] = mfma32(pf[c], frag_tr(dOs, kLD, 16 * c, 32 * db, lane), dv[db]);
-          dk[db] = mfma32(df[c], frag_tr(Qs, kLD, 16 * c, 32 * db, lane), dk[db]);
+          s = mfma32(frag_row(st.q, qr, 16 * c + 8 * h2), kf[c], s);
+          dp = mfma32(frag_row(st.dout, qr, 16 * c + 8 * h2), vf[c], dp);
+        }
+        bf16x8 pf[2], df[2];
+        // Element (hb, i) of this lane is query row rbase + 16*hb + i against
+        // key key_n.  Visible iff lo <= 16*hb + i < hi (causal, window, and
+        // rows past the end of the sequence), with lo and hi per lane.
+        const int rbase = qb + 32 * mb + 8 * h2;
+        const int lo = key_n - rbase;
+        const int hi = min(L - rbase, window > 0 ? lo + window : 0x7fffffff);
+        auto softmax_grad = [&](auto masked) {
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            f32x8 pv, dv8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int r = 8 * hb + i;
+              float p = fast_exp2(s[r] * sl2);
+              if constexpr (decltype(masked)::value) {
+                const int idx = 16 * hb + i;
+                p = (idx >= lo && idx < hi) ? p : 0.0f;
+              }
+              pv[i] = p;
+              dv8[i] = p * dp[r];
+            }
+            pf[hb] = __builtin_convertvector(pv, bf16x8);
+            df[hb] = __builtin_convertvector(dv8, bf16x8);
+          }
+        };
+        if (need_mask)
+          softmax_grad(std::true_type{});
+        else
+          softmax_grad(std::false_type{});
+        // dV += P^T dO and dK += dS^T Q over these 32 rows (scale applied at the end).
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const int c = 2 * mb + cc;
+            dv[db] = mfma32(pf[cc], frag_tr_swz(st.dout, 16 * c, 32 * db, lane), dv[db]);
+            dk[db] = mfma32(df[cc], frag_tr_swz(st.q, 16 * c, 32 * db, lane), dk[db]);
+          }
         }
       }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) *(bf16x8*)(dst_row + 16 * c) = df[c];
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) *(bf16x8*)(dst_row + 16 * c) = zero8();
     }
-    __syncthreads();
-
-    // dQ tile (64 x 64) = dS (64 x 128 keys) K (128 x 64); wavefront w owns
-    // query rows 32*(w/2) .. and columns 32*(w%2) ..
-    {
-      const int qbk = w >> 1, dbk = w & 1;
-      f32x16 acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-#pragma unroll
-      for (int c = 0; c < kBN / 16; ++c)
-        acc = mfma32(frag_tr(dSt, kLDT, 16 * c, 32 * qbk, lane), frag_tr(Ks, kLD, 16 * c, 32 * dbk, lane),
-                     acc);
-      const int d = 32 * dbk + l32;
-      if (d < hd) {
-        float* base = a.dq_acc + (long)hq * hd + d;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int q = qb + 32 * qbk + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          if (q < L) unsafeAtomicAdd(base + (bos + q) * qs, acc[r] * a.scale);
-        }
-      }
-    }
+    if (++buf == kStages) buf = 0;
   }
 
   // dK, dV rows of this wavefront: register r holds key wk_lo + 8*(r/4) + 4*h2 + r%4.
+  float* dk_g = a.dk_acc + (long)bos * ks + g * hd;
+  float* dv_g = a.dv_acc + (long)bos * ks + g * hd;
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
     const int d = 32 * db + l32;
@@ -312,58 +324,243 @@ __global__ __launch_bounds__(256, 2) void bwd_main_kernel(BwdArgs a) {
     for (int r = 0; r < 16; ++r) {
       const int key = wk_lo + 8 * (r >> 2) + 4 * h2 + (r & 3);
       if (key < L) {
-        const long off = (bos + key) * ks + (long)g * hd + d;
-        unsafeAtomicAdd(a.dk_acc + off, dk[db][r] * a.scale);
-        unsafeAtomicAdd(a.dv_acc + off, dv[db][r]);
+        unsafeAtomicAdd(dk_g + key * ks + d, dk[db][r] * a.scale);
+        unsafeAtomicAdd(dv_g + key * ks + d, dv[db][r]);
       }
     }
   }
 }
 
+constexpr int kQT = 128;  // query rows per dQ workgroup (4 wavefronts x 32)
+constexpr int kKT = 64;   // keys per dQ step
+
+// One stage of the key-side ring buffer of the dQ kernel.
+struct __attribute__((aligned(16))) KStage {
+  bf16 k[kKT * kD];  // K tile, swizzled [key][d]
+  bf16 v[kKT * kD];  // V tile, swizzled [key][d]
+};
+
+// dQ for one 128-row query tile of one head.  Transposed products keep each
+// query row on a lane: S^T = K Q^T and dP^T = V dO^T (accumulators seeded
+// with -LSE/scale and -D of the lane's row), P^T = exp2(S^T scale log2 e),
+// dS^T = P^T dP^T, dQ^T += K^T dS^T with K^T from the row-major K tile
+// through transposing reads.  dQ is written once, in the output type.
+template <typename TIn, bool kDirect>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  __shared__ KStage stage[kStages];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const int seq = blockIdx.z, hq = blockIdx.y;
+  const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest (last) query tiles first
+  const int bos = a.cu_seqlens[seq];
+  const int L = a.cu_seqlens[seq + 1] - bos;
+  const int q0 = qt * kQT;
+  if (q0 >= L) return;
+
+  const int hd = a.head_dim, T = a.total_tokens, window = a.window;
+  const int g = hq / (a.num_q_heads / a.num_kv_heads);
+  const int qs = a.num_q_heads * hd, ks = a.num_kv_heads * hd;
+  const TIn* __restrict__ Qh = (const TIn*)a.q + (long)bos * qs + hq * hd;
+  const TIn* __restrict__ dOh = (const TIn*)a.dout + (long)bos * qs + hq * hd;
+  const TIn* __restrict__ Kg = (const TIn*)a.k + (long)bos * ks + g * hd;
+  const TIn* __restrict__ Vg = (const TIn*)a.v + (long)bos * ks + g * hd;
+
+  const int kend = min(L, q0 + kQT);
+  const int kbeg = window > 0 ? max(0, q0 - window + 1) : 0;
+  const int t0 = kbeg / kKT, t1 = (kend + kKT - 1) / kKT;
+
+  // Direct path: 2 + 2 VMEM instructions per wavefront per key tile.
+  auto prefetch = [&](int t, int buf) {
+    const int k0 = min(t, t1 - 1) * kKT;
+    KStage& st = stage[buf];
+    if constexpr (kDirect) {
+      stage_direct<kKT>(st.k, (const bf16*)Kg, k0, L, ks, w, lane);
+      stage_direct<kKT>(st.v, (const bf16*)Vg, k0, L, ks, w, lane);
+    } else {
+      stage_regs<kKT>(st.k, Kg, k0, L, ks, hd, tid);
+      stage_regs<kKT>(st.v, Vg, k0, L, ks, hd, tid);
+    }
+  };
+
+  // This lane's query row (column n of the transposed products) and its Q and
+  // dO fragments (B operands), plus its row statistics.
+  const int qrow = q0 + 32 * w + l32;
+  const int qcl = min(qrow, L - 1);
+  bf16x8 qf[4], of[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int d0 = 16 * c + 8 * h2;
+    qf[c] = d0 < hd ? load8(Qh + qcl * qs + d0) : zero8();
+    of[c] = d0 < hd ? load8(dOh + qcl * qs + d0) : zero8();
+  }
+  const float nlse = a.nlse[(long)hq * T + bos + qcl];
+  const float nD = a.ndelta[(long)hq * T + bos + qcl];
+  issue_fence();
+  prefetch(t0, 0);
+  issue_fence();
+  prefetch(t0 + 1, 1);
+  issue_fence();
+
+  f32x16 acc[2];  // dQ^T: register r of block db holds d = 32*db + 8*(r/4) + 4*h2 + r%4
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { acc[0][i] = 0.0f; acc[1][i] = 0.0f; }
+
+  const float sl2 = a.scale_log2;
+  const int krow_base = row_perm(l32);
+  const int wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
+
+  int buf = 0;
+  for (int t = t0; t < t1; ++t) {
+    if constexpr (kDirect) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    lds_barrier();
+    {
+      int nb = buf + 2;
+      if (nb >= kStages) nb -= kStages;
+      prefetch(t + 2, nb);
+      issue_fence();
+    }
+    const KStage& st = stage[buf];
+    const int kb = t * kKT;
+    if (++buf == kStages) buf = 0;
+    if (kb > wq_hi) continue;                                      // all keys after all rows
+    if (window > 0 && wq_lo - (kb + kKT - 1) >= window) continue;  // all keys left of window
+
+    // S^T and dP^T for two 32-key blocks; register r of block blk holds key
+    // kb + 32*blk + 16*(r/8) + 8*h2 + r%8 (A rows permuted).
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { s[blk][i] = nlse; dp[blk][i] = nD; }
+      const int kr = krow_base + 32 * blk;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        s[blk] = mfma32(frag_row(st.k, kr, 16 * c + 8 * h2), qf[c], s[blk]);
+        dp[blk] = mfma32(frag_row(st.v, kr, 16 * c + 8 * h2), of[c], dp[blk]);
+      }
+    }
+    const bool need_mask = (kb + kKT - 1 > wq_lo) || (window > 0 && wq_hi - kb >= window);
+    // key index 32*blk + 16*(r/8) + r%8 (+ 8*h2) is visible iff lo <= idx < hi
+    const int lo = window > 0 ? qrow - window + 1 - kb - 8 * h2 : -0x7fffffff;
+    const int hi = qrow + 1 - kb - 8 * h2;
+    bf16x8 df[4];
+    auto grad = [&](auto masked) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        f32x8 v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 8 * (c & 1) + i;
+          float p = fast_exp2(s[c >> 1][r] * sl2);
+          if constexpr (decltype(masked)::value) {
+            const int idx = 16 * c + i;
+            p = (idx >= lo && idx < hi) ? p : 0.0f;
+          }
+          v[i] = p * dp[c >> 1][r];
+        }
+        df[c] = __builtin_convertvector(v, bf16x8);
+      }
+    };
+    if (need_mask)
+      grad(std::true_type{});
+    else
+      grad(std::false_type{});
+    // dQ^T += K^T dS^T (chunk c = keys 16c .. 16c+15 of the tile).
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[db] = mfma32(frag_tr_swz(st.k, 16 * c, 32 * db, lane), df[c], acc[db]);
+    }
+  }
+
+  if (qrow < L) {
+    TIn* dq = (TIn*)a.dq + (long)(bos + qrow) * qs + hq * hd;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const int d = 32 * db + 8 * gi + 4 * h2;
+        if (d < hd) {
+          f32x4 v = {acc[db][4 * gi] * a.scale, acc[db][4 * gi + 1] * a.scale, acc[db][4 * gi + 2] * a.scale,
+                     acc[db][4 * gi + 3] * a.scale};
+          store4(dq + d, v);
+        }
+      }
+    }
+  }
+}
+
+int flat_blocks(long work_items) {
+  const long b = (work_items + kFlatThreads - 1) / kFlatThreads;
+  return (int)(b < 1 ? 1 : (b > 1024 ? 1024 : b));
+}
+
 }  // namespace
+
+int bwd_pre_blocks(int total_tokens, int hq) { return flat_blocks((long)total_tokens * hq * 8); }
 
 BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   BwdWorkspace w;
-  w.delta = up((size_t)hq * total_tokens * sizeof(float));
-  w.dq_acc = up((size_t)total_tokens * hq * d * sizeof(float));
+  w.ndelta = up((size_t)hq * total_tokens * sizeof(float));
+  w.nlse = w.ndelta;
   w.dk_acc = up((size_t)total_tokens * hkv * d * sizeof(float));
   w.dv_acc = w.dk_acc;
-  w.total = w.delta + w.dq_acc + w.dk_acc + w.dv_acc;
+  w.dsink_part = up((size_t)bwd_pre_blocks(total_tokens, hq) * hq * sizeof(float));
+  w.total = w.ndelta + w.nlse + w.dk_acc + w.dv_acc + w.dsink_part;
   return w;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t stream,
                       const hipEvent_t* events) {
-  const int T = a.total_tokens;
-  dim3 rows((T + kRowsPerBlock - 1) / kRowsPerBlock, a.num_q_heads);
-  if (T == 0) rows.x = 1;  // still zero dsinks
-  dim3 grid((max_seqlen + kBN - 1) / kBN, a.num_q_heads, num_seqs);
+  const int T = a.total_tokens, Hq = a.num_q_heads;
+  const int pre_blocks = bwd_pre_blocks(T, Hq);
+  const size_t bins_bytes = (size_t)Hq * sizeof(float);
+  const long chunks = (long)T * 2 * a.num_kv_heads * a.head_dim / 8;
+  const int conv_blocks = T > 0 ? flat_blocks(chunks) : 0;
+  const int post_blocks = conv_blocks + (Hq + 3) / 4;
+  const dim3 grid_kv((max_seqlen + kBN - 1) / kBN, Hq, num_seqs);
+  const dim3 grid_q((max_seqlen + kQT - 1) / kQT, Hq, num_seqs);
+  const bool direct = dtype == 0 && a.head_dim == kD;
   auto mark = [&](int i) { return events ? hipEventRecord(events[i], stream) : hipSuccess; };
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return e;
   if (dtype == 0)
-    hipLaunchKernelGGL(bwd_pre_kernel<bf16>, rows, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_pre_kernel<bf16>, dim3(pre_blocks), dim3(kFlatThreads), bins_bytes, stream, a);
   else
-    hipLaunchKernelGGL(bwd_pre_kernel<float>, rows, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_pre_kernel<float>, dim3(pre_blocks), dim3(kFlatThreads), bins_bytes, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = mark(1)) != hipSuccess) return e;
   if (T > 0) {
-    if (dtype == 0)
-      hipLaunchKernelGGL(bwd_main_kernel<bf16>, grid, dim3(256), 0, stream, a);
+    if (direct)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, true>), grid_kv, dim3(256), 0, stream, a);
+    else if (dtype == 0)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, false>), grid_kv, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL(bwd_main_kernel<float>, grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<float, false>), grid_kv, dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark(2)) != hipSuccess) return e;
   if (T > 0) {
-    if (dtype == 0)
-      hipLaunchKernelGGL(bwd_post_kernel<bf16>, rows, dim3(256), 0, stream, a);
+    if (direct)
+      hipLaunchKernelGGL((bwd_dq_kernel<bf16, true>), grid_q, dim3(256), 0, stream, a);
+    else if (dtype == 0)
+      hipLaunchKernelGGL((bwd_dq_kernel<bf16, false>), grid_q, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL(bwd_post_kernel<float>, rows, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<float, false>), grid_q, dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  return mark(3);
+  if ((e = mark(3)) != hipSuccess) return e;
+  if (dtype == 0)
+    hipLaunchKernelGGL(bwd_post_kernel<bf16>, dim3(post_blocks), dim3(kFlatThreads), 0, stream, a, conv_blocks,
+                       pre_blocks);
+  else
+    hipLaunchKernelGGL(bwd_post_kernel<float>, dim3(post_blocks), dim3(kFlatThreads), 0, stream, a, conv_blocks,
+                       pre_blocks);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return mark(4);
 }
 
 }  // namespace sinkattn

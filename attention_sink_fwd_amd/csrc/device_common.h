@@ -92,6 +92,83 @@ __device__ __forceinline__ int row_perm(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
+// ---------------------------------------------------------------------------
+// Swizzled LDS tiles: rows of 64 bf16 (128 bytes, no padding).  The 16-byte
+// chunk j of row r is stored in slot j ^ f(r), f(r) = bit-reverse of the three
+// bits (r >> 1) & 7.  With 64 four-byte banks (two rows per bank sweep) this
+// keeps both access patterns free of bank conflicts: 16 lanes reading one
+// chunk from 16 consecutive rows (operand reads), and 16 lanes reading two
+// adjacent chunks from 4 consecutive rows (transposing reads).
+__device__ __forceinline__ int swz_f(int r) {
+  const int x = (r >> 1) & 7;
+  return ((x & 1) << 2) | (x & 2) | ((x & 4) >> 2);
+}
+__device__ __forceinline__ int swz(int r, int col) {
+  return r * 64 + ((((col >> 3) ^ swz_f(r))) << 3) + (col & 7);
+}
+
+// 8 consecutive elements X[r][col .. col+7] (col % 8 == 0) of a swizzled tile.
+__device__ __forceinline__ bf16x8 frag_row(const bf16* X, int r, int col) {
+  return *(const bf16x8*)(X + swz(r, col));
+}
+
+// Operand fragment with 8 consecutive contraction indices k for lane index n
+// from a swizzled tile X[k][n]: lane l receives X[k0 + 8*(l/32) + s][n0 + l%32],
+// s = 0..7, through two transposing LDS reads (see frag_tr).
+__device__ __forceinline__ bf16x8 frag_tr_swz(const bf16* X, int k0, int n0, int lane) {
+  const int G = lane >> 4, j = lane & 15;
+  const int r = k0 + 8 * (G >> 1) + (j >> 2);
+  const int col = n0 + 16 * (G & 1) + 4 * (j & 3);
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS i16x4*)(X + swz(r, col)));
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS i16x4*)(X + swz(r + 4, col)));
+  i16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// Stage rows row0 .. row0+kRows-1 (clamped to nvalid-1) of a bf16 tensor with
+// row stride `stride` into a swizzled LDS tile using direct global->LDS loads
+// (global_load_lds_dwordx4: lane l of one instruction fills LDS bytes
+// base + 16*l).  Requires head_dim == 64.  Issues kRows/32 VMEM instructions
+// per wavefront of a 256-thread workgroup.
+template <int kRows>
+__device__ __forceinline__ void stage_direct(bf16* tile, const bf16* g, int row0, int nvalid, int stride,
+                                             int w, int lane) {
+#pragma unroll
+  for (int i = 0; i < kRows / 32; ++i) {
+    const int blk = (kRows / 32) * w + i;  // 1 KB block = 8 rows
+    const int r = 8 * blk + (lane >> 3);
+    const int j = (lane & 7) ^ swz_f(r);  // chunk that belongs in this slot
+    const int grow = min(row0 + r, nvalid - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(g + grow * stride + 8 * j), (SA_LDS void*)(tile + 512 * blk),
+                                     16, 0, 0);
+  }
+}
+
+// Same tile through registers: any input type, zero for rows >= nvalid and
+// columns >= hd.
+template <int kRows, typename TIn>
+__device__ __forceinline__ void stage_regs(bf16* tile, const TIn* g, int row0, int nvalid, int stride, int hd,
+                                           int tid) {
+#pragma unroll
+  for (int i = 0; i < kRows / 32; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c >> 3, j = (c & 7) ^ swz_f(r);
+    const bool ok = row0 + r < nvalid && 8 * j < hd;
+    *(bf16x8*)(tile + 8 * c) = ok ? load8(g + (row0 + r) * stride + 8 * j) : zero8();
+  }
+}
+
+// Compiler-level fence: keeps the order of memory operations in the source
+// (the explicit vmcnt waits below count instructions in issue order).
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+
+// Workgroup barrier for LDS hand-offs between wavefronts.  It waits only for
+// this wavefront's own LDS operations (lgkmcnt), not for outstanding global
+// loads, stores or atomics, which __syncthreads() would also drain.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);

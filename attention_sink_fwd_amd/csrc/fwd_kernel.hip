@@ -16,6 +16,8 @@
 // straight from registers; V^T comes from the row-major V tile through the
 // transposing LDS read.  The epilogue writes O = acc / l and
 // LSE = m + ln(l) (natural log, sink included).
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -33,7 +35,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Ks[kBN * kLD];
   __shared__ __attribute__((aligned(16))) bf16 Vs[kBN * kLD];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int h2 = lane >> 5, l32 = lane & 31;
   const int seq = blockIdx.z, hq = blockIdx.y;
   const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest (last) query tiles first
@@ -59,6 +62,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
 
   const int window = a.window;
+  const int wlim = window > 0 ? window : 0x7fffffff;
   const int kend = min(L, q0 + kBM);
   const int kbeg = window > 0 ? max(0, q0 - window + 1) : 0;
   const int t0 = kbeg / kBN, t1 = (kend + kBN - 1) / kBN;
@@ -99,9 +103,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
   if (t0 < t1) gload(t0);
   for (int t = t0; t < t1; ++t) {
-    __syncthreads();  // every wavefront is done with the previous tile
+    lds_barrier();  // every wavefront is done with the previous tile
     sstore();
-    __syncthreads();
+    lds_barrier();
     if (t + 1 < t1) gload(t + 1);
 
     const int kb = t * kBN;
@@ -121,20 +125,26 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
     const bool need_mask = (kb + kBN - 1 > wq_lo) || (window > 0 && wq_hi - kb >= window);
     float mx = -__builtin_inff();
+    auto scale_mask = [&](auto masked) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+      for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[blk][r] * sl2;
-        if (need_mask) {
-          const int key = kb + 32 * blk + 16 * (r >> 3) + 8 * h2 + (r & 7);
-          const bool vis = key <= qrow && (window == 0 || qrow - key < window);
-          x = vis ? x : -__builtin_inff();
+        for (int r = 0; r < 16; ++r) {
+          float x = s[blk][r] * sl2;
+          if constexpr (decltype(masked)::value) {
+            const int key = kb + 32 * blk + 16 * (r >> 3) + 8 * h2 + (r & 7);
+            const int dist = qrow - key;  // visible iff 0 <= dist < wlim
+            x = ((dist >= 0) & (dist < wlim)) ? x : -__builtin_inff();
+          }
+          s[blk][r] = x;
+          mx = fmaxf(mx, x);
         }
-        s[blk][r] = x;
-        mx = fmaxf(mx, x);
       }
-    }
+    };
+    if (need_mask)
+      scale_mask(std::true_type{});
+    else
+      scale_mask(std::false_type{});
     mx = fmaxf(mx, __shfl_xor(mx, 32));  // the other half of the row
     const float mnew = fmaxf(m, mx);
     const float muse = (mnew == -__builtin_inff()) ? 0.0f : mnew;

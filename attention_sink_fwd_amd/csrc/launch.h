@@ -31,10 +31,11 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dsinks;
-  float* delta;   // workspace: D_i = dO_i . O_i, [Hq, T]
-  float* dq_acc;  // workspace: float dQ accumulator, [T, Hq, d]
+  float* ndelta;  // workspace: -D_i = -(dO_i . O_i), [Hq, T]
+  float* nlse;    // workspace: -LSE_i / scale, [Hq, T]
   float* dk_acc;  // workspace: float dK accumulator, [T, Hkv, d]
   float* dv_acc;  // workspace: float dV accumulator, [T, Hkv, d]
+  float* dsink_part;  // workspace: per-preprocess-block dS partials, [blocks, Hq]
   int num_q_heads, num_kv_heads, head_dim, total_tokens, window;
   float scale;
   float scale_log2;
@@ -42,12 +43,12 @@ struct BwdArgs {
 
 // Workspace sections (bytes, each rounded up to 256).
 struct BwdWorkspace {
-  size_t delta, dq_acc, dk_acc, dv_acc, total;
+  size_t ndelta, nlse, dk_acc, dv_acc, dsink_part, total;
 };
 BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d);
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s);
-// events: NULL, or four events recorded around the three kernels.
+// events: NULL, or five events recorded around the four kernels.
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s,
                       const hipEvent_t* events);
 

@@ -9,8 +9,8 @@ L=4096, causal, bf16.
 
 Prints ONE JSON line.  Throughput counts algorithmic flops (14*d per visible
 query/key pair per query head: 4d forward, 10d backward).  The roofline
-object is for the dominant kernel (the main backward kernel), timed live
-with HIP events recorded around it on the stream it runs on.
+object is for the dominant (longest) matrix-core kernel, timed live with HIP
+events recorded around it on the stream it runs on.
 """
 from __future__ import annotations
 
@@ -30,8 +30,7 @@ if ROOT not in sys.path:
 METRIC = "sink-attn fwd+bwd TFLOP/s + % bf16 MFMA peak, Hq64/Hkv8/d64 L=4096 causal"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_traffic.json")
-BWD_SOURCE = os.path.join(ROOT, "attention_sink_fwd_amd", "csrc", "bwd_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 class Hip:
@@ -62,26 +61,27 @@ class Hip:
         self.lib.hipEventDestroy(e)
 
 
-def traffic_for_current_kernel():
-    """HBM bytes per launch of the main backward kernel from rocprofv3 counters.
+def traffic_for_current_kernel(kernel):
+    """HBM bytes per launch of `kernel` from rocprofv3 FETCH_SIZE + WRITE_SIZE.
 
-    Taken from profiles/bwd_main_traffic.json, and only while the kernel
-    source is the one the counters were measured on; otherwise None.
+    Taken from profiles/traffic.json, and only while the kernel's source file
+    is byte-identical to the one the counters were measured on; else None.
     """
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-        with open(BWD_SOURCE, "rb") as f:
+            entry = json.load(f)[kernel]
+        with open(os.path.join(ROOT, entry["source"]), "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
-        if t.get("source_sha256") != sha:
+        if entry.get("source_sha256") != sha:
             return None
-        return float(t["bytes_per_launch"])
-    except (OSError, ValueError, KeyError):
+        return float(entry["bytes_per_launch"])
+    except (OSError, ValueError, KeyError, TypeError):
         return None
 
 
-def cpu_baseline(inp, w):
-    """The oracle (unchanged) on one KV group of the same workload, timed on the host."""
+def cpu_baseline(inp, w, min_seconds=10.0):
+    """The oracle (unchanged), timed on the host over whole KV groups of the
+    same workload: group after group until at least ``min_seconds`` passed."""
     import oracle
 
     try:
@@ -90,22 +90,39 @@ def cpu_baseline(inp, w):
     except Exception:  # noqa: BLE001
         threads = None
     grp = w.num_q_heads // w.num_kv_heads
-    heads = list(range(grp))
+    done = 0
     t0 = time.perf_counter()
-    oracle.forward(inp["q"], inp["k"], inp["v"], inp["sinks"], inp["cu_seqlens"],
-                   w.softmax_scale, w.window, heads=heads)
-    oracle.backward(inp["q"], inp["k"], inp["v"], inp["sinks"], inp["dout"], inp["cu_seqlens"],
-                    w.softmax_scale, w.window, kv_heads=[0])
+    while done < w.num_kv_heads and (time.perf_counter() - t0) < min_seconds:
+        g = done
+        oracle.forward(inp["q"], inp["k"], inp["v"], inp["sinks"], inp["cu_seqlens"],
+                       w.softmax_scale, w.window, heads=list(range(g * grp, (g + 1) * grp)))
+        oracle.backward(inp["q"], inp["k"], inp["v"], inp["sinks"], inp["dout"],
+                        inp["cu_seqlens"], w.softmax_scale, w.window, kv_heads=[g])
+        done += 1
     dt = time.perf_counter() - t0
-    flops = w.flops()["total"] * grp / w.num_q_heads
+    flops = w.flops()["total"] * done / w.num_kv_heads
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": threads if threads is not None else os.cpu_count(),
         "kind": "oracle",
-        "sample": (f"KV group 0 (query heads 0-{grp - 1}) of {w.name}: float64 forward + "
-                   f"backward, {flops / 1e9:.2f} GFLOP in {dt:.1f} s"),
+        "sample": (f"KV groups 0-{done - 1} (query heads 0-{done * grp - 1}) of {w.name}: "
+                   f"float64 forward + backward, {flops / 1e9:.1f} GFLOP in {dt:.1f} s"),
     }
+
+
+def calibrate_copy(nbytes=1 << 30):
+    """A plain copy kernel of known size for scaling rocprofv3's FETCH_SIZE /
+    WRITE_SIZE: torch.neg over float32 reads and writes nbytes each."""
+    import torch
+
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "torch.neg float32", "bytes_read_per_launch": nbytes,
+                      "bytes_written_per_launch": nbytes, "launches": 3}), flush=True)
 
 
 def main():
@@ -115,6 +132,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, help="workload id 1-5 (default 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a known-size copy kernel (for rocprofv3 counter scaling)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -122,6 +141,10 @@ def main():
               "on one GPU only: the kernel works on one GPU's head share and there is no "
               "multi-GPU path. Run with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     import torch
 
@@ -157,7 +180,7 @@ def main():
 
     K = args.steps
     sh = ctypes.c_void_p(stream.cuda_stream)
-    evs = [[hip.event() for _ in range(6)] for _ in range(K)]
+    evs = [[hip.event() for _ in range(7)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -166,7 +189,7 @@ def main():
         sa.sink_attn_fwd(q, k, v, s, cu, w.max_seqlen, w.softmax_scale, w.window, o=o, lse=lse,
                          stream=stream)
         hip.record(e[1], sh)
-        arr = (ctypes.c_void_p * 4)(e[2].value, e[3].value, e[4].value, e[5].value)
+        arr = (ctypes.c_void_p * 5)(e[2].value, e[3].value, e[4].value, e[5].value, e[6].value)
         _lib.check(lib.sink_attn_set_bwd_events(arr))
         sa.sink_attn_bwd(q, k, v, s, o, lse, do, cu, w.max_seqlen, w.softmax_scale, w.window,
                          dq=dq, dk=dk, dv=dv, dsinks=ds, workspace=ws, stream=stream)
@@ -177,7 +200,7 @@ def main():
     def avg(a, b):
         return sum(hip.ms(evs[i][a], evs[i][b]) for i in range(K)) / K
 
-    k_fwd, k_pre, k_main, k_post = avg(0, 1), avg(2, 3), avg(3, 4), avg(4, 5)
+    k_fwd, k_pre, k_dkdv, k_dq, k_post = avg(0, 1), avg(2, 3), avg(3, 4), avg(4, 5), avg(5, 6)
     for row in evs:
         for e in row:
             hip.destroy(e)
@@ -185,8 +208,17 @@ def main():
     ms = (t1 - t0) * 1000.0 / K
     fl = w.flops()
     tflops = fl["total"] / (ms * 1e-3) / 1e12
-    main_tflops = fl["bwd"] / (k_main * 1e-3) / 1e12
-    traffic = traffic_for_current_kernel()
+    # Algorithmic flops per launch of each matrix-core kernel (FA convention,
+    # 2*d flops per visible pair per product): forward 2 products (S, PV);
+    # dK/dV kernel 4 of the 5 backward products (S, dP, dV, dK); dQ kernel the
+    # remaining one (dQ) -- its recomputed S and dP are not counted.
+    pairs = w.visible_pairs()
+    algo = {"fwd": 4.0 * w.head_dim * pairs, "bwd_dkdv": 8.0 * w.head_dim * pairs,
+            "bwd_dq": 2.0 * w.head_dim * pairs}
+    kms = {"fwd": k_fwd, "bwd_dkdv": k_dkdv, "bwd_dq": k_dq}
+    dom = max(kms, key=kms.get)
+    dom_tflops = algo[dom] / (kms[dom] * 1e-3) / 1e12
+    traffic = traffic_for_current_kernel(dom)
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -213,15 +245,16 @@ def main():
             "flops_per_step": fl["total"],
         },
         "pct_bf16_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "kernel_ms": {"fwd": round(k_fwd, 4), "bwd_pre": round(k_pre, 4),
-                      "bwd_main": round(k_main, 4), "bwd_post": round(k_post, 4)},
+        "kernel_ms": {"fwd": round(k_fwd, 4), "bwd_pre": round(k_pre, 4), "bwd_dkdv": round(k_dkdv, 4),
+                      "bwd_dq": round(k_dq, 4), "bwd_post": round(k_post, 4)},
+        "kernel_tflops": {k: round(algo[k] / (kms[k] * 1e-3) / 1e12, 1) for k in kms},
         "roofline": {
-            "kernel": "bwd_main_kernel",
+            "kernel": dom,
             "bound": "mfma",
-            "achieved": round(main_tflops, 2),
+            "achieved": round(dom_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
+            "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
         },
     }

@@ -84,9 +84,9 @@ typedef struct {
   int32_t num_seqs;          /* >= 1 */
   int32_t max_seqlen;        /* >= every sequence length; 0 allowed only if total_tokens == 0 */
   int32_t total_tokens;      /* T = cu_seqlens[num_seqs] */
-  int32_t num_q_heads;       /* Hq >= 1 */
+  int32_t num_q_heads;       /* 1 <= Hq <= 8192 */
   int32_t num_kv_heads;      /* Hkv >= 1, Hq % Hkv == 0 */
-  int32_t head_dim;          /* d: a multiple of 8 in [8, 64] */
+  int32_t head_dim;          /* d: a multiple of 8 in [8, 64]; T * Hq * d < 2^31 */
   float softmax_scale;       /* tau > 0, finite; usually 1/sqrt(d) */
   int32_t causal;            /* must be 1 (keys after the query are never visible) */
   int32_t window;            /* 0 = unlimited; else key j visible iff i - window < j <= i */
@@ -142,13 +142,13 @@ int sink_attn_bwd(const sink_attn_params *p, const void *q, const void *k, const
 
 /*
  * Instrumentation (benchmarks and profilers).  Sets, for the calling thread,
- * four hipEvent_t handles that every later sink_attn_bwd call on this thread
+ * five hipEvent_t handles that every later sink_attn_bwd call on this thread
  * records on its stream: events[0] before the preprocess kernel, events[1]
- * before the main kernel, events[2] before the epilogue kernel and events[3]
- * after it, so hipEventElapsedTime(events[1], events[2]) is the main
- * kernel's duration.  The four handles are copied; the caller keeps owning
- * the events.  Pass NULL to stop recording.  Returns SINK_ATTN_OK, or
- * SINK_ATTN_ERR_INVALID_ARG if one of the four handles is NULL.
+ * before the dK/dV kernel, events[2] before the dQ kernel, events[3] before
+ * the epilogue kernel and events[4] after it, so consecutive pairs time the
+ * four kernels.  The handles are copied; the caller keeps owning the events.
+ * Pass NULL to stop recording.  Returns SINK_ATTN_OK, or
+ * SINK_ATTN_ERR_INVALID_ARG if one of the five handles is NULL.
  */
 int sink_attn_set_bwd_events(void *const *events);
 
