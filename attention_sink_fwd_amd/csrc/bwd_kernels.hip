@@ -146,7 +146,11 @@ constexpr int kStages = 3;
 // of its KV group; summed with float atomics into the workspace).
 template <typename TIn, bool kDirect>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ QStage stage[kStages];
+  // Three separate LDS objects (not an array): with every access naming its
+  // stage at compile time, the compiler can tell that reading one stage does
+  // not alias the direct-to-LDS loads still landing in another, and inserts
+  // no wait for them.
+  __shared__ QStage st0, st1, st2;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
@@ -175,15 +179,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
   // Prefetch query tile t (clamped to the last visible tile) into stage buf.
   // Direct path: exactly kPrefetchOps VMEM instructions per wavefront.
-  auto prefetch = [&](int t, int buf) {
+  auto prefetch = [&](int t, QStage& st) {
     const int q0 = min(t, qt1 - 1) * kBM;
-    QStage& st = stage[buf];
     if constexpr (kDirect) {
       stage_direct<kBM>(st.q, (const bf16*)Qh, q0, L, qs, w, lane);
       stage_direct<kBM>(st.dout, (const bf16*)dOh, q0, L, qs, w, lane);
       const float* src = (w == 1) ? nD_h : nlse_h;
       float* dst = (w == 0) ? st.nlse : (w == 1 ? st.ndelta : st.spare);
-      __builtin_amdgcn_global_load_lds((const void*)(src + min(q0 + lane, L - 1)), (SA_LDS void*)dst, 4, 0, 0);
+      lds_dma4(src + min(q0 + lane, L - 1), dst);
     } else {
       stage_regs<kBM>(st.q, Qh, q0, L, qs, hd, tid);
       stage_regs<kBM>(st.dout, dOh, q0, L, qs, hd, tid);
@@ -209,10 +212,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       vf[c] = d0 < hd ? load8(Vg + krow * ks + d0) : zero8();
     }
   }
+  wait_vmem_all();  // fragments resident before the loop (see wait_vmem_all)
   issue_fence();
-  prefetch(qt0, 0);
+  prefetch(qt0, st0);
   issue_fence();
-  prefetch(qt0 + 1, 1);
+  prefetch(qt0 + 1, st1);
   issue_fence();
 
   f32x16 dk[2], dv[2];
@@ -222,20 +226,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const float sl2 = a.scale_log2;
   const int qrow_base = row_perm(l32);
 
-  int buf = 0;
-  for (int t = qt0; t < qt1; ++t) {
+  // One step: consume tile t from `st`, prefetch tile t+2 into `nx` (the
+  // stage consumed in the previous step).
+  auto step = [&](int t, const QStage& st, QStage& nx) {
     // Wait for this wavefront's part of tile t (only the next prefetch may
     // still be in flight), then make all parts visible.
     if constexpr (kDirect) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
     static_assert(kPrefetchOps == 5, "wait count");
-    lds_barrier();  // tile t visible; stage (t+2)%3 was last read in step t-1
-    {
-      int nb = buf + 2;
-      if (nb >= kStages) nb -= kStages;
-      prefetch(t + 2, nb);
-      issue_fence();
-    }
-    const QStage& st = stage[buf];
+    lds_barrier();  // tile t visible; `nx` was last read in the previous step
+    prefetch(t + 2, nx);
+    issue_fence();
     const int qb = t * kBM;
 
     const bool active = wk_lo < L && wk_lo <= qb + kBM - 1 && !(window > 0 && qb - wk_hi >= window);
@@ -310,7 +310,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         }
       }
     }
-    if (++buf == kStages) buf = 0;
+  };
+  for (int t = qt0; t < qt1; t += kStages) {
+    step(t, st0, st2);
+    if (t + 1 < qt1) step(t + 1, st1, st0);
+    if (t + 2 < qt1) step(t + 2, st2, st1);
   }
 
   // dK, dV rows of this wavefront: register r holds key wk_lo + 8*(r/4) + 4*h2 + r%4.
@@ -397,6 +401,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
   const float nlse = a.nlse[(long)hq * T + bos + qcl];
   const float nD = a.ndelta[(long)hq * T + bos + qcl];
+  wait_vmem_all();  // fragments resident before the loop (see wait_vmem_all)
   issue_fence();
   prefetch(t0, 0);
   issue_fence();

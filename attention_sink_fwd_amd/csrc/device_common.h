@@ -125,11 +125,34 @@ __device__ __forceinline__ bf16x8 frag_tr_swz(const bf16* X, int k0, int n0, int
   return __builtin_bit_cast(bf16x8, c);
 }
 
+// Direct global->LDS loads (global_load_lds_dword / _dwordx4): lane l of one
+// instruction writes its 4 or 16 bytes to LDS at lds_base + size * l
+// (lds_base must be wavefront-uniform; it goes through M0).  Written as inline
+// assembly on purpose: the compiler's wait insertion cannot tell which LDS
+// bytes such a load writes, so for the builtin form it waits for every
+// outstanding vector-memory operation before each later LDS read, which would
+// expose the full latency of the prefetch.  Callers wait explicitly instead
+// (s_waitcnt vmcnt with the exact number of instructions issued since).
+// M0 is clobbered here; clang warns that a clobbered reserved register is not
+// preserved for the surrounding code.  These kernels use M0 for nothing else
+// (a CPU test compiles them and checks that every write of M0 sits in one of
+// these blocks), so nothing live is lost.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* g, const void* lds_base) {
+  const unsigned m0 = (unsigned)(uintptr_t)(SA_LDS const void*)lds_base;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* g, const void* lds_base) {
+  const unsigned m0 = (unsigned)(uintptr_t)(SA_LDS const void*)lds_base;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Stage rows row0 .. row0+kRows-1 (clamped to nvalid-1) of a bf16 tensor with
-// row stride `stride` into a swizzled LDS tile using direct global->LDS loads
-// (global_load_lds_dwordx4: lane l of one instruction fills LDS bytes
-// base + 16*l).  Requires head_dim == 64.  Issues kRows/32 VMEM instructions
-// per wavefront of a 256-thread workgroup.
+// row stride `stride` into a swizzled LDS tile with direct loads.  Requires
+// head_dim == 64.  Issues kRows/32 VMEM instructions per wavefront of a
+// 256-thread workgroup.
 template <int kRows>
 __device__ __forceinline__ void stage_direct(bf16* tile, const bf16* g, int row0, int nvalid, int stride,
                                              int w, int lane) {
@@ -139,8 +162,7 @@ __device__ __forceinline__ void stage_direct(bf16* tile, const bf16* g, int row0
     const int r = 8 * blk + (lane >> 3);
     const int j = (lane & 7) ^ swz_f(r);  // chunk that belongs in this slot
     const int grow = min(row0 + r, nvalid - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(g + grow * stride + 8 * j), (SA_LDS void*)(tile + 512 * blk),
-                                     16, 0, 0);
+    lds_dma16(g + grow * stride + 8 * j, tile + 512 * blk);
   }
 }
 
@@ -157,6 +179,12 @@ __device__ __forceinline__ void stage_regs(bf16* tile, const TIn* g, int row0, i
     *(bf16x8*)(tile + 8 * c) = ok ? load8(g + (row0 + r) * stride + 8 * j) : zero8();
   }
 }
+
+// s_waitcnt vmcnt(0) that the compiler's own wait insertion sees (so it also
+// stops tracking earlier loads as pending inside later loops).  gfx9
+// encoding: vmcnt bits [3:0] and [15:14] = 0, expcnt [6:4] = 7, lgkmcnt
+// [11:8] = 15 (no wait on those).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Compiler-level fence: keeps the order of memory operations in the source
 // (the explicit vmcnt waits below count instructions in issue order).

@@ -7,15 +7,21 @@
 //
 // One workgroup = one query head h, one sequence, a tile of 128 query rows;
 // four wavefronts own 32 rows each.  Keys/values of head g(h) stream through
-// LDS in tiles of 64 keys (coalesced 16-byte loads, prefetched into registers
-// one tile ahead).  Per tile a wavefront computes the transposed score block
-// S^T = K Q^T on the matrix cores, so each lane owns one query row and its
-// softmax statistics stay in the lane; the online softmax starts from the
-// sink (running max m = S_h, running sum l = 1), which is how the virtual
-// token enters without a value vector.  P^T (bf16) feeds O^T += V^T P^T
-// straight from registers; V^T comes from the row-major V tile through the
-// transposing LDS read.  The epilogue writes O = acc / l and
-// LSE = m + ln(l) (natural log, sink included).
+// a three-stage LDS ring in tiles of 64 keys (direct global->LDS loads into
+// XOR-swizzled rows, issued two tiles ahead; one barrier per tile).  Per tile
+// a wavefront computes the transposed score block S^T = K Q^T on the matrix
+// cores, so each lane owns one query row and its softmax statistics stay in
+// the lane; the online softmax starts from the sink (reference max m = S_h,
+// running sum l = 1), which is how the virtual token enters without a value
+// vector.  P^T (bf16) feeds O^T += V^T P^T straight from registers; V^T comes
+// from the row-major V tile through transposing LDS reads.  The epilogue
+// writes O = acc / l and LSE = m + ln(l) (natural log, sink included).
+//
+// The reference max m is only raised when a tile's max exceeds it by more
+// than kRescaleSlack (log2 units) in some row of the wavefront; otherwise the
+// tile is exponentiated against the old m (values up to 2^kRescaleSlack) and
+// the 32-register accumulator rescale is skipped.  The result is the same
+// softmax: m cancels between O's numerator and l.
 #include <type_traits>
 
 #include "device_common.h"
@@ -28,12 +34,17 @@ namespace {
 constexpr int kBM = 128;  // query rows per workgroup
 constexpr int kBN = 64;   // keys per LDS tile
 constexpr int kD = 64;    // padded head dimension
-constexpr int kLD = kD + 8;
+constexpr int kStages = 3;
+constexpr float kRescaleSlack = 8.0f;
 
-template <typename TIn>
+struct __attribute__((aligned(16))) KVStage {
+  bf16 k[kBN * kD];  // K tile, swizzled [key][d]
+  bf16 v[kBN * kD];  // V tile, swizzled [key][d]
+};
+
+template <typename TIn, bool kDirect>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kBN * kLD];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[kBN * kLD];
+  __shared__ KVStage stage[kStages];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
@@ -47,83 +58,95 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
   const int hd = a.head_dim;
   const int g = hq / (a.num_q_heads / a.num_kv_heads);
-  const TIn* __restrict__ Q = (const TIn*)a.q;
-  const TIn* __restrict__ K = (const TIn*)a.k;
-  const TIn* __restrict__ V = (const TIn*)a.v;
-  const long qs = (long)a.num_q_heads * hd, ks = (long)a.num_kv_heads * hd;
-
-  // This lane's query row (column n of S^T) and its Q fragments (B operand).
-  const int qrow = q0 + 32 * w + l32;
-  bf16x8 qf[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int d0 = 16 * c + 8 * h2;
-    qf[c] = (qrow < L && d0 < hd) ? load8(Q + (bos + qrow) * qs + (long)hq * hd + d0) : zero8();
-  }
+  const int qs = a.num_q_heads * hd, ks = a.num_kv_heads * hd;  // row strides (< 2^31 elements)
+  const TIn* __restrict__ Qh = (const TIn*)a.q + (long)bos * qs + hq * hd;
+  const TIn* __restrict__ Kg = (const TIn*)a.k + (long)bos * ks + g * hd;
+  const TIn* __restrict__ Vg = (const TIn*)a.v + (long)bos * ks + g * hd;
 
   const int window = a.window;
-  const int wlim = window > 0 ? window : 0x7fffffff;
   const int kend = min(L, q0 + kBM);
   const int kbeg = window > 0 ? max(0, q0 - window + 1) : 0;
   const int t0 = kbeg / kBN, t1 = (kend + kBN - 1) / kBN;
 
+  // Prefetch key tile t (clamped to the last tile) into stage buf; on the
+  // direct path exactly 4 VMEM instructions per wavefront.
+  auto prefetch = [&](int t, int buf) {
+    const int k0 = min(t, t1 - 1) * kBN;
+    KVStage& st = stage[buf];
+    if constexpr (kDirect) {
+      stage_direct<kBN>(st.k, (const bf16*)Kg, k0, L, ks, w, lane);
+      stage_direct<kBN>(st.v, (const bf16*)Vg, k0, L, ks, w, lane);
+    } else {
+      stage_regs<kBN>(st.k, Kg, k0, L, ks, hd, tid);
+      stage_regs<kBN>(st.v, Vg, k0, L, ks, hd, tid);
+    }
+  };
+
+  // This lane's query row (column n of S^T) and its Q fragments (B operand).
+  const int qrow = q0 + 32 * w + l32;
+  bf16x8 qf[4];
+  {
+    const int qcl = min(qrow, L - 1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int d0 = 16 * c + 8 * h2;
+      qf[c] = d0 < hd ? load8(Qh + qcl * qs + d0) : zero8();
+    }
+  }
+  wait_vmem_all();  // fragments resident before the loop (see wait_vmem_all)
+  issue_fence();
+  prefetch(t0, 0);
+  issue_fence();
+  prefetch(t0 + 1, 1);
+  issue_fence();
+
   // Online softmax state in the log2 domain, seeded with the sink.
   const float sink = a.sinks[hq];
-  float m = sink * kLog2e;                                    // -inf stays -inf
+  float m = sink * kLog2e;                                          // -inf stays -inf
   float l = (h2 == 0 && sink != -__builtin_inff()) ? 1.0f : 0.0f;  // counted once per row
   f32x16 o[2];
 #pragma unroll
   for (int i = 0; i < 16; ++i) { o[0][i] = 0.0f; o[1][i] = 0.0f; }
 
-  // Staging: 64 keys x 8 chunks of 8 = 512 chunks per tensor, 2 per thread.
-  bf16x8 kreg[2], vreg[2];
-  auto gload = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      const int key = t * kBN + row;
-      const bool ok = key < L && col < hd;
-      const long off = (bos + key) * ks + (long)g * hd + col;
-      kreg[i] = ok ? load8(K + off) : zero8();
-      vreg[i] = ok ? load8(V + off) : zero8();
-    }
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      *(bf16x8*)(Ks + row * kLD + col) = kreg[i];
-      *(bf16x8*)(Vs + row * kLD + col) = vreg[i];
-    }
-  };
-
   const int wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
   const float sl2 = a.scale_log2;
   const int krow_base = row_perm(l32);
 
-  if (t0 < t1) gload(t0);
+  int buf = 0;
   for (int t = t0; t < t1; ++t) {
-    lds_barrier();  // every wavefront is done with the previous tile
-    sstore();
+    // This wavefront's part of tile t has landed (only the next prefetch may
+    // still be in flight); the barrier makes every part visible and ends all
+    // reads of the stage the next prefetch overwrites.
+    if constexpr (kDirect) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     lds_barrier();
-    if (t + 1 < t1) gload(t + 1);
-
+    {
+      int nb = buf + 2;
+      if (nb >= kStages) nb -= kStages;
+      prefetch(t + 2, nb);
+      issue_fence();
+    }
+    const KVStage& st = stage[buf];
+    if (++buf == kStages) buf = 0;
     const int kb = t * kBN;
-    if (kb > wq_hi) continue;                                   // all keys after all rows
+    if (kb > wq_hi) continue;                                      // all keys after all rows
     if (window > 0 && wq_lo - (kb + kBN - 1) >= window) continue;  // all keys left of window
 
-    // S^T = K Q^T for two 32-key blocks.
+    // S^T = K Q^T for two 32-key blocks; register r of block blk holds key
+    // kb + 32*blk + 16*(r/8) + 8*h2 + r%8 (A rows permuted).
     f32x16 s[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[blk][i] = 0.0f;
-      const bf16* krow = Ks + (krow_base + 32 * blk) * kLD + 8 * h2;
+      const int kr = krow_base + 32 * blk;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) s[blk] = mfma32(*(const bf16x8*)(krow + 16 * c), qf[c], s[blk]);
+      for (int c = 0; c < 4; ++c) s[blk] = mfma32(frag_row(st.k, kr, 16 * c + 8 * h2), qf[c], s[blk]);
     }
 
     const bool need_mask = (kb + kBN - 1 > wq_lo) || (window > 0 && wq_hi - kb >= window);
+    // key index 32*blk + 16*(r/8) + r%8 (+ kb + 8*h2) is visible iff lo <= idx < hi
+    const int hi = qrow + 1 - kb - 8 * h2;
+    const int lo = window > 0 ? hi - window : -0x7fffffff;
     float mx = -__builtin_inff();
     auto scale_mask = [&](auto masked) {
 #pragma unroll
@@ -132,13 +155,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         for (int r = 0; r < 16; ++r) {
           float x = s[blk][r] * sl2;
           if constexpr (decltype(masked)::value) {
-            const int key = kb + 32 * blk + 16 * (r >> 3) + 8 * h2 + (r & 7);
-            const int dist = qrow - key;  // visible iff 0 <= dist < wlim
-            x = ((dist >= 0) & (dist < wlim)) ? x : -__builtin_inff();
+            const int idx = 32 * blk + 16 * (r >> 3) + (r & 7);
+            x = (idx >= lo && idx < hi) ? x : -__builtin_inff();
           }
           s[blk][r] = x;
-          mx = fmaxf(mx, x);
         }
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[blk][r], s[blk][r + 1]));
       }
     };
     if (need_mask)
@@ -146,10 +169,17 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     else
       scale_mask(std::false_type{});
     mx = fmaxf(mx, __shfl_xor(mx, 32));  // the other half of the row
-    const float mnew = fmaxf(m, mx);
-    const float muse = (mnew == -__builtin_inff()) ? 0.0f : mnew;
-    const float alpha = fast_exp2(m - muse);
-    m = mnew;
+    // Raise the reference max (and rescale the accumulator) only when some
+    // row of the wavefront outgrew it by more than the slack.
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - ((mnew == -__builtin_inff()) ? 0.0f : mnew));
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { o[0][i] *= alpha; o[1][i] *= alpha; }
+      m = mnew;
+    }
+    const float muse = (m == -__builtin_inff()) ? 0.0f : m;
     float rs = 0.0f;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -160,9 +190,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         rs += p;
       }
     }
-    l = l * alpha + rs;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { o[0][i] *= alpha; o[1][i] *= alpha; }
+    l += rs;
 
     // P^T fragments: chunk c covers keys 16c .. 16c+15 of the tile.
     bf16x8 pf[4];
@@ -177,14 +205,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[db] = mfma32(frag_tr(Vs, kLD, 16 * c, 32 * db, lane), pf[c], o[db]);
+      for (int c = 0; c < 4; ++c) o[db] = mfma32(frag_tr_swz(st.v, 16 * c, 32 * db, lane), pf[c], o[db]);
     }
   }
 
   const float lt = l + __shfl_xor(l, 32);
   if (qrow < L) {
     const float inv = 1.0f / lt;
-    TIn* O = (TIn*)a.o + (bos + qrow) * qs + (long)hq * hd;
+    TIn* O = (TIn*)a.o + (long)(bos + qrow) * qs + hq * hd;
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
 #pragma unroll
@@ -205,10 +233,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t stream) {
   dim3 grid((max_seqlen + kBM - 1) / kBM, a.num_q_heads, num_seqs);
-  if (dtype == 0)
-    hipLaunchKernelGGL(fwd_kernel<bf16>, grid, dim3(256), 0, stream, a);
+  if (dtype == 0 && a.head_dim == kD)
+    hipLaunchKernelGGL((fwd_kernel<bf16, true>), grid, dim3(256), 0, stream, a);
+  else if (dtype == 0)
+    hipLaunchKernelGGL((fwd_kernel<bf16, false>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(fwd_kernel<float>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<float, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
