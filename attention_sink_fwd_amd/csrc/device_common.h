@@ -127,7 +127,8 @@ __device__ __forceinline__ bf16x8 frag_tr_swz(const bf16* X, int k0, int n0, int
 
 // Direct global->LDS loads (global_load_lds_dword / _dwordx4): lane l of one
 // instruction writes its 4 or 16 bytes to LDS at lds_base + size * l
-// (lds_base must be wavefront-uniform; it goes through M0).  Written as inline
+// (lds_base must be wavefront-uniform; it goes through M0, and one wait state
+// separates the M0 write from the load that reads it).  Written as inline
 // assembly on purpose: the compiler's wait insertion cannot tell which LDS
 // bytes such a load writes, so for the builtin form it waits for every
 // outstanding vector-memory operation before each later LDS read, which would
@@ -141,11 +142,11 @@ __device__ __forceinline__ bf16x8 frag_tr_swz(const bf16* X, int k0, int n0, int
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_dma16(const void* g, const void* lds_base) {
   const unsigned m0 = (unsigned)(uintptr_t)(SA_LDS const void*)lds_base;
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
 }
 __device__ __forceinline__ void lds_dma4(const void* g, const void* lds_base) {
   const unsigned m0 = (unsigned)(uintptr_t)(SA_LDS const void*)lds_base;
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 

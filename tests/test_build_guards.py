@@ -50,7 +50,8 @@ def test_no_scratch_and_m0_only_in_dma_blocks(source):
         lines = [l.strip() for l in body.splitlines()]
         for i, line in enumerate(lines):
             if re.search(r"\bm0\b", line) and not line.startswith(";"):
-                ok = line.startswith("s_mov_b32 m0,") and "global_load_lds" in lines[i + 1]
+                ok = (line.startswith("s_mov_b32 m0,") and lines[i + 1] == "s_nop 0"
+                      and "global_load_lds" in lines[i + 2])
                 ok = ok or line.startswith("global_load_lds")
                 assert ok, f"{name}: unexpected use of M0: {line}"
     for m in re.finditer(r"\.private_segment_fixed_size:\s+(\d+)", asm):
