@@ -61,18 +61,25 @@ class Hip:
         self.lib.hipEventDestroy(e)
 
 
+def sources_sha256(paths):
+    """sha256 over the concatenated bytes of the given repo files, in order."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def traffic_for_current_kernel(kernel):
     """HBM bytes per launch of `kernel` from rocprofv3 FETCH_SIZE + WRITE_SIZE.
 
-    Taken from profiles/traffic.json, and only while the kernel's source file
-    is byte-identical to the one the counters were measured on; else None.
+    Taken from profiles/traffic.json, and only while the kernel's sources are
+    byte-identical to the ones the counters were measured on; else None.
     """
     try:
         with open(TRAFFIC_FILE) as f:
             entry = json.load(f)[kernel]
-        with open(os.path.join(ROOT, entry["source"]), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        if entry.get("source_sha256") != sha:
+        if entry.get("sources_sha256") != sources_sha256(entry["sources"]):
             return None
         return float(entry["bytes_per_launch"])
     except (OSError, ValueError, KeyError, TypeError):
