@@ -52,6 +52,10 @@ int check_params(const sink_attn_params* p) {
     return fail(SINK_ATTN_ERR_UNSUPPORTED, "total_tokens * num_q_heads * head_dim must stay below 2^31");
   if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.0f))
     return fail(SINK_ATTN_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  // The tiled kernels run one workgroup of 256 lanes per (128-row tile,
+  // query head, sequence); the dispatch's lane count must fit 32 bits.
+  if (((int64_t)p->max_seqlen + 127) / 128 * p->num_q_heads * p->num_seqs >= (int64_t)1 << 24)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "ceil(max_seqlen / 128) * num_q_heads * num_seqs must stay below 2^24");
   if (p->causal != 1) return fail(SINK_ATTN_ERR_UNSUPPORTED, "only causal attention is built (causal must be 1)");
   if (p->window < 0) return fail(SINK_ATTN_ERR_INVALID_ARG, "window must be >= 0 (got %d)", p->window);
   if (p->dtype != SINK_ATTN_BF16 && p->dtype != SINK_ATTN_F32)
@@ -115,7 +119,7 @@ int sink_attn_fwd(const sink_attn_params* p, const void* q, const void* k, const
   a.q = q; a.k = k; a.v = v; a.sinks = sinks; a.o = o; a.lse = lse;
   a.cu_seqlens = p->cu_seqlens;
   a.num_q_heads = p->num_q_heads; a.num_kv_heads = p->num_kv_heads; a.head_dim = p->head_dim;
-  a.total_tokens = p->total_tokens; a.window = p->window;
+  a.total_tokens = p->total_tokens; a.window = p->window; a.num_seqs = p->num_seqs;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   hipError_t e = sinkattn::launch_fwd(a, p->dtype, p->max_seqlen, p->num_seqs, s);
   if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
@@ -168,7 +172,7 @@ int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const
   a.dv_acc = carve(ws.dv_acc);
   a.dsink_part = carve(ws.dsink_part);
   a.num_q_heads = p->num_q_heads; a.num_kv_heads = p->num_kv_heads; a.head_dim = p->head_dim;
-  a.total_tokens = p->total_tokens; a.window = p->window;
+  a.total_tokens = p->total_tokens; a.window = p->window; a.num_seqs = p->num_seqs;
   a.scale = p->softmax_scale;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   hipError_t e = sinkattn::launch_bwd(a, p->dtype, p->max_seqlen, p->num_seqs, s,

@@ -155,8 +155,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int h2 = lane >> 5, l32 = lane & 31;
-  const int seq = blockIdx.z, hq = blockIdx.y;
-  const int kt = blockIdx.x;  // key tile 0 sees the most query tiles: runs first
+  const TileUnit unit = xcd_unit(a.num_q_heads, a.num_seqs);
+  const int seq = unit.seq, hq = unit.head;
+  const int kt = unit.rank;  // key tile 0 sees the most query tiles: runs first
   const int bos = a.cu_seqlens[seq];
   const int L = a.cu_seqlens[seq + 1] - bos;
   const int k0 = kt * kBN;
@@ -356,8 +357,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
-  const int seq = blockIdx.z, hq = blockIdx.y;
-  const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest (last) query tiles first
+  const TileUnit unit = xcd_unit(a.num_q_heads, a.num_seqs);
+  const int seq = unit.seq, hq = unit.head;
+  const int ntiles = (int)gridDim.x / (a.num_q_heads * a.num_seqs);
+  const int qt = ntiles - 1 - unit.rank;  // heaviest (last) query tiles first
   const int bos = a.cu_seqlens[seq];
   const int L = a.cu_seqlens[seq + 1] - bos;
   const int q0 = qt * kQT;
@@ -526,8 +529,8 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs,
   const long chunks = (long)T * 2 * a.num_kv_heads * a.head_dim / 8;
   const int conv_blocks = T > 0 ? flat_blocks(chunks) : 0;
   const int post_blocks = conv_blocks + (Hq + 3) / 4;
-  const dim3 grid_kv((max_seqlen + kBN - 1) / kBN, Hq, num_seqs);
-  const dim3 grid_q((max_seqlen + kQT - 1) / kQT, Hq, num_seqs);
+  const dim3 grid_kv((max_seqlen + kBN - 1) / kBN * Hq * num_seqs);
+  const dim3 grid_q((max_seqlen + kQT - 1) / kQT * Hq * num_seqs);
   const bool direct = dtype == 0 && a.head_dim == kD;
   auto mark = [&](int i) { return events ? hipEventRecord(events[i], stream) : hipSuccess; };
   hipError_t e;

@@ -198,6 +198,29 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Work order of the tiled kernels (1-D launch of n = tiles * heads * seqs
+// workgroups).  The dispatcher places workgroup b on XCD b % 8, and each XCD
+// has its own L2, so workgroup b takes unit
+//   u = x * floor(n / 8) + min(x, n % 8) + b / 8,   x = b % 8,
+// which gives every XCD one contiguous run of units (a bijection on [0, n)).
+// Units count head-major, then sequence, then tile rank: the tiles of one
+// head, and the heads of one KV group, run on one XCD and share its L2.
+struct TileUnit {
+  int head, seq, rank;
+};
+__device__ __forceinline__ TileUnit xcd_unit(int num_heads, int num_seqs) {
+  const int b = blockIdx.x, n = gridDim.x;
+  const int x = b & 7;
+  const int u = x * (n >> 3) + min(x, n & 7) + (b >> 3);
+  const int tiles = n / (num_heads * num_seqs);
+  TileUnit t;
+  t.rank = u % tiles;
+  const int r = u / tiles;
+  t.seq = r % num_seqs;
+  t.head = r / num_seqs;
+  return t;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);

@@ -49,8 +49,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int h2 = lane >> 5, l32 = lane & 31;
-  const int seq = blockIdx.z, hq = blockIdx.y;
-  const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest (last) query tiles first
+  const TileUnit unit = xcd_unit(a.num_q_heads, a.num_seqs);
+  const int seq = unit.seq, hq = unit.head;
+  const int ntiles = (int)gridDim.x / (a.num_q_heads * a.num_seqs);
+  const int qt = ntiles - 1 - unit.rank;  // heaviest (last) query tiles first
   const int bos = a.cu_seqlens[seq];
   const int L = a.cu_seqlens[seq + 1] - bos;
   const int q0 = qt * kBM;
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t stream) {
-  dim3 grid((max_seqlen + kBM - 1) / kBM, a.num_q_heads, num_seqs);
+  const dim3 grid((max_seqlen + kBM - 1) / kBM * a.num_q_heads * num_seqs);
   if (dtype == 0 && a.head_dim == kD)
     hipLaunchKernelGGL((fwd_kernel<bf16, true>), grid, dim3(256), 0, stream, a);
   else if (dtype == 0)

@@ -14,7 +14,7 @@ struct FwdArgs {
   void* o;
   float* lse;
   const int32_t* cu_seqlens;
-  int num_q_heads, num_kv_heads, head_dim, total_tokens, window;
+  int num_q_heads, num_kv_heads, head_dim, total_tokens, window, num_seqs;
   float scale_log2;  // softmax_scale * log2(e)
 };
 
@@ -36,7 +36,7 @@ struct BwdArgs {
   float* dk_acc;  // workspace: float dK accumulator, [T, Hkv, d]
   float* dv_acc;  // workspace: float dV accumulator, [T, Hkv, d]
   float* dsink_part;  // workspace: per-preprocess-block dS partials, [blocks, Hq]
-  int num_q_heads, num_kv_heads, head_dim, total_tokens, window;
+  int num_q_heads, num_kv_heads, head_dim, total_tokens, window, num_seqs;
   float scale;
   float scale_log2;
 };

@@ -88,6 +88,7 @@ def _bwd(p, ws_bytes=None, **override):
     ("num_q_heads", 0, _lib.SINK_ATTN_ERR_INVALID_ARG),
     ("num_q_heads", 16384, _lib.SINK_ATTN_ERR_UNSUPPORTED),
     ("total_tokens", 1 << 26, _lib.SINK_ATTN_ERR_UNSUPPORTED),
+    ("max_seqlen", 1 << 30, _lib.SINK_ATTN_ERR_UNSUPPORTED),
     ("num_kv_heads", 3, _lib.SINK_ATTN_ERR_INVALID_ARG),
     ("head_dim", 12, _lib.SINK_ATTN_ERR_INVALID_ARG),
     ("head_dim", 0, _lib.SINK_ATTN_ERR_INVALID_ARG),
