@@ -175,6 +175,23 @@ int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const
   a.total_tokens = p->total_tokens; a.window = p->window; a.num_seqs = p->num_seqs;
   a.scale = p->softmax_scale;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.dkdv_heads = 0;
+  if (const char* env = std::getenv("SINK_ATTN_DKDV_HEADS")) {
+    const int grp = p->num_q_heads / p->num_kv_heads;
+    const int hg = std::atoi(env);
+    if (hg < 1 || grp % hg != 0)
+      return fail(SINK_ATTN_ERR_INVALID_ARG, "SINK_ATTN_DKDV_HEADS=%s must divide num_q_heads / num_kv_heads = %d", env,
+                  grp);
+    a.dkdv_heads = hg;
+  }
+  if (a.dkdv_heads == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      return fail(SINK_ATTN_ERR_HIP, "cannot query the compute-unit count of the current device");
+    a.dkdv_heads = sinkattn::dkdv_heads_per_workgroup(p->total_tokens, p->max_seqlen, p->num_q_heads,
+                                                      p->num_kv_heads, p->window, cus);
+  }
   hipError_t e = sinkattn::launch_bwd(a, p->dtype, p->max_seqlen, p->num_seqs, s,
                                        g_bwd_events_on ? g_bwd_events : nullptr);
   if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));

@@ -35,6 +35,7 @@
 // which for L = 4096, 64 heads (2.7e8 additions) alone takes longer than the
 // whole backward pass.  Recomputing S and dP in the dQ kernel costs two
 // extra matrix products per visible block instead.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -84,7 +85,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
       atomicAdd(&bins[h], -__expf(a.sinks[h] - lse) * acc);
     }
   }
-  const long kchunks = (long)T * a.num_kv_heads * hd / 8;
+  // The float dK/dV accumulators are only used when a dK/dV workgroup covers
+  // part of a KV group.
+  const long kchunks = a.dkdv_heads * a.num_kv_heads == Hq ? 0 : (long)T * a.num_kv_heads * hd / 8;
   for (long c = (long)blockIdx.x * kFlatThreads + tid; c < kchunks; c += (long)gridDim.x * kFlatThreads) {
     *(f32x4*)(a.dk_acc + 8 * c) = z;
     *(f32x4*)(a.dk_acc + 8 * c + 4) = z;
@@ -142,8 +145,11 @@ struct __attribute__((aligned(16))) QStage {
 };
 constexpr int kStages = 3;
 
-// dK and dV for one 128-key tile of one query head (partial over the heads
-// of its KV group; summed with float atomics into the workspace).
+// dK and dV for one 128-key tile and `dkdv_heads` query heads of one KV
+// group.  The workgroup walks (head, query tile) steps through one LDS ring,
+// so K, V and the dK, dV accumulators stay in registers across its heads.
+// When it covers the whole group it writes dK, dV directly; otherwise its
+// partial sums go to the float accumulators with atomics.
 template <typename TIn, bool kDirect>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // Three separate LDS objects (not an array): with every access naming its
@@ -155,8 +161,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int h2 = lane >> 5, l32 = lane & 31;
-  const TileUnit unit = xcd_unit(a.num_q_heads, a.num_seqs);
-  const int seq = unit.seq, hq = unit.head;
+  const int HG = a.dkdv_heads, grp = a.num_q_heads / a.num_kv_heads;
+  const TileUnit unit = xcd_unit(a.num_q_heads / HG, a.num_seqs);
+  const int seq = unit.seq, hq0 = unit.head * HG;
   const int kt = unit.rank;  // key tile 0 sees the most query tiles: runs first
   const int bos = a.cu_seqlens[seq];
   const int L = a.cu_seqlens[seq + 1] - bos;
@@ -164,37 +171,48 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   if (k0 >= L) return;
 
   const int hd = a.head_dim, T = a.total_tokens, window = a.window;
-  const int g = hq / (a.num_q_heads / a.num_kv_heads);
+  const int g = hq0 / grp;
   const int qs = a.num_q_heads * hd, ks = a.num_kv_heads * hd;  // row strides (< 2^31 elements)
-  // Base pointers of this (sequence, head): row i of the sequence is base + i * stride.
-  const TIn* __restrict__ Qh = (const TIn*)a.q + (long)bos * qs + hq * hd;
-  const TIn* __restrict__ dOh = (const TIn*)a.dout + (long)bos * qs + hq * hd;
+  // Base pointers of this sequence and the first head: row i of head hq0 + j
+  // is base + i * stride + j * hd (Q, dO) or base + j * T + i (statistics).
+  const TIn* __restrict__ Qh = (const TIn*)a.q + (long)bos * qs + hq0 * hd;
+  const TIn* __restrict__ dOh = (const TIn*)a.dout + (long)bos * qs + hq0 * hd;
   const TIn* __restrict__ Kg = (const TIn*)a.k + (long)bos * ks + g * hd;
   const TIn* __restrict__ Vg = (const TIn*)a.v + (long)bos * ks + g * hd;
-  const float* __restrict__ nlse_h = a.nlse + (long)hq * T + bos;
-  const float* __restrict__ nD_h = a.ndelta + (long)hq * T + bos;
+  const float* __restrict__ nlse_h = a.nlse + (long)hq0 * T + bos;
+  const float* __restrict__ nD_h = a.ndelta + (long)hq0 * T + bos;
 
   // Query rows that can see a key of this tile: k0 <= q < k0 + kBN - 1 + window.
   const int qhi = window > 0 ? min(L, k0 + kBN - 1 + window) : L;
   const int qt0 = k0 / kBM, qt1 = (qhi + kBM - 1) / kBM;
+  const int nsteps = HG * (qt1 - qt0);
 
-  // Prefetch query tile t (clamped to the last visible tile) into stage buf.
+  // Prefetch cursor: head pj, query tile pt of step pf; it stops at the last
+  // step, so the ring's look-ahead past the end re-loads that tile.
+  int pf = 0, pj = 0, pt = qt0;
   // Direct path: exactly kPrefetchOps VMEM instructions per wavefront.
-  auto prefetch = [&](int t, QStage& st) {
-    const int q0 = min(t, qt1 - 1) * kBM;
+  auto prefetch = [&](QStage& st) {
+    const int q0 = pt * kBM;
     if constexpr (kDirect) {
-      stage_direct<kBM>(st.q, (const bf16*)Qh, q0, L, qs, w, lane);
-      stage_direct<kBM>(st.dout, (const bf16*)dOh, q0, L, qs, w, lane);
-      const float* src = (w == 1) ? nD_h : nlse_h;
+      stage_direct<kBM>(st.q, (const bf16*)Qh + pj * hd, q0, L, qs, w, lane);
+      stage_direct<kBM>(st.dout, (const bf16*)dOh + pj * hd, q0, L, qs, w, lane);
+      const float* src = ((w == 1) ? nD_h : nlse_h) + (long)pj * T;
       float* dst = (w == 0) ? st.nlse : (w == 1 ? st.ndelta : st.spare);
       lds_dma4(src + min(q0 + lane, L - 1), dst);
     } else {
-      stage_regs<kBM>(st.q, Qh, q0, L, qs, hd, tid);
-      stage_regs<kBM>(st.dout, dOh, q0, L, qs, hd, tid);
+      stage_regs<kBM>(st.q, Qh + pj * hd, q0, L, qs, hd, tid);
+      stage_regs<kBM>(st.dout, dOh + pj * hd, q0, L, qs, hd, tid);
       if (tid < kBM) {
         const int q = min(q0 + tid, L - 1);
-        st.nlse[tid] = nlse_h[q];
-        st.ndelta[tid] = nD_h[q];
+        st.nlse[tid] = nlse_h[(long)pj * T + q];
+        st.ndelta[tid] = nD_h[(long)pj * T + q];
+      }
+    }
+    if (pf + 1 < nsteps) {
+      ++pf;
+      if (++pt == qt1) {
+        pt = qt0;
+        ++pj;
       }
     }
   };
@@ -215,9 +233,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   }
   wait_vmem_all();  // fragments resident before the loop (see wait_vmem_all)
   issue_fence();
-  prefetch(qt0, st0);
+  prefetch(st0);
   issue_fence();
-  prefetch(qt0 + 1, st1);
+  prefetch(st1);
   issue_fence();
 
   f32x16 dk[2], dv[2];
@@ -227,17 +245,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const float sl2 = a.scale_log2;
   const int qrow_base = row_perm(l32);
 
-  // One step: consume tile t from `st`, prefetch tile t+2 into `nx` (the
-  // stage consumed in the previous step).
-  auto step = [&](int t, const QStage& st, QStage& nx) {
-    // Wait for this wavefront's part of tile t (only the next prefetch may
+  // One step: consume query tile ct (of some head) from `st`, prefetch two
+  // steps ahead into `nx` (the stage consumed in the previous step).
+  int ct = qt0;
+  auto step = [&](const QStage& st, QStage& nx) {
+    // Wait for this wavefront's part of the tile (only the next prefetch may
     // still be in flight), then make all parts visible.
     if constexpr (kDirect) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
     static_assert(kPrefetchOps == 5, "wait count");
-    lds_barrier();  // tile t visible; `nx` was last read in the previous step
-    prefetch(t + 2, nx);
+    lds_barrier();  // tile visible; `nx` was last read in the previous step
+    prefetch(nx);
     issue_fence();
-    const int qb = t * kBM;
+    const int qb = ct * kBM;
+    if (++ct == qt1) ct = qt0;
 
     const bool active = wk_lo < L && wk_lo <= qb + kBM - 1 && !(window > 0 && qb - wk_hi >= window);
     if (active) {
@@ -312,13 +332,31 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       }
     }
   };
-  for (int t = qt0; t < qt1; t += kStages) {
-    step(t, st0, st2);
-    if (t + 1 < qt1) step(t + 1, st1, st0);
-    if (t + 2 < qt1) step(t + 2, st2, st1);
+  for (int f = 0; f < nsteps; f += kStages) {
+    step(st0, st2);
+    if (f + 1 < nsteps) step(st1, st0);
+    if (f + 2 < nsteps) step(st2, st1);
   }
 
   // dK, dV rows of this wavefront: register r holds key wk_lo + 8*(r/4) + 4*h2 + r%4.
+  if (HG == grp) {
+    TIn* dk_g = (TIn*)a.dk + (long)bos * ks + g * hd;
+    TIn* dv_g = (TIn*)a.dv + (long)bos * ks + g * hd;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int d = 32 * db + l32;
+      if (d >= hd) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = wk_lo + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        if (key < L) {
+          dk_g[key * ks + d] = (TIn)(dk[db][r] * a.scale);
+          dv_g[key * ks + d] = (TIn)dv[db][r];
+        }
+      }
+    }
+    return;
+  }
   float* dk_g = a.dk_acc + (long)bos * ks + g * hd;
   float* dv_g = a.dv_acc + (long)bos * ks + g * hd;
 #pragma unroll
@@ -521,15 +559,37 @@ BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d) {
   return w;
 }
 
+int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, int window, int num_cus) {
+  const int grp = hq / hkv;
+  // Work in (64-row query step x 128-key tile) units.  Longest workgroup per
+  // head: key tile 0 of a max_seqlen sequence.  Average per key tile: half of
+  // that under the causal mask (exact for equal lengths, high for mixed
+  // ones), at most the window's rows.
+  const long steps_max = window > 0 ? std::min<long>((max_seqlen + kBM - 1) / kBM, (kBN - 1 + window + kBM - 1) / kBM + 1)
+                                    : (max_seqlen + kBM - 1) / kBM;
+  const long steps_avg = window > 0 ? std::min<long>(max_seqlen / (2 * kBM) + 1, (kBN + window) / kBM)
+                                    : max_seqlen / (2 * kBM) + 1;
+  const long tiles = ((long)total_tokens + kBN - 1) / kBN;
+  const long per_slot = (long)hq * tiles * steps_avg / (2L * num_cus);  // two workgroups per CU
+  // The most heads per workgroup (fewest atomics; none for the whole group)
+  // such that the longest workgroup fits in a slot's average load and the
+  // tail it leaves (its excess over an average workgroup) stays within an
+  // eighth of that load.
+  for (int hg = grp; hg > 1; --hg)
+    if (grp % hg == 0 && hg * steps_max <= per_slot && 8 * hg * (steps_max - steps_avg) <= per_slot) return hg;
+  return 1;
+}
+
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t stream,
                       const hipEvent_t* events) {
   const int T = a.total_tokens, Hq = a.num_q_heads;
   const int pre_blocks = bwd_pre_blocks(T, Hq);
   const size_t bins_bytes = (size_t)Hq * sizeof(float);
   const long chunks = (long)T * 2 * a.num_kv_heads * a.head_dim / 8;
-  const int conv_blocks = T > 0 ? flat_blocks(chunks) : 0;
+  const bool dkdv_atomics = a.dkdv_heads * a.num_kv_heads != Hq;
+  const int conv_blocks = (T > 0 && dkdv_atomics) ? flat_blocks(chunks) : 0;
   const int post_blocks = conv_blocks + (Hq + 3) / 4;
-  const dim3 grid_kv((max_seqlen + kBN - 1) / kBN * Hq * num_seqs);
+  const dim3 grid_kv((max_seqlen + kBN - 1) / kBN * (Hq / a.dkdv_heads) * num_seqs);
   const dim3 grid_q((max_seqlen + kQT - 1) / kQT * Hq * num_seqs);
   const bool direct = dtype == 0 && a.head_dim == kD;
   auto mark = [&](int i) { return events ? hipEventRecord(events[i], stream) : hipSuccess; };

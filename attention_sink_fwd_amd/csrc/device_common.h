@@ -199,19 +199,19 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Work order of the tiled kernels (1-D launch of n = tiles * heads * seqs
-// workgroups).  The dispatcher places workgroup b on XCD b % 8, and each XCD
-// has its own L2, so workgroup b takes unit
-//   u = x * floor(n / 8) + min(x, n % 8) + b / 8,   x = b % 8,
-// which gives every XCD one contiguous run of units (a bijection on [0, n)).
-// Units count head-major, then sequence, then tile rank: the tiles of one
-// head, and the heads of one KV group, run on one XCD and share its L2.
+// workgroups; units count head-major, then sequence, then tile rank).  The
+// dispatcher places workgroup b on XCD b % 8, and each XCD has its own L2.
+// When the heads split evenly over the 8 XCDs, workgroup b takes unit
+//   u = x * (n / 8) + b / 8,   x = b % 8,
+// so every XCD runs whole heads (tiles that share Q, dO or K, V hit one L2)
+// with equal work.  Otherwise u = b: tiles of every head are dealt round-robin
+// over the XCDs, which keeps the work even at the cost of L2 sharing.
 struct TileUnit {
   int head, seq, rank;
 };
 __device__ __forceinline__ TileUnit xcd_unit(int num_heads, int num_seqs) {
   const int b = blockIdx.x, n = gridDim.x;
-  const int x = b & 7;
-  const int u = x * (n >> 3) + min(x, n & 7) + (b >> 3);
+  const int u = (num_heads & 7) == 0 ? (b & 7) * (n >> 3) + (b >> 3) : b;
   const int tiles = n / (num_heads * num_seqs);
   TileUnit t;
   t.rank = u % tiles;

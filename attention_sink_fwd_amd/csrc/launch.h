@@ -37,6 +37,7 @@ struct BwdArgs {
   float* dv_acc;  // workspace: float dV accumulator, [T, Hkv, d]
   float* dsink_part;  // workspace: per-preprocess-block dS partials, [blocks, Hq]
   int num_q_heads, num_kv_heads, head_dim, total_tokens, window, num_seqs;
+  int dkdv_heads;  // query heads per dK/dV workgroup (divides Hq / Hkv)
   float scale;
   float scale_log2;
 };
@@ -48,6 +49,8 @@ struct BwdWorkspace {
 BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d);
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s);
+// Query heads per dK/dV workgroup for a problem shape (a divisor of Hq/Hkv).
+int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, int window, int num_cus);
 // events: NULL, or five events recorded around the four kernels.
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s,
                       const hipEvent_t* events);

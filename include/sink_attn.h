@@ -52,6 +52,13 @@
  * max_seqlen (set SINK_ATTN_VALIDATE=1 to have the host copy and check it,
  * which synchronises the stream).
  *
+ * Tuning.  The backward's dK/dV kernel gives each workgroup one 128-key tile
+ * and some of the query heads that share its KV head: all of them when the
+ * problem has enough parallel work (dK, dV written once), else fewer, with
+ * float atomics combining their partial sums in the workspace.  The library
+ * picks the number from the shape; SINK_ATTN_DKDV_HEADS=n (a divisor of
+ * num_q_heads / num_kv_heads) overrides it, for tests and tuning.
+ *
  * Streams.  All work is enqueued on `stream` (a hipStream_t; NULL is the
  * default stream) and is asynchronous.  Entry points are thread-safe.
  */

@@ -111,6 +111,14 @@ def test_bad_params_are_rejected_without_launch(field, value, status):
     assert lib.sink_attn_bwd_workspace_size(ctypes.byref(p)) == 0
 
 
+@pytest.mark.parametrize("value", ["0", "3", "-2", "abc"])
+def test_bad_dkdv_heads_override_is_rejected(monkeypatch, value):
+    monkeypatch.setenv("SINK_ATTN_DKDV_HEADS", value)
+    p = _good_params()
+    assert _bwd(p) == _lib.SINK_ATTN_ERR_INVALID_ARG
+    assert "SINK_ATTN_DKDV_HEADS" in _lib.load().sink_attn_last_error().decode()
+
+
 def test_null_params():
     lib = _lib.load()
     assert _fwd(None) == _lib.SINK_ATTN_ERR_INVALID_ARG

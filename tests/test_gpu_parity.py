@@ -74,6 +74,36 @@ def test_small_cases_match_oracle(lengths, hq, hkv, d, window, dtype, sinks):
         assert np.all(gpu["ds"] == 0.0)
 
 
+GROUPED = [
+    # lengths, hq, hkv, d, window, dtype, sinks: dK/dV workgroups covering
+    # every query head of a KV group (direct dK, dV stores) and some of them
+    ((1,), 4, 2, 64, 0, "bf16", "normal"),
+    ((300,), 8, 2, 64, 0, "bf16", "mixed"),
+    ((0, 5, 1, 130, 0, 64, 257), 4, 2, 64, 0, "bf16", "normal"),
+    ((333, 129), 8, 1, 64, 128, "bf16", "normal"),
+    ((129, 70), 4, 2, 16, 0, "bf16", "normal"),
+    ((200, 3), 4, 2, 40, 9, "f32", "mixed"),
+    ((520,), 16, 2, 64, 0, "bf16", "normal"),
+]
+
+
+@pytest.mark.parametrize("heads", ["group", 2])
+@pytest.mark.parametrize("lengths,hq,hkv,d,window,dtype,sinks", GROUPED)
+def test_grouped_dkdv_workgroups_match_oracle(monkeypatch, heads, lengths, hq, hkv, d, window, dtype, sinks):
+    hg = hq // hkv if heads == "group" else heads
+    if (hq // hkv) % hg:
+        pytest.skip("head count does not divide the group")
+    monkeypatch.setenv("SINK_ATTN_DKDV_HEADS", str(hg))
+    label = f"L={lengths} hq={hq} hkv={hkv} d={d} W={window} {dtype} sinks={sinks} dkdv_heads={hg}"
+    say("case", label)
+    w = custom_workload(lengths, hq, hkv, d, window, dtype)
+    inp = _set_sinks(make_inputs(w, seed=sum(lengths) + 7 * hq + d + 1), sinks, hq)
+    scale = 1.0 / math.sqrt(d)
+    gpu = run_gpu(inp, w.max_seqlen, scale, window)
+    ref = _oracle_full(inp, scale, window)
+    check_full(gpu, ref, label)
+
+
 def test_workload1_tiny_fp32_matches_oracle():
     w = WORKLOADS[1]
     say("case workload 1", w.name)
