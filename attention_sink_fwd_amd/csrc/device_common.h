@@ -18,6 +18,7 @@ namespace sinkattn {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -219,6 +220,12 @@ __device__ __forceinline__ TileUnit xcd_unit(int num_heads, int num_seqs) {
   t.seq = r % num_seqs;
   t.head = r / num_seqs;
   return t;
+}
+
+// acc + x.x + x.y in one instruction (v_dot2_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float dot2_bf16(bf16x2 x, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
 }
 
 __device__ __forceinline__ float wave_sum(float x) {

@@ -146,31 +146,31 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     }
 
     const bool need_mask = (kb + kBN - 1 > wq_lo) || (window > 0 && wq_hi - kb >= window);
-    // key index 32*blk + 16*(r/8) + r%8 (+ kb + 8*h2) is visible iff lo <= idx < hi
-    const int hi = qrow + 1 - kb - 8 * h2;
-    const int lo = window > 0 ? hi - window : -0x7fffffff;
-    float mx = -__builtin_inff();
-    auto scale_mask = [&](auto masked) {
+    if (need_mask) {
+      // key index 32*blk + 16*(r/8) + r%8 (+ kb + 8*h2) is visible iff lo <= idx < hi;
+      // hidden raw scores become -inf (the scale is positive, so they stay
+      // -inf through the scaling below).
+      const int hi = qrow + 1 - kb - 8 * h2;
+      const int lo = window > 0 ? hi - window : -0x7fffffff;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = s[blk][r] * sl2;
-          if constexpr (decltype(masked)::value) {
-            const int idx = 32 * blk + 16 * (r >> 3) + (r & 7);
-            x = (idx >= lo && idx < hi) ? x : -__builtin_inff();
-          }
-          s[blk][r] = x;
+          const int idx = 32 * blk + 16 * (r >> 3) + (r & 7);
+          s[blk][r] = (idx >= lo && idx < hi) ? s[blk][r] : -__builtin_inff();
         }
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[blk][r], s[blk][r + 1]));
       }
-    };
-    if (need_mask)
-      scale_mask(std::true_type{});
-    else
-      scale_mask(std::false_type{});
-    mx = fmaxf(mx, __shfl_xor(mx, 32));  // the other half of the row
+    }
+    // Row max of the raw scores (two chains of three-way maxima), then the
+    // other half of the row, then into the log2 domain (scale > 0).
+    float mx0 = -__builtin_inff(), mx1 = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      mx0 = __builtin_fmaxf(__builtin_fmaxf(mx0, s[0][r]), s[0][r + 1]);
+      mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, s[1][r]), s[1][r + 1]);
+    }
+    float mx = __builtin_fmaxf(mx0, mx1);
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
     // Raise the reference max (and rescale the accumulator) only when some
     // row of the wavefront outgrew it by more than the slack.
     if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
@@ -181,28 +181,25 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       for (int i = 0; i < 16; ++i) { o[0][i] *= alpha; o[1][i] *= alpha; }
       m = mnew;
     }
-    const float muse = (m == -__builtin_inff()) ? 0.0f : m;
-    float rs = 0.0f;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(s[blk][r] - muse);
-        s[blk][r] = p;
-        rs += p;
-      }
-    }
-    l += rs;
-
-    // P^T fragments: chunk c covers keys 16c .. 16c+15 of the tile.
+    const float nmuse = (m == -__builtin_inff()) ? 0.0f : -m;
+    // P = exp2(S * scale * log2 e - m) as P^T fragments (chunk c covers keys
+    // 16c .. 16c+15 of the tile); the row sum adds the rounded values, two per
+    // dot product, in two chains.
     bf16x8 pf[4];
+    float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       f32x8 v;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = s[c >> 1][8 * (c & 1) + i];
+      for (int i = 0; i < 8; ++i) v[i] = fast_exp2(__builtin_fmaf(s[c >> 1][8 * (c & 1) + i], sl2, nmuse));
       pf[c] = __builtin_convertvector(v, bf16x8);
+      ls0 = dot2_bf16(__builtin_shufflevector(pf[c], pf[c], 0, 1), ls0);
+      ls1 = dot2_bf16(__builtin_shufflevector(pf[c], pf[c], 2, 3), ls1);
+      ls0 = dot2_bf16(__builtin_shufflevector(pf[c], pf[c], 4, 5), ls0);
+      ls1 = dot2_bf16(__builtin_shufflevector(pf[c], pf[c], 6, 7), ls1);
     }
+    l += ls0 + ls1;
+
     // O^T += V^T P^T.
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
