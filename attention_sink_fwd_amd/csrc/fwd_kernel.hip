@@ -7,8 +7,9 @@
 //
 // One workgroup = one query head h, one sequence, a tile of 128 query rows;
 // four wavefronts own 32 rows each.  Keys/values of head g(h) stream through
-// a three-stage LDS ring in tiles of 64 keys (direct global->LDS loads into
-// XOR-swizzled rows, issued two tiles ahead; one barrier per tile).  Per tile
+// a two-stage LDS ring in tiles of 64 keys (direct global->LDS loads into
+// XOR-swizzled rows, issued one tile ahead; one barrier per tile; the small
+// ring leaves room for four workgroups per compute unit).  Per tile
 // a wavefront computes the transposed score block S^T = K Q^T on the matrix
 // cores, so each lane owns one query row and its softmax statistics stay in
 // the lane; the online softmax starts from the sink (reference max m = S_h,
@@ -34,7 +35,7 @@ namespace {
 constexpr int kBM = 128;  // query rows per workgroup
 constexpr int kBN = 64;   // keys per LDS tile
 constexpr int kD = 64;    // padded head dimension
-constexpr int kStages = 3;
+constexpr int kStages = 2;
 constexpr float kRescaleSlack = 8.0f;
 
 struct __attribute__((aligned(16))) KVStage {
@@ -99,8 +100,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   issue_fence();
   prefetch(t0, 0);
   issue_fence();
-  prefetch(t0 + 1, 1);
-  issue_fence();
 
   // Online softmax state in the log2 domain, seeded with the sink.
   const float sink = a.sinks[hq];
@@ -116,15 +115,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
   int buf = 0;
   for (int t = t0; t < t1; ++t) {
-    // This wavefront's part of tile t has landed (only the next prefetch may
-    // still be in flight); the barrier makes every part visible and ends all
-    // reads of the stage the next prefetch overwrites.
-    if constexpr (kDirect) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    // This wavefront's part of tile t has landed; the barrier makes every
+    // part visible and ends all reads of the stage the next prefetch
+    // overwrites (tile t-1).
+    if constexpr (kDirect) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
     {
-      int nb = buf + 2;
+      int nb = buf + 1;
       if (nb >= kStages) nb -= kStages;
-      prefetch(t + 2, nb);
+      prefetch(t + 1, nb);
       issue_fence();
     }
     const KVStage& st = stage[buf];
