@@ -18,7 +18,7 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
-thread_local hipEvent_t g_bwd_events[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+thread_local hipEvent_t g_bwd_events[4] = {nullptr, nullptr, nullptr, nullptr};
 thread_local bool g_bwd_events_on = false;
 
 int fail(int status, const char* fmt, ...) {
@@ -128,7 +128,9 @@ int sink_attn_fwd(const sink_attn_params* p, const void* q, const void* k, const
 
 size_t sink_attn_bwd_workspace_size(const sink_attn_params* p) {
   if (check_params(p) != SINK_ATTN_OK) return 0;
-  return sinkattn::bwd_workspace_layout(p->total_tokens, p->num_q_heads, p->num_kv_heads, p->head_dim).total;
+  return sinkattn::bwd_workspace_layout(p->total_tokens, p->num_q_heads, p->num_kv_heads, p->head_dim, p->max_seqlen,
+                                        p->num_seqs)
+      .total;
 }
 
 int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const void* v, const float* sinks,
@@ -150,7 +152,8 @@ int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const
   }
   if (!dsinks) return fail(SINK_ATTN_ERR_INVALID_ARG, "dsinks is NULL");
   const sinkattn::BwdWorkspace ws =
-      sinkattn::bwd_workspace_layout(p->total_tokens, p->num_q_heads, p->num_kv_heads, p->head_dim);
+      sinkattn::bwd_workspace_layout(p->total_tokens, p->num_q_heads, p->num_kv_heads, p->head_dim, p->max_seqlen,
+                                     p->num_seqs);
   if (workspace_bytes < ws.total)
     return fail(SINK_ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, ws.total);
   if (ws.total > 0 && !workspace) return fail(SINK_ATTN_ERR_INVALID_ARG, "workspace is NULL");
@@ -204,9 +207,9 @@ int sink_attn_set_bwd_events(void* const* events) {
     g_bwd_events_on = false;
     return SINK_ATTN_OK;
   }
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < 4; ++i)
     if (!events[i]) return fail(SINK_ATTN_ERR_INVALID_ARG, "events[%d] is NULL", i);
-  for (int i = 0; i < 5; ++i) g_bwd_events[i] = static_cast<hipEvent_t>(events[i]);
+  for (int i = 0; i < 4; ++i) g_bwd_events[i] = static_cast<hipEvent_t>(events[i]);
   g_bwd_events_on = true;
   return SINK_ATTN_OK;
 }

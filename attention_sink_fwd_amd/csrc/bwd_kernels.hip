@@ -10,25 +10,26 @@
 // memory-efficient attention backward, with P recomputed from the saved LSE
 // (which already includes the sink, so P needs no other change).
 //
-//  1. bwd_pre_kernel   streams O and dO once (flat, coalesced): -D_i and
-//                      -LSE_i / scale into the workspace, the sink term
-//                      -p_sink,i D_i reduced per block (8-lane shuffles, then
-//                      LDS float atomics per head) into a per-block partial;
-//                      zeroes the float dK/dV accumulators.
-//  2. bwd_dkdv_kernel  one workgroup per (sequence, query head, 128-key tile),
-//                      looping over the visible 64-row query tiles:
+//  1. bwd_dq_kernel    one workgroup per (sequence, query head, 128-row query
+//                      tile).  First the row statistics: D_i = dO_i . O_i,
+//                      and the sink term -p_sink,i D_i summed over the tile
+//                      into a per-tile partial; -D_i and -LSE_i / scale go to
+//                      the workspace for the next kernel.  Then it loops over
+//                      the visible 64-key tiles: recomputes S and dP in
+//                      transposed form and accumulates dQ = scale * dS K in
+//                      registers; writes dQ once.  When the next kernel will
+//                      use float atomics it also clears their accumulators.
+//  2. bwd_dkdv_kernel  one workgroup per (sequence, 128-key tile, group of
+//                      query heads sharing a KV head), looping over the
+//                      visible 64-row query tiles of each of those heads:
 //                      S = Q K^T, dP = dO V^T, P = exp(S - LSE),
 //                      dS = P (dP - D), dV += P^T dO, dK += dS^T Q on the
-//                      matrix cores, K, V, dK, dV in registers; the per-head
-//                      dK, dV are added to float accumulators (float atomics,
-//                      once per key and head).
-//  3. bwd_dq_kernel    one workgroup per (sequence, query head, 128-row query
-//                      tile), looping over the visible 64-key tiles: recomputes
-//                      S and dP in transposed form and accumulates
-//                      dQ = scale * dS K in registers; writes dQ once.
-//  4. bwd_post_kernel  converts the dK/dV accumulators to the output type
-//                      (flat, coalesced) and sums the per-block dS partials of
-//                      each head in a fixed order (deterministic dS_h).
+//                      matrix cores, K, V, dK, dV in registers; writes dK, dV
+//                      directly when the group covers all heads of the KV
+//                      head, else adds them to float accumulators.
+//  3. bwd_post_kernel  sums the per-tile dS partials of each head in a fixed
+//                      order (deterministic dS_h) and, after atomics,
+//                      converts the dK/dV accumulators to the output type.
 //
 // dQ is not accumulated with float atomics across key tiles: on this chip
 // float atomics retire at about 0.3 G element-operations per microsecond,
@@ -49,55 +50,6 @@ constexpr int kFlatThreads = 256;
 // VMEM instructions one wavefront issues per query-tile prefetch of the
 // dK/dV kernel on the direct path (2 Q + 2 dO + 1 statistics).
 constexpr int kPrefetchOps = 5;
-constexpr int kPairsPerIter = kFlatThreads / 8;  // 8 lanes per (row, head) pair
-
-template <typename TIn>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
-  extern __shared__ float bins[];  // [num_q_heads] sink-term partial per head
-  const int tid = threadIdx.x;
-  const int Hq = a.num_q_heads, hd = a.head_dim, T = a.total_tokens;
-  for (int i = tid; i < Hq; i += kFlatThreads) bins[i] = 0.0f;
-  __syncthreads();
-
-  const int part = tid & 7;  // 8-element chunk of the head dimension
-  const int npairs = T * Hq;
-  const TIn* O = (const TIn*)a.o;
-  const TIn* dO = (const TIn*)a.dout;
-  const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int pr = blockIdx.x * kPairsPerIter + (tid >> 3); pr < npairs; pr += gridDim.x * kPairsPerIter) {
-    const int row = pr / Hq, h = pr - row * Hq;
-    const long off = (long)pr * hd + part * 8;
-    float acc = 0.0f;
-    if (part * 8 < hd) {
-      const f32x8 x = load8f(O + off), y = load8f(dO + off);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc += x[i] * y[i];
-    }
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    acc += __shfl_xor(acc, 4);
-    if (part == 0) {
-      const long si = (long)h * T + row;
-      const float lse = a.lse[si];
-      a.ndelta[si] = -acc;          // -D: initial value of the dP accumulators
-      a.nlse[si] = -lse / a.scale;  // -LSE/scale: initial value of the S accumulators
-      // sink's softmax-Jacobian entry: p_sink * (0 - D); exp(-inf) = 0
-      atomicAdd(&bins[h], -__expf(a.sinks[h] - lse) * acc);
-    }
-  }
-  // The float dK/dV accumulators are only used when a dK/dV workgroup covers
-  // part of a KV group.
-  const long kchunks = a.dkdv_heads * a.num_kv_heads == Hq ? 0 : (long)T * a.num_kv_heads * hd / 8;
-  for (long c = (long)blockIdx.x * kFlatThreads + tid; c < kchunks; c += (long)gridDim.x * kFlatThreads) {
-    *(f32x4*)(a.dk_acc + 8 * c) = z;
-    *(f32x4*)(a.dk_acc + 8 * c + 4) = z;
-    *(f32x4*)(a.dv_acc + 8 * c) = z;
-    *(f32x4*)(a.dv_acc + 8 * c + 4) = z;
-  }
-  __syncthreads();
-  for (int i = tid; i < Hq; i += kFlatThreads) a.dsink_part[(long)blockIdx.x * Hq + i] = bins[i];
-}
-
 __device__ __forceinline__ void convert8(const float* src, bf16* dst) {
   const f32x4 x = *(const f32x4*)src, y = *(const f32x4*)(src + 4);
   const f32x8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
@@ -109,15 +61,16 @@ __device__ __forceinline__ void convert8(const float* src, float* dst) {
 }
 
 template <typename TIn>
-__global__ __launch_bounds__(256) void bwd_post_kernel(BwdArgs a, int conv_blocks, int pre_blocks) {
+__global__ __launch_bounds__(256) void bwd_post_kernel(BwdArgs a, int conv_blocks, int parts) {
   const int tid = threadIdx.x;
   const int Hq = a.num_q_heads;
   if ((int)blockIdx.x >= conv_blocks) {
-    // dS_h = sum of the preprocess partials, one wavefront per head, fixed order.
+    // dS_h = sum of the head's per-tile partials, one wavefront per head,
+    // fixed order.
     const int h = (blockIdx.x - conv_blocks) * 4 + (tid >> 6);
     if (h >= Hq) return;
     float s = 0.0f;
-    for (int j = tid & 63; j < pre_blocks; j += 64) s += a.dsink_part[(long)j * Hq + h];
+    for (int j = tid & 63; j < parts; j += 64) s += a.dsink_part[(long)h * parts + j];
     s = wave_sum(s);
     if ((tid & 63) == 0) a.dsinks[h] = s;
     return;
@@ -170,7 +123,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int k0 = kt * kBN;
   if (k0 >= L) return;
 
-  const int hd = a.head_dim, T = a.total_tokens, window = a.window;
+  // The direct path is only built for head_dim == kD.
+  const int hd = kDirect ? kD : a.head_dim, T = a.total_tokens, window = a.window;
   const int g = hq0 / grp;
   const int qs = a.num_q_heads * hd, ks = a.num_kv_heads * hd;  // row strides (< 2^31 elements)
   // Base pointers of this sequence and the first head: row i of head hq0 + j
@@ -383,8 +337,8 @@ struct __attribute__((aligned(16))) KStage {
   bf16 v[kKT * kD];  // V tile, swizzled [key][d]
 };
 
-// dQ for one 128-row query tile of one head.  Transposed products keep each
-// query row on a lane: S^T = K Q^T and dP^T = V dO^T (accumulators seeded
+// Row statistics and dQ for one 128-row query tile of one head.  Transposed
+// products keep each query row on a lane: S^T = K Q^T and dP^T = V dO^T (accumulators seeded
 // with -LSE/scale and -D of the lane's row), P^T = exp2(S^T scale log2 e),
 // dS^T = P^T dP^T, dQ^T += K^T dS^T with K^T from the row-major K tile
 // through transposing reads.  dQ is written once, in the output type.
@@ -395,20 +349,38 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
+  // The direct path is only built for head_dim == kD.
+  const int hd = kDirect ? kD : a.head_dim, T = a.total_tokens, window = a.window;
+  if (a.dkdv_heads * a.num_kv_heads != a.num_q_heads) {
+    // The dK/dV kernel will add partial sums: clear its float accumulators,
+    // one slice per workgroup (T * Hkv * d is a multiple of 8).
+    const long n4 = (long)T * a.num_kv_heads * hd / 4;
+    const long per = (n4 + gridDim.x - 1) / gridDim.x;
+    const long end = min(n4, (long)(blockIdx.x + 1) * per);
+    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (long c = (long)blockIdx.x * per + tid; c < end; c += 256) {
+      *(f32x4*)(a.dk_acc + 4 * c) = z;
+      *(f32x4*)(a.dv_acc + 4 * c) = z;
+    }
+  }
   const TileUnit unit = xcd_unit(a.num_q_heads, a.num_seqs);
   const int seq = unit.seq, hq = unit.head;
   const int ntiles = (int)gridDim.x / (a.num_q_heads * a.num_seqs);
   const int qt = ntiles - 1 - unit.rank;  // heaviest (last) query tiles first
+  float* __restrict__ dsink_slot = a.dsink_part + ((long)hq * a.num_seqs + seq) * ntiles + qt;
   const int bos = a.cu_seqlens[seq];
   const int L = a.cu_seqlens[seq + 1] - bos;
   const int q0 = qt * kQT;
-  if (q0 >= L) return;
+  if (q0 >= L) {
+    if (tid == 0) *dsink_slot = 0.0f;
+    return;
+  }
 
-  const int hd = a.head_dim, T = a.total_tokens, window = a.window;
   const int g = hq / (a.num_q_heads / a.num_kv_heads);
   const int qs = a.num_q_heads * hd, ks = a.num_kv_heads * hd;
   const TIn* __restrict__ Qh = (const TIn*)a.q + (long)bos * qs + hq * hd;
   const TIn* __restrict__ dOh = (const TIn*)a.dout + (long)bos * qs + hq * hd;
+  const TIn* __restrict__ Oh = (const TIn*)a.o + (long)bos * qs + hq * hd;
   const TIn* __restrict__ Kg = (const TIn*)a.k + (long)bos * ks + g * hd;
   const TIn* __restrict__ Vg = (const TIn*)a.v + (long)bos * ks + g * hd;
 
@@ -430,24 +402,37 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   };
 
   // This lane's query row (column n of the transposed products) and its Q and
-  // dO fragments (B operands), plus its row statistics.
+  // dO fragments (B operands); the lane holds half of the row's d values.
   const int qrow = q0 + 32 * w + l32;
   const int qcl = min(qrow, L - 1);
+  const float lse = a.lse[(long)hq * T + bos + qcl];
+  const float sink = a.sinks[hq];
   bf16x8 qf[4], of[4];
+  float dpart = 0.0f;  // this half's share of D = dO . O, in float from the inputs
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int d0 = 16 * c + 8 * h2;
     qf[c] = d0 < hd ? load8(Qh + qcl * qs + d0) : zero8();
-    of[c] = d0 < hd ? load8(dOh + qcl * qs + d0) : zero8();
+    if (d0 < hd) {
+      const f32x8 x = load8f(dOh + qcl * qs + d0), y = load8f(Oh + qcl * qs + d0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dpart += x[i] * y[i];
+      of[c] = __builtin_convertvector(x, bf16x8);
+    } else {
+      of[c] = zero8();
+    }
   }
-  const float nlse = a.nlse[(long)hq * T + bos + qcl];
-  const float nD = a.ndelta[(long)hq * T + bos + qcl];
   wait_vmem_all();  // fragments resident before the loop (see wait_vmem_all)
   issue_fence();
   prefetch(t0, 0);
   issue_fence();
   prefetch(t0 + 1, 1);
   issue_fence();
+  // Row statistics: the accumulator seeds of this kernel and of the dK/dV
+  // kernel (stored after the loop, so the loop's load waits do not cover
+  // them).
+  const float D = dpart + __shfl_xor(dpart, 32);
+  const float nlse = -lse / a.scale, nD = -D;
 
   f32x16 acc[2];  // dQ^T: register r of block db holds d = 32*db + 8*(r/4) + 4*h2 + r%4
 #pragma unroll
@@ -521,6 +506,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   }
 
+  // Statistics for the dK/dV kernel, and the sink's softmax-Jacobian entry
+  // p_sink * (0 - D) summed over the tile's rows (exp(-inf) = 0).
+  const bool own_row = qrow < L && h2 == 0;
+  if (own_row) {
+    a.nlse[(long)hq * T + bos + qrow] = nlse;
+    a.ndelta[(long)hq * T + bos + qrow] = nD;
+  }
+  {
+    __shared__ float wsum[4];
+    const float sw = wave_sum(own_row ? -__expf(sink - lse) * D : 0.0f);
+    if (lane == 0) wsum[w] = sw;
+    __syncthreads();
+    if (tid == 0) *dsink_slot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  }
   if (qrow < L) {
     TIn* dq = (TIn*)a.dq + (long)(bos + qrow) * qs + hq * hd;
 #pragma unroll
@@ -545,16 +544,16 @@ int flat_blocks(long work_items) {
 
 }  // namespace
 
-int bwd_pre_blocks(int total_tokens, int hq) { return flat_blocks((long)total_tokens * hq * 8); }
+int bwd_dsink_parts(int max_seqlen, int num_seqs) { return (max_seqlen + kQT - 1) / kQT * num_seqs; }
 
-BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d) {
+BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d, int max_seqlen, int num_seqs) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   BwdWorkspace w;
   w.ndelta = up((size_t)hq * total_tokens * sizeof(float));
   w.nlse = w.ndelta;
   w.dk_acc = up((size_t)total_tokens * hkv * d * sizeof(float));
   w.dv_acc = w.dk_acc;
-  w.dsink_part = up((size_t)bwd_pre_blocks(total_tokens, hq) * hq * sizeof(float));
+  w.dsink_part = up((size_t)bwd_dsink_parts(max_seqlen, num_seqs) * hq * sizeof(float));
   w.total = w.ndelta + w.nlse + w.dk_acc + w.dv_acc + w.dsink_part;
   return w;
 }
@@ -583,8 +582,7 @@ int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, 
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t stream,
                       const hipEvent_t* events) {
   const int T = a.total_tokens, Hq = a.num_q_heads;
-  const int pre_blocks = bwd_pre_blocks(T, Hq);
-  const size_t bins_bytes = (size_t)Hq * sizeof(float);
+  const int parts = T > 0 ? bwd_dsink_parts(max_seqlen, num_seqs) : 0;
   const long chunks = (long)T * 2 * a.num_kv_heads * a.head_dim / 8;
   const bool dkdv_atomics = a.dkdv_heads * a.num_kv_heads != Hq;
   const int conv_blocks = (T > 0 && dkdv_atomics) ? flat_blocks(chunks) : 0;
@@ -595,11 +593,15 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs,
   auto mark = [&](int i) { return events ? hipEventRecord(events[i], stream) : hipSuccess; };
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return e;
-  if (dtype == 0)
-    hipLaunchKernelGGL(bwd_pre_kernel<bf16>, dim3(pre_blocks), dim3(kFlatThreads), bins_bytes, stream, a);
-  else
-    hipLaunchKernelGGL(bwd_pre_kernel<float>, dim3(pre_blocks), dim3(kFlatThreads), bins_bytes, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (T > 0) {
+    if (direct)
+      hipLaunchKernelGGL((bwd_dq_kernel<bf16, true>), grid_q, dim3(256), 0, stream, a);
+    else if (dtype == 0)
+      hipLaunchKernelGGL((bwd_dq_kernel<bf16, false>), grid_q, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<float, false>), grid_q, dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if ((e = mark(1)) != hipSuccess) return e;
   if (T > 0) {
     if (direct)
@@ -611,24 +613,12 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs,
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark(2)) != hipSuccess) return e;
-  if (T > 0) {
-    if (direct)
-      hipLaunchKernelGGL((bwd_dq_kernel<bf16, true>), grid_q, dim3(256), 0, stream, a);
-    else if (dtype == 0)
-      hipLaunchKernelGGL((bwd_dq_kernel<bf16, false>), grid_q, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((bwd_dq_kernel<float, false>), grid_q, dim3(256), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if ((e = mark(3)) != hipSuccess) return e;
   if (dtype == 0)
-    hipLaunchKernelGGL(bwd_post_kernel<bf16>, dim3(post_blocks), dim3(kFlatThreads), 0, stream, a, conv_blocks,
-                       pre_blocks);
+    hipLaunchKernelGGL(bwd_post_kernel<bf16>, dim3(post_blocks), dim3(kFlatThreads), 0, stream, a, conv_blocks, parts);
   else
-    hipLaunchKernelGGL(bwd_post_kernel<float>, dim3(post_blocks), dim3(kFlatThreads), 0, stream, a, conv_blocks,
-                       pre_blocks);
+    hipLaunchKernelGGL(bwd_post_kernel<float>, dim3(post_blocks), dim3(kFlatThreads), 0, stream, a, conv_blocks, parts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return mark(4);
+  return mark(3);
 }
 
 }  // namespace sinkattn

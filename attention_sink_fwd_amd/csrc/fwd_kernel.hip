@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int q0 = qt * kBM;
   if (q0 >= L) return;
 
-  const int hd = a.head_dim;
+  const int hd = kDirect ? kD : a.head_dim;  // the direct path is only built for head_dim == kD
   const int g = hq / (a.num_q_heads / a.num_kv_heads);
   const int qs = a.num_q_heads * hd, ks = a.num_kv_heads * hd;  // row strides (< 2^31 elements)
   const TIn* __restrict__ Qh = (const TIn*)a.q + (long)bos * qs + hq * hd;

@@ -35,7 +35,7 @@ struct BwdArgs {
   float* nlse;    // workspace: -LSE_i / scale, [Hq, T]
   float* dk_acc;  // workspace: float dK accumulator, [T, Hkv, d]
   float* dv_acc;  // workspace: float dV accumulator, [T, Hkv, d]
-  float* dsink_part;  // workspace: per-preprocess-block dS partials, [blocks, Hq]
+  float* dsink_part;  // workspace: per-query-tile dS partials, [Hq, num_seqs, query tiles]
   int num_q_heads, num_kv_heads, head_dim, total_tokens, window, num_seqs;
   int dkdv_heads;  // query heads per dK/dV workgroup (divides Hq / Hkv)
   float scale;
@@ -46,12 +46,12 @@ struct BwdArgs {
 struct BwdWorkspace {
   size_t ndelta, nlse, dk_acc, dv_acc, dsink_part, total;
 };
-BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d);
+BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d, int max_seqlen, int num_seqs);
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s);
 // Query heads per dK/dV workgroup for a problem shape (a divisor of Hq/Hkv).
 int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, int window, int num_cus);
-// events: NULL, or five events recorded around the four kernels.
+// events: NULL, or four events recorded around the three kernels.
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s,
                       const hipEvent_t* events);
 

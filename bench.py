@@ -3,7 +3,8 @@
 
 One step = the whole hot path on one batch of synthetic input already
 resident in HBM: host dispatch, the forward kernel (O, LSE), then the
-backward (D_i preprocess, main backward kernel, epilogue with dS_h).
+backward (dQ kernel with the row statistics D_i, dK/dV kernel, epilogue
+with dS_h).
 Default workload: GPT-OSS-20B-shaped attention, B=1, Hq=64, Hkv=8, d=64,
 L=4096, causal, bf16.
 
@@ -187,7 +188,7 @@ def main():
 
     K = args.steps
     sh = ctypes.c_void_p(stream.cuda_stream)
-    evs = [[hip.event() for _ in range(7)] for _ in range(K)]
+    evs = [[hip.event() for _ in range(6)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -196,7 +197,7 @@ def main():
         sa.sink_attn_fwd(q, k, v, s, cu, w.max_seqlen, w.softmax_scale, w.window, o=o, lse=lse,
                          stream=stream)
         hip.record(e[1], sh)
-        arr = (ctypes.c_void_p * 5)(e[2].value, e[3].value, e[4].value, e[5].value, e[6].value)
+        arr = (ctypes.c_void_p * 4)(e[2].value, e[3].value, e[4].value, e[5].value)
         _lib.check(lib.sink_attn_set_bwd_events(arr))
         sa.sink_attn_bwd(q, k, v, s, o, lse, do, cu, w.max_seqlen, w.softmax_scale, w.window,
                          dq=dq, dk=dk, dv=dv, dsinks=ds, workspace=ws, stream=stream)
@@ -207,7 +208,7 @@ def main():
     def avg(a, b):
         return sum(hip.ms(evs[i][a], evs[i][b]) for i in range(K)) / K
 
-    k_fwd, k_pre, k_dkdv, k_dq, k_post = avg(0, 1), avg(2, 3), avg(3, 4), avg(4, 5), avg(5, 6)
+    k_fwd, k_dq, k_dkdv, k_post = avg(0, 1), avg(2, 3), avg(3, 4), avg(4, 5)
     for row in evs:
         for e in row:
             hip.destroy(e)
@@ -252,8 +253,8 @@ def main():
             "flops_per_step": fl["total"],
         },
         "pct_bf16_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "kernel_ms": {"fwd": round(k_fwd, 4), "bwd_pre": round(k_pre, 4), "bwd_dkdv": round(k_dkdv, 4),
-                      "bwd_dq": round(k_dq, 4), "bwd_post": round(k_post, 4)},
+        "kernel_ms": {"fwd": round(k_fwd, 4), "bwd_dq": round(k_dq, 4), "bwd_dkdv": round(k_dkdv, 4),
+                      "bwd_post": round(k_post, 4)},
         "kernel_tflops": {k: round(algo[k] / (kms[k] * 1e-3) / 1e12, 1) for k in kms},
         "roofline": {
             "kernel": dom,

@@ -119,8 +119,9 @@ int sink_attn_fwd(const sink_attn_params *p, const void *q, const void *k, const
 
 /*
  * Bytes of device workspace sink_attn_bwd needs for these parameters
- * (float row statistics and float gradient accumulators, 256-byte aligned
- * sections).  Returns 0 when the parameters are invalid.
+ * (float row statistics, float dK/dV accumulators and per-query-tile dS
+ * partials, 256-byte aligned sections; the last depends on max_seqlen and
+ * num_seqs).  Returns 0 when the parameters are invalid.
  */
 size_t sink_attn_bwd_workspace_size(const sink_attn_params *p);
 
@@ -138,8 +139,10 @@ size_t sink_attn_bwd_workspace_size(const sink_attn_params *p);
  *                                  256-byte aligned; contents on entry are
  *                                  ignored and on exit unspecified.
  * LSE is treated as a saved statistic, not an output: no gradient flows into
- * it.  Float atomics accumulate dQ, dK, dV and dS, so the last bits may vary
- * from run to run.
+ * it.  dQ and dS are deterministic (dS_h is summed in a fixed order).  dK and
+ * dV are deterministic when a dK/dV workgroup covers every query head of its
+ * KV head (see Tuning); otherwise float atomics add the heads' partial sums
+ * and the last bits may vary from run to run.
  * Reference: "GPT-OSS Agentic RL Training: A Practical Retrospective",
  * section "Implementation in FlashAttention v3" (the backward pass that
  * computes the sink gradient dL/dS_h).
@@ -151,13 +154,13 @@ int sink_attn_bwd(const sink_attn_params *p, const void *q, const void *k, const
 
 /*
  * Instrumentation (benchmarks and profilers).  Sets, for the calling thread,
- * five hipEvent_t handles that every later sink_attn_bwd call on this thread
- * records on its stream: events[0] before the preprocess kernel, events[1]
- * before the dK/dV kernel, events[2] before the dQ kernel, events[3] before
- * the epilogue kernel and events[4] after it, so consecutive pairs time the
- * four kernels.  The handles are copied; the caller keeps owning the events.
- * Pass NULL to stop recording.  Returns SINK_ATTN_OK, or
- * SINK_ATTN_ERR_INVALID_ARG if one of the five handles is NULL.
+ * four hipEvent_t handles that every later sink_attn_bwd call on this thread
+ * records on its stream: events[0] before the dQ kernel (which also derives
+ * the row statistics), events[1] before the dK/dV kernel, events[2] before
+ * the epilogue kernel and events[3] after it, so consecutive pairs time the
+ * three kernels.  The handles are copied; the caller keeps owning the
+ * events.  Pass NULL to stop recording.  Returns SINK_ATTN_OK, or
+ * SINK_ATTN_ERR_INVALID_ARG if one of the four handles is NULL.
  */
 int sink_attn_set_bwd_events(void *const *events);
 

@@ -146,8 +146,8 @@ def test_workspace_size_and_too_small():
     T, hq, hkv, d = 1000, 8, 2, 64
     p = _good_params(T, hq, hkv, d)
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    pre_blocks = min(1024, (T * hq * 8 + 255) // 256)
-    want = 2 * up(4 * hq * T) + 2 * up(4 * T * hkv * d) + up(4 * pre_blocks * hq)
+    parts = (T + 127) // 128  # one dS partial per 128-row query tile and head
+    want = 2 * up(4 * hq * T) + 2 * up(4 * T * hkv * d) + up(4 * parts * hq)
     assert lib.sink_attn_bwd_workspace_size(ctypes.byref(p)) == want
     assert _bwd(p, ws_bytes=want - 1) == _lib.SINK_ATTN_ERR_WORKSPACE_TOO_SMALL
     assert "workspace" in lib.sink_attn_last_error().decode()
@@ -169,6 +169,6 @@ def test_package_raises_when_library_is_missing(monkeypatch, tmp_path):
 
 def test_set_bwd_events_validation():
     lib = _lib.load()
-    arr = (ctypes.c_void_p * 5)(FAKE, FAKE, None, FAKE, FAKE)
+    arr = (ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)
     assert lib.sink_attn_set_bwd_events(arr) == _lib.SINK_ATTN_ERR_INVALID_ARG
     assert lib.sink_attn_set_bwd_events(None) == _lib.SINK_ATTN_OK
