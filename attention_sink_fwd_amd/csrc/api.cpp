@@ -207,10 +207,12 @@ int sink_attn_set_bwd_events(void* const* events) {
     g_bwd_events_on = false;
     return SINK_ATTN_OK;
   }
-  for (int i = 0; i < 4; ++i)
-    if (!events[i]) return fail(SINK_ATTN_ERR_INVALID_ARG, "events[%d] is NULL", i);
-  for (int i = 0; i < 4; ++i) g_bwd_events[i] = static_cast<hipEvent_t>(events[i]);
-  g_bwd_events_on = true;
+  bool any = false;
+  for (int i = 0; i < 4; ++i) {
+    g_bwd_events[i] = static_cast<hipEvent_t>(events[i]);
+    any = any || events[i];
+  }
+  g_bwd_events_on = any;
   return SINK_ATTN_OK;
 }
 

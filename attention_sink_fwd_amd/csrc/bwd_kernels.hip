@@ -590,7 +590,7 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs,
   const dim3 grid_kv((max_seqlen + kBN - 1) / kBN * (Hq / a.dkdv_heads) * num_seqs);
   const dim3 grid_q((max_seqlen + kQT - 1) / kQT * Hq * num_seqs);
   const bool direct = dtype == 0 && a.head_dim == kD;
-  auto mark = [&](int i) { return events ? hipEventRecord(events[i], stream) : hipSuccess; };
+  auto mark = [&](int i) { return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess; };
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return e;
   if (T > 0) {

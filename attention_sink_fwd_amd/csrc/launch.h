@@ -51,7 +51,7 @@ BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d, int 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s);
 // Query heads per dK/dV workgroup for a problem shape (a divisor of Hq/Hkv).
 int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, int window, int num_cus);
-// events: NULL, or four events recorded around the three kernels.
+// events: NULL, or four events (NULL entries skipped) recorded around the three kernels.
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s,
                       const hipEvent_t* events);
 

@@ -9,9 +9,11 @@ Default workload: GPT-OSS-20B-shaped attention, B=1, Hq=64, Hkv=8, d=64,
 L=4096, causal, bf16.
 
 Prints ONE JSON line.  Throughput counts algorithmic flops (14*d per visible
-query/key pair per query head: 4d forward, 10d backward).  The roofline
-object is for the dominant (longest) matrix-core kernel, timed live with HIP
-events recorded around it on the stream it runs on.
+query/key pair per query head: 4d forward, 10d backward).  An untimed pass
+first brackets every kernel with HIP events (kernel_ms) and picks the
+dominant (longest) matrix-core kernel; in the timed region only that kernel
+is bracketed, with two events per step on the stream it runs on, and the
+roofline object reports it.
 """
 from __future__ import annotations
 
@@ -136,8 +138,8 @@ def calibrate_copy(nbytes=1 << 30):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2, help="workload id 1-5 (default 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -186,30 +188,61 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    K = args.steps
     sh = ctypes.c_void_p(stream.cuda_stream)
-    evs = [[hip.event() for _ in range(6)] for _ in range(K)]
+
+    def run_steps(n, fwd_events, bwd_events):
+        """n steps; fwd_events(i) -> (start, end) or None, bwd_events(i) -> 4 handles."""
+        for i in range(n):
+            fe = fwd_events(i)
+            if fe:
+                hip.record(fe[0], sh)
+            sa.sink_attn_fwd(q, k, v, s, cu, w.max_seqlen, w.softmax_scale, w.window, o=o,
+                             lse=lse, stream=stream)
+            if fe:
+                hip.record(fe[1], sh)
+            arr = (ctypes.c_void_p * 4)(*bwd_events(i))
+            _lib.check(lib.sink_attn_set_bwd_events(arr))
+            sa.sink_attn_bwd(q, k, v, s, o, lse, do, cu, w.max_seqlen, w.softmax_scale, w.window,
+                             dq=dq, dk=dk, dv=dv, dsinks=ds, workspace=ws, stream=stream)
+        _lib.check(lib.sink_attn_set_bwd_events(None))
+
+    # Untimed pass: every kernel bracketed by events, for the per-kernel
+    # breakdown and to find the dominant kernel.
+    nb = min(args.steps, 20)
+    evb = [[hip.event() for _ in range(6)] for _ in range(nb)]
+    run_steps(nb, lambda i: (evb[i][0], evb[i][1]),
+              lambda i: (evb[i][2].value, evb[i][3].value, evb[i][4].value, evb[i][5].value))
+    torch.cuda.synchronize()
+
+    def avg(evs, a, b):
+        return sum(hip.ms(e[a], e[b]) for e in evs) / len(evs)
+
+    kernel_ms = {"fwd": avg(evb, 0, 1), "bwd_dq": avg(evb, 2, 3), "bwd_dkdv": avg(evb, 3, 4),
+                 "bwd_post": avg(evb, 4, 5)}
+    for row in evb:
+        for e in row:
+            hip.destroy(e)
+    kms = {kname: kernel_ms[kname] for kname in ("fwd", "bwd_dkdv", "bwd_dq")}
+    dom = max(kms, key=kms.get)
+
+    # Timed region: K steps; only the dominant kernel is bracketed (two
+    # events per step on the stream it runs on).
+    K = args.steps
+    evt = [[hip.event() for _ in range(2)] for _ in range(K)]
+    none = None
+    if dom == "fwd":
+        fwd_ev, bwd_ev = (lambda i: (evt[i][0], evt[i][1])), (lambda i: (none, none, none, none))
+    elif dom == "bwd_dq":
+        fwd_ev, bwd_ev = (lambda i: None), (lambda i: (evt[i][0].value, evt[i][1].value, none, none))
+    else:
+        fwd_ev, bwd_ev = (lambda i: None), (lambda i: (none, evt[i][0].value, evt[i][1].value, none))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        e = evs[i]
-        hip.record(e[0], sh)
-        sa.sink_attn_fwd(q, k, v, s, cu, w.max_seqlen, w.softmax_scale, w.window, o=o, lse=lse,
-                         stream=stream)
-        hip.record(e[1], sh)
-        arr = (ctypes.c_void_p * 4)(e[2].value, e[3].value, e[4].value, e[5].value)
-        _lib.check(lib.sink_attn_set_bwd_events(arr))
-        sa.sink_attn_bwd(q, k, v, s, o, lse, do, cu, w.max_seqlen, w.softmax_scale, w.window,
-                         dq=dq, dk=dk, dv=dv, dsinks=ds, workspace=ws, stream=stream)
+    run_steps(K, fwd_ev, bwd_ev)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    _lib.check(lib.sink_attn_set_bwd_events(None))
-
-    def avg(a, b):
-        return sum(hip.ms(evs[i][a], evs[i][b]) for i in range(K)) / K
-
-    k_fwd, k_dq, k_dkdv, k_post = avg(0, 1), avg(2, 3), avg(3, 4), avg(4, 5)
-    for row in evs:
+    dom_ms = avg(evt, 0, 1)
+    for row in evt:
         for e in row:
             hip.destroy(e)
 
@@ -223,9 +256,7 @@ def main():
     pairs = w.visible_pairs()
     algo = {"fwd": 4.0 * w.head_dim * pairs, "bwd_dkdv": 8.0 * w.head_dim * pairs,
             "bwd_dq": 2.0 * w.head_dim * pairs}
-    kms = {"fwd": k_fwd, "bwd_dkdv": k_dkdv, "bwd_dq": k_dq}
-    dom = max(kms, key=kms.get)
-    dom_tflops = algo[dom] / (kms[dom] * 1e-3) / 1e12
+    dom_tflops = algo[dom] / (dom_ms * 1e-3) / 1e12
     traffic = traffic_for_current_kernel(dom)
     result = {
         "metric": METRIC,
@@ -253,11 +284,11 @@ def main():
             "flops_per_step": fl["total"],
         },
         "pct_bf16_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "kernel_ms": {"fwd": round(k_fwd, 4), "bwd_dq": round(k_dq, 4), "bwd_dkdv": round(k_dkdv, 4),
-                      "bwd_post": round(k_post, 4)},
-        "kernel_tflops": {k: round(algo[k] / (kms[k] * 1e-3) / 1e12, 1) for k in kms},
+        "kernel_ms": {kname: round(val, 4) for kname, val in kernel_ms.items()},
+        "kernel_tflops": {kname: round(algo[kname] / (kms[kname] * 1e-3) / 1e12, 1) for kname in kms},
         "roofline": {
             "kernel": dom,
+            "kernel_ms": round(dom_ms, 4),
             "bound": "mfma",
             "achieved": round(dom_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,

@@ -158,9 +158,10 @@ int sink_attn_bwd(const sink_attn_params *p, const void *q, const void *k, const
  * records on its stream: events[0] before the dQ kernel (which also derives
  * the row statistics), events[1] before the dK/dV kernel, events[2] before
  * the epilogue kernel and events[3] after it, so consecutive pairs time the
- * three kernels.  The handles are copied; the caller keeps owning the
- * events.  Pass NULL to stop recording.  Returns SINK_ATTN_OK, or
- * SINK_ATTN_ERR_INVALID_ARG if one of the four handles is NULL.
+ * three kernels.  A NULL entry skips that point (each recorded event is one
+ * more packet on the stream).  The handles are copied; the caller keeps
+ * owning the events.  Pass NULL (or four NULL entries) to stop recording.
+ * Always returns SINK_ATTN_OK.
  */
 int sink_attn_set_bwd_events(void *const *events);
 

@@ -167,8 +167,11 @@ def test_package_raises_when_library_is_missing(monkeypatch, tmp_path):
         _lib.load()
 
 
-def test_set_bwd_events_validation():
+def test_set_bwd_events_accepts_partial_and_null():
     lib = _lib.load()
-    arr = (ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)
-    assert lib.sink_attn_set_bwd_events(arr) == _lib.SINK_ATTN_ERR_INVALID_ARG
-    assert lib.sink_attn_set_bwd_events(None) == _lib.SINK_ATTN_OK
+    try:
+        arr = (ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)  # NULL entries skip that point
+        assert lib.sink_attn_set_bwd_events(arr) == _lib.SINK_ATTN_OK
+        assert lib.sink_attn_set_bwd_events((ctypes.c_void_p * 4)()) == _lib.SINK_ATTN_OK
+    finally:
+        assert lib.sink_attn_set_bwd_events(None) == _lib.SINK_ATTN_OK
