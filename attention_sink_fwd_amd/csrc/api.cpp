@@ -126,11 +126,36 @@ int sink_attn_fwd(const sink_attn_params* p, const void* q, const void* k, const
   return SINK_ATTN_OK;
 }
 
-size_t sink_attn_bwd_workspace_size(const sink_attn_params* p) {
-  if (check_params(p) != SINK_ATTN_OK) return 0;
+namespace {
+
+// Query heads per dK/dV workgroup: SINK_ATTN_DKDV_HEADS if set (it must
+// divide Hq/Hkv), else the shape-based choice.
+int resolve_dkdv_heads(const sink_attn_params* p, int* out) {
+  const int grp = p->num_q_heads / p->num_kv_heads;
+  if (const char* env = std::getenv("SINK_ATTN_DKDV_HEADS")) {
+    const int hg = std::atoi(env);
+    if (hg < 1 || grp % hg != 0)
+      return fail(SINK_ATTN_ERR_INVALID_ARG, "SINK_ATTN_DKDV_HEADS=%s must divide num_q_heads / num_kv_heads = %d", env,
+                  grp);
+    *out = hg;
+    return SINK_ATTN_OK;
+  }
+  *out = sinkattn::dkdv_heads_per_workgroup(p->total_tokens, p->max_seqlen, p->num_q_heads, p->num_kv_heads,
+                                            p->window);
+  return SINK_ATTN_OK;
+}
+
+sinkattn::BwdWorkspace workspace_layout(const sink_attn_params* p, int dkdv_heads) {
   return sinkattn::bwd_workspace_layout(p->total_tokens, p->num_q_heads, p->num_kv_heads, p->head_dim, p->max_seqlen,
-                                        p->num_seqs)
-      .total;
+                                        p->num_seqs, dkdv_heads);
+}
+
+}  // namespace
+
+size_t sink_attn_bwd_workspace_size(const sink_attn_params* p) {
+  int hg = 0;
+  if (check_params(p) != SINK_ATTN_OK || resolve_dkdv_heads(p, &hg) != SINK_ATTN_OK) return 0;
+  return workspace_layout(p, hg).total;
 }
 
 int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const void* v, const float* sinks,
@@ -151,9 +176,9 @@ int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const
     if (!lse) return fail(SINK_ATTN_ERR_INVALID_ARG, "lse is NULL");
   }
   if (!dsinks) return fail(SINK_ATTN_ERR_INVALID_ARG, "dsinks is NULL");
-  const sinkattn::BwdWorkspace ws =
-      sinkattn::bwd_workspace_layout(p->total_tokens, p->num_q_heads, p->num_kv_heads, p->head_dim, p->max_seqlen,
-                                     p->num_seqs);
+  int dkdv_heads = 0;
+  SA_CHECK(resolve_dkdv_heads(p, &dkdv_heads));
+  const sinkattn::BwdWorkspace ws = workspace_layout(p, dkdv_heads);
   if (workspace_bytes < ws.total)
     return fail(SINK_ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, ws.total);
   if (ws.total > 0 && !workspace) return fail(SINK_ATTN_ERR_INVALID_ARG, "workspace is NULL");
@@ -171,30 +196,14 @@ int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const
   auto carve = [&](size_t bytes) { float* p = reinterpret_cast<float*>(wsb + off); off += bytes; return p; };
   a.ndelta = carve(ws.ndelta);
   a.nlse = carve(ws.nlse);
-  a.dk_acc = carve(ws.dk_acc);
-  a.dv_acc = carve(ws.dv_acc);
+  a.dk_part = carve(ws.dk_part);
+  a.dv_part = carve(ws.dv_part);
   a.dsink_part = carve(ws.dsink_part);
   a.num_q_heads = p->num_q_heads; a.num_kv_heads = p->num_kv_heads; a.head_dim = p->head_dim;
   a.total_tokens = p->total_tokens; a.window = p->window; a.num_seqs = p->num_seqs;
   a.scale = p->softmax_scale;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
-  a.dkdv_heads = 0;
-  if (const char* env = std::getenv("SINK_ATTN_DKDV_HEADS")) {
-    const int grp = p->num_q_heads / p->num_kv_heads;
-    const int hg = std::atoi(env);
-    if (hg < 1 || grp % hg != 0)
-      return fail(SINK_ATTN_ERR_INVALID_ARG, "SINK_ATTN_DKDV_HEADS=%s must divide num_q_heads / num_kv_heads = %d", env,
-                  grp);
-    a.dkdv_heads = hg;
-  }
-  if (a.dkdv_heads == 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-      return fail(SINK_ATTN_ERR_HIP, "cannot query the compute-unit count of the current device");
-    a.dkdv_heads = sinkattn::dkdv_heads_per_workgroup(p->total_tokens, p->max_seqlen, p->num_q_heads,
-                                                      p->num_kv_heads, p->window, cus);
-  }
+  a.dkdv_heads = dkdv_heads;
   hipError_t e = sinkattn::launch_bwd(a, p->dtype, p->max_seqlen, p->num_seqs, s,
                                        g_bwd_events_on ? g_bwd_events : nullptr);
   if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));

@@ -17,8 +17,7 @@
 //                      the workspace for the next kernel.  Then it loops over
 //                      the visible 64-key tiles: recomputes S and dP in
 //                      transposed form and accumulates dQ = scale * dS K in
-//                      registers; writes dQ once.  When the next kernel will
-//                      use float atomics it also clears their accumulators.
+//                      registers; writes dQ once.
 //  2. bwd_dkdv_kernel  one workgroup per (sequence, 128-key tile, group of
 //                      query heads sharing a KV head), looping over the
 //                      visible 64-row query tiles of each of those heads:
@@ -26,10 +25,13 @@
 //                      dS = P (dP - D), dV += P^T dO, dK += dS^T Q on the
 //                      matrix cores, K, V, dK, dV in registers; writes dK, dV
 //                      directly when the group covers all heads of the KV
-//                      head, else adds them to float accumulators.
-//  3. bwd_post_kernel  sums the per-tile dS partials of each head in a fixed
-//                      order (deterministic dS_h) and, after atomics,
-//                      converts the dK/dV accumulators to the output type.
+//                      head, else stores its float partial sums.
+//  3. bwd_post_kernel  sums the per-tile dS partials of each head and the
+//                      dK/dV partial sums of the head groups, each in a fixed
+//                      order, and converts the latter to the output type.
+//
+// No float atomics anywhere: every gradient is a fixed-order sum, so the
+// backward pass is bitwise reproducible run to run.
 //
 // dQ is not accumulated with float atomics across key tiles: on this chip
 // float atomics retire at about 0.3 G element-operations per microsecond,
@@ -50,16 +52,6 @@ constexpr int kFlatThreads = 256;
 // VMEM instructions one wavefront issues per query-tile prefetch of the
 // dK/dV kernel on the direct path (2 Q + 2 dO + 1 statistics).
 constexpr int kPrefetchOps = 5;
-__device__ __forceinline__ void convert8(const float* src, bf16* dst) {
-  const f32x4 x = *(const f32x4*)src, y = *(const f32x4*)(src + 4);
-  const f32x8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-  *(bf16x8*)dst = __builtin_convertvector(v, bf16x8);
-}
-__device__ __forceinline__ void convert8(const float* src, float* dst) {
-  *(f32x4*)dst = *(const f32x4*)src;
-  *(f32x4*)(dst + 4) = *(const f32x4*)(src + 4);
-}
-
 template <typename TIn>
 __global__ __launch_bounds__(256) void bwd_post_kernel(BwdArgs a, int conv_blocks, int parts) {
   const int tid = threadIdx.x;
@@ -75,12 +67,16 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(BwdArgs a, int conv_block
     if ((tid & 63) == 0) a.dsinks[h] = s;
     return;
   }
+  // dK, dV = the head groups' partial sums, in group order.
   const long kchunks = (long)a.total_tokens * a.num_kv_heads * a.head_dim / 8;
+  const int P = a.num_q_heads / a.num_kv_heads / a.dkdv_heads;
   for (long c = (long)blockIdx.x * kFlatThreads + tid; c < 2 * kchunks; c += (long)conv_blocks * kFlatThreads) {
-    if (c < kchunks)
-      convert8(a.dk_acc + 8 * c, (TIn*)a.dk + 8 * c);
-    else
-      convert8(a.dv_acc + 8 * (c - kchunks), (TIn*)a.dv + 8 * (c - kchunks));
+    const bool is_k = c < kchunks;
+    const long e = 8 * (is_k ? c : c - kchunks);
+    const float* src = (is_k ? a.dk_part : a.dv_part) + e;
+    f32x8 acc = load8f(src);
+    for (int j = 1; j < P; ++j) acc += load8f(src + (long)j * 8 * kchunks);
+    store8((TIn*)(is_k ? a.dk : a.dv) + e, acc);
   }
 }
 
@@ -311,8 +307,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     }
     return;
   }
-  float* dk_g = a.dk_acc + (long)bos * ks + g * hd;
-  float* dv_g = a.dv_acc + (long)bos * ks + g * hd;
+  // Partial sums of this head group: plane j of the partial buffers.
+  const long plane = (long)T * ks;
+  const int j = (hq0 % grp) / HG;
+  float* dk_g = a.dk_part + j * plane + (long)bos * ks + g * hd;
+  float* dv_g = a.dv_part + j * plane + (long)bos * ks + g * hd;
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
     const int d = 32 * db + l32;
@@ -321,8 +320,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     for (int r = 0; r < 16; ++r) {
       const int key = wk_lo + 8 * (r >> 2) + 4 * h2 + (r & 3);
       if (key < L) {
-        unsafeAtomicAdd(dk_g + key * ks + d, dk[db][r] * a.scale);
-        unsafeAtomicAdd(dv_g + key * ks + d, dv[db][r]);
+        dk_g[key * ks + d] = dk[db][r] * a.scale;
+        dv_g[key * ks + d] = dv[db][r];
       }
     }
   }
@@ -351,18 +350,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int h2 = lane >> 5, l32 = lane & 31;
   // The direct path is only built for head_dim == kD.
   const int hd = kDirect ? kD : a.head_dim, T = a.total_tokens, window = a.window;
-  if (a.dkdv_heads * a.num_kv_heads != a.num_q_heads) {
-    // The dK/dV kernel will add partial sums: clear its float accumulators,
-    // one slice per workgroup (T * Hkv * d is a multiple of 8).
-    const long n4 = (long)T * a.num_kv_heads * hd / 4;
-    const long per = (n4 + gridDim.x - 1) / gridDim.x;
-    const long end = min(n4, (long)(blockIdx.x + 1) * per);
-    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (long c = (long)blockIdx.x * per + tid; c < end; c += 256) {
-      *(f32x4*)(a.dk_acc + 4 * c) = z;
-      *(f32x4*)(a.dv_acc + 4 * c) = z;
-    }
-  }
   const TileUnit unit = xcd_unit(a.num_q_heads, a.num_seqs);
   const int seq = unit.seq, hq = unit.head;
   const int ntiles = (int)gridDim.x / (a.num_q_heads * a.num_seqs);
@@ -546,19 +533,22 @@ int flat_blocks(long work_items) {
 
 int bwd_dsink_parts(int max_seqlen, int num_seqs) { return (max_seqlen + kQT - 1) / kQT * num_seqs; }
 
-BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d, int max_seqlen, int num_seqs) {
+BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d, int max_seqlen, int num_seqs,
+                                  int dkdv_heads) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const int P = hq / hkv / dkdv_heads;  // head groups per KV head
   BwdWorkspace w;
   w.ndelta = up((size_t)hq * total_tokens * sizeof(float));
   w.nlse = w.ndelta;
-  w.dk_acc = up((size_t)total_tokens * hkv * d * sizeof(float));
-  w.dv_acc = w.dk_acc;
+  w.dk_part = P > 1 ? up((size_t)P * total_tokens * hkv * d * sizeof(float)) : 0;
+  w.dv_part = w.dk_part;
   w.dsink_part = up((size_t)bwd_dsink_parts(max_seqlen, num_seqs) * hq * sizeof(float));
-  w.total = w.ndelta + w.nlse + w.dk_acc + w.dv_acc + w.dsink_part;
+  w.total = w.ndelta + w.nlse + w.dk_part + w.dv_part + w.dsink_part;
   return w;
 }
 
-int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, int window, int num_cus) {
+int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, int window) {
+  constexpr long num_cus = 256;
   const int grp = hq / hkv;
   // Work in (64-row query step x 128-key tile) units.  Longest workgroup per
   // head: key tile 0 of a max_seqlen sequence.  Average per key tile: half of
@@ -570,8 +560,8 @@ int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, 
                                     : max_seqlen / (2 * kBM) + 1;
   const long tiles = ((long)total_tokens + kBN - 1) / kBN;
   const long per_slot = (long)hq * tiles * steps_avg / (2L * num_cus);  // two workgroups per CU
-  // The most heads per workgroup (fewest atomics; none for the whole group)
-  // such that the longest workgroup fits in a slot's average load and the
+  // The most heads per workgroup (fewest partial sums; none for the whole
+  // group) such that the longest workgroup fits in a slot's average load and the
   // tail it leaves (its excess over an average workgroup) stays within an
   // eighth of that load.
   for (int hg = grp; hg > 1; --hg)
@@ -584,8 +574,8 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs,
   const int T = a.total_tokens, Hq = a.num_q_heads;
   const int parts = T > 0 ? bwd_dsink_parts(max_seqlen, num_seqs) : 0;
   const long chunks = (long)T * 2 * a.num_kv_heads * a.head_dim / 8;
-  const bool dkdv_atomics = a.dkdv_heads * a.num_kv_heads != Hq;
-  const int conv_blocks = (T > 0 && dkdv_atomics) ? flat_blocks(chunks) : 0;
+  const bool dkdv_partials = a.dkdv_heads * a.num_kv_heads != Hq;
+  const int conv_blocks = (T > 0 && dkdv_partials) ? flat_blocks(chunks) : 0;
   const int post_blocks = conv_blocks + (Hq + 3) / 4;
   const dim3 grid_kv((max_seqlen + kBN - 1) / kBN * (Hq / a.dkdv_heads) * num_seqs);
   const dim3 grid_q((max_seqlen + kQT - 1) / kQT * Hq * num_seqs);

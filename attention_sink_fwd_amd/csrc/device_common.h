@@ -70,6 +70,13 @@ __device__ __forceinline__ void store4(bf16* p, f32x4 v) {
 }
 __device__ __forceinline__ void store4(float* p, f32x4 v) { *(f32x4*)p = v; }
 
+// Store 8 consecutive floats in the output type (16-byte aligned).
+__device__ __forceinline__ void store8(bf16* p, f32x8 v) { *(bf16x8*)p = __builtin_convertvector(v, bf16x8); }
+__device__ __forceinline__ void store8(float* p, f32x8 v) {
+  *(f32x4*)p = f32x4{v[0], v[1], v[2], v[3]};
+  *(f32x4*)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
 // Operand fragment (8 consecutive contraction indices k for lane index n)
 // from a row-major LDS tile X[k][n] whose n index is contiguous, row stride
 // `ld` elements: lane l receives X[k0 + 8*(l/32) + s][n0 + l%32], s = 0..7.

@@ -33,8 +33,8 @@ struct BwdArgs {
   float* dsinks;
   float* ndelta;  // workspace: -D_i = -(dO_i . O_i), [Hq, T]
   float* nlse;    // workspace: -LSE_i / scale, [Hq, T]
-  float* dk_acc;  // workspace: float dK accumulator, [T, Hkv, d]
-  float* dv_acc;  // workspace: float dV accumulator, [T, Hkv, d]
+  float* dk_part;  // workspace: float dK partial sums, [P, T, Hkv, d], P = (Hq/Hkv) / dkdv_heads
+  float* dv_part;  // workspace: float dV partial sums, same shape (both unused when P == 1)
   float* dsink_part;  // workspace: per-query-tile dS partials, [Hq, num_seqs, query tiles]
   int num_q_heads, num_kv_heads, head_dim, total_tokens, window, num_seqs;
   int dkdv_heads;  // query heads per dK/dV workgroup (divides Hq / Hkv)
@@ -44,13 +44,15 @@ struct BwdArgs {
 
 // Workspace sections (bytes, each rounded up to 256).
 struct BwdWorkspace {
-  size_t ndelta, nlse, dk_acc, dv_acc, dsink_part, total;
+  size_t ndelta, nlse, dk_part, dv_part, dsink_part, total;
 };
-BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d, int max_seqlen, int num_seqs);
+BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d, int max_seqlen, int num_seqs,
+                                  int dkdv_heads);
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s);
-// Query heads per dK/dV workgroup for a problem shape (a divisor of Hq/Hkv).
-int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, int window, int num_cus);
+// Query heads per dK/dV workgroup for a problem shape (a divisor of Hq/Hkv),
+// sized for the 256 compute units of an MI355X.
+int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, int window);
 // events: NULL, or four events (NULL entries skipped) recorded around the three kernels.
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s,
                       const hipEvent_t* events);

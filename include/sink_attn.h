@@ -54,10 +54,12 @@
  *
  * Tuning.  The backward's dK/dV kernel gives each workgroup one 128-key tile
  * and some of the query heads that share its KV head: all of them when the
- * problem has enough parallel work (dK, dV written once), else fewer, with
- * float atomics combining their partial sums in the workspace.  The library
- * picks the number from the shape; SINK_ATTN_DKDV_HEADS=n (a divisor of
- * num_q_heads / num_kv_heads) overrides it, for tests and tuning.
+ * problem has enough parallel work (dK, dV written once), else fewer, each
+ * workgroup storing its float partial sums to the workspace for a fixed-order
+ * sum.  The library picks the number from the shape (for an MI355X's 256
+ * compute units); SINK_ATTN_DKDV_HEADS=n (a divisor of num_q_heads /
+ * num_kv_heads) overrides it, for tests and tuning.  The workspace size
+ * depends on it: query sink_attn_bwd_workspace_size under the same setting.
  *
  * Streams.  All work is enqueued on `stream` (a hipStream_t; NULL is the
  * default stream) and is asynchronous.  Entry points are thread-safe.
@@ -119,9 +121,9 @@ int sink_attn_fwd(const sink_attn_params *p, const void *q, const void *k, const
 
 /*
  * Bytes of device workspace sink_attn_bwd needs for these parameters
- * (float row statistics, float dK/dV accumulators and per-query-tile dS
- * partials, 256-byte aligned sections; the last depends on max_seqlen and
- * num_seqs).  Returns 0 when the parameters are invalid.
+ * (float row statistics, float dK/dV partial sums of the head groups and
+ * per-query-tile dS partials, 256-byte aligned sections; the last depends on
+ * max_seqlen and num_seqs).  Returns 0 when the parameters are invalid.
  */
 size_t sink_attn_bwd_workspace_size(const sink_attn_params *p);
 
@@ -139,10 +141,9 @@ size_t sink_attn_bwd_workspace_size(const sink_attn_params *p);
  *                                  256-byte aligned; contents on entry are
  *                                  ignored and on exit unspecified.
  * LSE is treated as a saved statistic, not an output: no gradient flows into
- * it.  dQ and dS are deterministic (dS_h is summed in a fixed order).  dK and
- * dV are deterministic when a dK/dV workgroup covers every query head of its
- * KV head (see Tuning); otherwise float atomics add the heads' partial sums
- * and the last bits may vary from run to run.
+ * it.  No float atomics are used: every gradient, dS_h included, is summed in
+ * a fixed order, so repeated calls on the same inputs give bitwise identical
+ * results.
  * Reference: "GPT-OSS Agentic RL Training: A Practical Retrospective",
  * section "Implementation in FlashAttention v3" (the backward pass that
  * computes the sink gradient dL/dS_h).

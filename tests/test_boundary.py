@@ -147,11 +147,24 @@ def test_workspace_size_and_too_small():
     p = _good_params(T, hq, hkv, d)
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     parts = (T + 127) // 128  # one dS partial per 128-row query tile and head
-    want = 2 * up(4 * hq * T) + 2 * up(4 * T * hkv * d) + up(4 * parts * hq)
+    # dK/dV partial sums: one plane per head group; this small shape takes one
+    # head per group (P = hq / hkv planes)
+    want = 2 * up(4 * hq * T) + 2 * up(4 * (hq // hkv) * T * hkv * d) + up(4 * parts * hq)
     assert lib.sink_attn_bwd_workspace_size(ctypes.byref(p)) == want
     assert _bwd(p, ws_bytes=want - 1) == _lib.SINK_ATTN_ERR_WORKSPACE_TOO_SMALL
     assert "workspace" in lib.sink_attn_last_error().decode()
     assert _bwd(p, ws_bytes=want, ws=FAKE + 16) == _lib.SINK_ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("heads,planes", [(4, 0), (2, 2), (1, 4)])
+def test_workspace_follows_dkdv_heads(monkeypatch, heads, planes):
+    monkeypatch.setenv("SINK_ATTN_DKDV_HEADS", str(heads))
+    lib = _lib.load()
+    T, hq, hkv, d = 1000, 8, 2, 64
+    p = _good_params(T, hq, hkv, d)
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    want = 2 * up(4 * hq * T) + 2 * up(4 * planes * T * hkv * d) + up(4 * ((T + 127) // 128) * hq)
+    assert lib.sink_attn_bwd_workspace_size(ctypes.byref(p)) == want
 
 
 def test_forward_with_no_tokens_is_a_no_op():

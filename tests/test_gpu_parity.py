@@ -135,6 +135,32 @@ def test_forward_is_deterministic_and_packing_is_invariant():
     assert rel_l2(ds_sum, a["ds"]) < 1e-5
 
 
+@pytest.mark.parametrize("heads", [1, 2, "group"])
+@pytest.mark.parametrize("window", [0, 37])
+def test_backward_is_bitwise_reproducible(monkeypatch, heads, window):
+    """Same inputs, different workspace garbage: identical bits (no atomics)."""
+    import attention_sink_fwd_amd as sa
+
+    w = custom_workload((300, 5, 190), 8, 2, 64, window, "bf16")
+    hg = 4 if heads == "group" else heads
+    monkeypatch.setenv("SINK_ATTN_DKDV_HEADS", str(hg))
+    say("case bitwise backward", w.lengths, "window", window, "dkdv_heads", hg)
+    d = {k: v.to("cuda:0") for k, v in make_inputs(w, seed=5 + window).items()}
+    o, lse = sa.sink_attn_fwd(d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens"], w.max_seqlen,
+                              w.softmax_scale, window)
+    nb = sa.sink_attn_bwd_workspace_size(d["q"], d["k"], d["cu_seqlens"], w.max_seqlen,
+                                         w.softmax_scale, window)
+    outs = []
+    for fill in (0x00, 0x7F):
+        ws = torch.full((nb,), fill, dtype=torch.uint8, device="cuda:0")
+        r = sa.sink_attn_bwd(d["q"], d["k"], d["v"], d["sinks"], o, lse, d["dout"], d["cu_seqlens"],
+                             w.max_seqlen, w.softmax_scale, window, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in r])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 def test_empty_batch_zeroes_dsinks():
     import attention_sink_fwd_amd as sa
     dev = "cuda:0"
