@@ -7,5 +7,6 @@ from .binding import (  # noqa: F401
     sink_attn_bwd,
     sink_attn_bwd_workspace_size,
     sink_attn_fwd,
+    sink_attn_fwd_paged,
 )
 from ._lib import LIB_PATH, SinkAttnError, load  # noqa: F401

@@ -22,6 +22,7 @@ SINK_ATTN_F32 = 1
 
 EXPORTED_SYMBOLS = (
     "sink_attn_fwd",
+    "sink_attn_fwd_paged",
     "sink_attn_bwd",
     "sink_attn_bwd_workspace_size",
     "sink_attn_set_bwd_events",
@@ -43,6 +44,18 @@ class SinkAttnParams(ctypes.Structure):
         ("causal", ctypes.c_int32),
         ("window", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+    ]
+
+
+class SinkAttnPagedKV(ctypes.Structure):
+    _fields_ = [
+        ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("kv_lens", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
     ]
 
 
@@ -69,6 +82,8 @@ def load() -> ctypes.CDLL:
     vp = ctypes.c_void_p
     lib.sink_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     lib.sink_attn_fwd.restype = ctypes.c_int
+    lib.sink_attn_fwd_paged.argtypes = [P, ctypes.POINTER(SinkAttnPagedKV), vp, vp, vp, vp, vp]
+    lib.sink_attn_fwd_paged.restype = ctypes.c_int
     lib.sink_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   ctypes.c_size_t, vp]
     lib.sink_attn_bwd.restype = ctypes.c_int

@@ -82,6 +82,43 @@ def sink_attn_fwd(q, k, v, sinks, cu_seqlens, max_seqlen, softmax_scale=None, wi
     return o, lse
 
 
+def sink_attn_fwd_paged(q, k_cache, v_cache, block_table, kv_lens, sinks, cu_seqlens, max_seqlen,
+                        softmax_scale=None, window=0, o=None, lse=None,
+                        stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O [T, Hq, d] and LSE [Hq, T] of the new tokens q over a paged KV cache.
+
+    k_cache, v_cache: [num_pages, page_size, Hkv, d]; block_table int32
+    [num_seqs, max_blocks_per_seq]; kv_lens int32 [num_seqs]; cu_seqlens and
+    max_seqlen describe the new tokens of each sequence.
+    """
+    lib = _lib.load()
+    T, hq, d = q.shape
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [num_pages, page_size, num_kv_heads, head_dim]")
+    num_pages, page_size, hkv, _ = k_cache.shape
+    _need(q, "q"); _need(k_cache, "k_cache", q.dtype, (num_pages, page_size, hkv, d))
+    _need(v_cache, "v_cache", q.dtype, k_cache.shape)
+    _need(sinks, "sinks", torch.float32, (hq,)); _need(cu_seqlens, "cu_seqlens", torch.int32)
+    num_seqs = cu_seqlens.numel() - 1
+    _need(kv_lens, "kv_lens", torch.int32, (num_seqs,))
+    if block_table.dim() != 2 or block_table.shape[0] != num_seqs:
+        raise ValueError("block_table must be [num_seqs, max_blocks_per_seq]")
+    _need(block_table, "block_table", torch.int32)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((hq, T), dtype=torch.float32, device=q.device)
+    _need(o, "o", q.dtype, q.shape); _need(lse, "lse", torch.float32, (hq, T))
+    p = make_params(q, k_cache[0], cu_seqlens, max_seqlen, softmax_scale, window)
+    kv = _lib.SinkAttnPagedKV()
+    kv.k_cache, kv.v_cache = _ptr(k_cache), _ptr(v_cache)
+    kv.block_table, kv.kv_lens = _ptr(block_table), _ptr(kv_lens)
+    kv.num_pages, kv.page_size, kv.max_blocks_per_seq = num_pages, page_size, block_table.shape[1]
+    _lib.check(lib.sink_attn_fwd_paged(ctypes.byref(p), ctypes.byref(kv), _ptr(q), _ptr(sinks),
+                                       _ptr(o), _ptr(lse), _stream(stream)))
+    return o, lse
+
+
 def sink_attn_bwd_workspace_size(q, k, cu_seqlens, max_seqlen, softmax_scale=None, window=0) -> int:
     lib = _lib.load()
     p = make_params(q, k, cu_seqlens, max_seqlen, softmax_scale, window)

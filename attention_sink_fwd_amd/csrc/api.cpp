@@ -115,7 +115,7 @@ int sink_attn_fwd(const sink_attn_params* p, const void* q, const void* k, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   SA_CHECK(maybe_validate_cu(p, s));
 
-  sinkattn::FwdArgs a;
+  sinkattn::FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.sinks = sinks; a.o = o; a.lse = lse;
   a.cu_seqlens = p->cu_seqlens;
   a.num_q_heads = p->num_q_heads; a.num_kv_heads = p->num_kv_heads; a.head_dim = p->head_dim;
@@ -123,6 +123,72 @@ int sink_attn_fwd(const sink_attn_params* p, const void* q, const void* k, const
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   hipError_t e = sinkattn::launch_fwd(a, p->dtype, p->max_seqlen, p->num_seqs, s);
   if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+  return SINK_ATTN_OK;
+}
+
+namespace {
+
+// Optional host-side check of the paged cache description against the device
+// arrays (SINK_ATTN_VALIDATE=1); synchronises.
+int maybe_validate_paged(const sink_attn_params* p, const sink_attn_paged_kv* kv, hipStream_t stream) {
+  const char* env = std::getenv("SINK_ATTN_VALIDATE");
+  if (!env || env[0] != '1') return SINK_ATTN_OK;
+  std::vector<int32_t> cu(p->num_seqs + 1), lens(p->num_seqs), bt((size_t)p->num_seqs * kv->max_blocks_per_seq);
+  hipError_t e = hipMemcpyAsync(cu.data(), p->cu_seqlens, cu.size() * 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(lens.data(), kv->kv_lens, lens.size() * 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(bt.data(), kv->block_table, bt.size() * 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "reading the paged-cache arrays: %s", hipGetErrorString(e));
+  for (int s = 0; s < p->num_seqs; ++s) {
+    const int qlen = cu[s + 1] - cu[s], kvlen = lens[s];
+    if (kvlen < qlen || kvlen > kv->max_blocks_per_seq * kv->page_size)
+      return fail(SINK_ATTN_ERR_INVALID_ARG, "sequence %d: kv_len %d must lie in [%d, %d]", s, kvlen, qlen,
+                  kv->max_blocks_per_seq * kv->page_size);
+    for (int b = 0; b * kv->page_size < kvlen; ++b) {
+      const int pid = bt[(size_t)s * kv->max_blocks_per_seq + b];
+      if (pid < 0 || pid >= kv->num_pages)
+        return fail(SINK_ATTN_ERR_INVALID_ARG, "block_table[%d][%d] = %d is not a page id", s, b, pid);
+    }
+  }
+  return SINK_ATTN_OK;
+}
+
+}  // namespace
+
+int sink_attn_fwd_paged(const sink_attn_params* p, const sink_attn_paged_kv* kv, const void* q, const float* sinks,
+                        void* o, float* lse, void* stream) {
+  g_last_error[0] = '\0';
+  SA_CHECK(check_params(p));
+  if (!kv) return fail(SINK_ATTN_ERR_INVALID_ARG, "kv is NULL");
+  if (kv->page_size < 64 || kv->page_size % 64 != 0)
+    return fail(SINK_ATTN_ERR_INVALID_ARG, "page_size must be a positive multiple of 64 (got %d)", kv->page_size);
+  if (kv->num_pages < 1) return fail(SINK_ATTN_ERR_INVALID_ARG, "num_pages must be >= 1");
+  if (kv->max_blocks_per_seq < 1) return fail(SINK_ATTN_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
+  if ((int64_t)kv->max_blocks_per_seq * kv->page_size > INT32_MAX)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "max_blocks_per_seq * page_size must stay below 2^31");
+  if (p->total_tokens == 0) return SINK_ATTN_OK;  // nothing to read or write
+  SA_CHECK(check_tensor(q, "q"));
+  SA_CHECK(check_tensor(kv->k_cache, "k_cache"));
+  SA_CHECK(check_tensor(kv->v_cache, "v_cache"));
+  SA_CHECK(check_tensor(o, "o"));
+  if (!kv->block_table) return fail(SINK_ATTN_ERR_INVALID_ARG, "block_table is NULL");
+  if (!kv->kv_lens) return fail(SINK_ATTN_ERR_INVALID_ARG, "kv_lens is NULL");
+  if (!sinks) return fail(SINK_ATTN_ERR_INVALID_ARG, "sinks is NULL");
+  if (!lse) return fail(SINK_ATTN_ERR_INVALID_ARG, "lse is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SA_CHECK(maybe_validate_cu(p, s));
+  SA_CHECK(maybe_validate_paged(p, kv, s));
+
+  sinkattn::FwdArgs a{};
+  a.q = q; a.k = kv->k_cache; a.v = kv->v_cache; a.sinks = sinks; a.o = o; a.lse = lse;
+  a.cu_seqlens = p->cu_seqlens;
+  a.num_q_heads = p->num_q_heads; a.num_kv_heads = p->num_kv_heads; a.head_dim = p->head_dim;
+  a.total_tokens = p->total_tokens; a.window = p->window; a.num_seqs = p->num_seqs;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.block_table = kv->block_table; a.kv_lens = kv->kv_lens;
+  a.page_size = kv->page_size; a.max_blocks_per_seq = kv->max_blocks_per_seq; a.num_pages = kv->num_pages;
+  hipError_t e = sinkattn::launch_fwd(a, p->dtype, p->max_seqlen, p->num_seqs, s);
+  if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "paged forward launch: %s", hipGetErrorString(e));
   return SINK_ATTN_OK;
 }
 
@@ -188,7 +254,7 @@ int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const
   SA_CHECK(maybe_validate_cu(p, s));
 
   char* wsb = static_cast<char*>(workspace);
-  sinkattn::BwdArgs a;
+  sinkattn::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.sinks = sinks;
   a.cu_seqlens = p->cu_seqlens;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dsinks = dsinks;

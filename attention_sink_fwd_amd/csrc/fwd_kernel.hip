@@ -18,11 +18,13 @@
 // from the row-major V tile through transposing LDS reads.  The epilogue
 // writes O = acc / l and LSE = m + ln(l) (natural log, sink included).
 //
-// The reference max m is only raised when a tile's max exceeds it by more
-// than kRescaleSlack (log2 units) in some row of the wavefront; otherwise the
-// tile is exponentiated against the old m (values up to 2^kRescaleSlack) and
-// the 32-register accumulator rescale is skipped.  The result is the same
-// softmax: m cancels between O's numerator and l.
+// A row's reference max m is only raised when a tile's max exceeds it by
+// more than kRescaleSlack (log2 units); otherwise the tile is exponentiated
+// against the old m (values up to 2^kRescaleSlack), and when no row of the
+// wavefront needs it the 32-register accumulator rescale is skipped.  The
+// result is the same softmax: m cancels between O's numerator and l.  The
+// decision is per row, so a row's bits do not depend on the other rows that
+// share its wavefront.
 #include <type_traits>
 
 #include "device_common.h"
@@ -43,7 +45,11 @@ struct __attribute__((aligned(16))) KVStage {
   bf16 v[kBN * kD];  // V tile, swizzled [key][d]
 };
 
-template <typename TIn, bool kDirect>
+// kPaged: keys and values come from a paged cache (new query rows of a
+// sequence at the end of its cached context); otherwise they are the packed
+// tokens of the sequence itself (query row i at position i).  The arithmetic
+// per query row is the same in both, so a row gets the same bits either way.
+template <typename TIn, bool kDirect, bool kPaged>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   __shared__ KVStage stage[kStages];
 
@@ -55,7 +61,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int ntiles = (int)gridDim.x / (a.num_q_heads * a.num_seqs);
   const int qt = ntiles - 1 - unit.rank;  // heaviest (last) query tiles first
   const int bos = a.cu_seqlens[seq];
-  const int L = a.cu_seqlens[seq + 1] - bos;
+  const int L = a.cu_seqlens[seq + 1] - bos;  // query rows of this sequence
   const int q0 = qt * kBM;
   if (q0 >= L) return;
 
@@ -63,30 +69,67 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int g = hq / (a.num_q_heads / a.num_kv_heads);
   const int qs = a.num_q_heads * hd, ks = a.num_kv_heads * hd;  // row strides (< 2^31 elements)
   const TIn* __restrict__ Qh = (const TIn*)a.q + (long)bos * qs + hq * hd;
-  const TIn* __restrict__ Kg = (const TIn*)a.k + (long)bos * ks + g * hd;
-  const TIn* __restrict__ Vg = (const TIn*)a.v + (long)bos * ks + g * hd;
+
+  // Keys of this sequence and the position of query row 0.  A paged
+  // sequence's length is clamped to what its block-table row can address.
+  // (A length below the number of new rows is raised to it; both stay within
+  // the block-table row, so bad lengths give wrong values, never a fault.)
+  int kvlen = L, qoff = 0;
+  if constexpr (kPaged) {
+    const int cap = a.max_blocks_per_seq * a.page_size;
+    kvlen = __builtin_amdgcn_readfirstlane(min(max(a.kv_lens[seq], L), cap));
+    qoff = max(0, kvlen - L);
+  }
+  const TIn* __restrict__ Kg = (const TIn*)a.k + (kPaged ? 0L : (long)bos * ks) + g * hd;
+  const TIn* __restrict__ Vg = (const TIn*)a.v + (kPaged ? 0L : (long)bos * ks) + g * hd;
 
   const int window = a.window;
-  const int kend = min(L, q0 + kBM);
-  const int kbeg = window > 0 ? max(0, q0 - window + 1) : 0;
-  const int t0 = kbeg / kBN, t1 = (kend + kBN - 1) / kBN;
+  const int kend = min(kvlen, qoff + min(L, q0 + kBM));
+  const int kbeg = window > 0 ? max(0, qoff + q0 - window + 1) : 0;
+  const int t0 = kbeg / kBN, t1 = (kend + kBN - 1) / kBN;  // t0 < t1 unless a paged length was bad
+
+  // Row offset (in keys) of tile t within the key/value tensors: the packed
+  // sequence, or the tile's page of the cache (a page holds a whole number
+  // of tiles; page ids outside the cache are clamped into it).
+  // The block-table entry of the next tile is loaded one prefetch early and
+  // only used at the next one, so its latency never stalls the wavefront.
+  const int* __restrict__ bt = kPaged ? a.block_table + (long)seq * a.max_blocks_per_seq : nullptr;
+  int pid_next = 0, k0_next = 0;  // paged: raw page id and first key of the next tile to prefetch
+  auto load_page = [&](int t) {
+    k0_next = min(t, t1 - 1) * kBN;
+    pid_next = bt[k0_next / a.page_size];
+  };
+  auto page_row = [&]() -> long {
+    const int pid = __builtin_amdgcn_readfirstlane(pid_next);
+    return (long)min(max(pid, 0), a.num_pages - 1) * a.page_size + k0_next % a.page_size;
+  };
 
   // Prefetch key tile t (clamped to the last tile) into stage buf; on the
   // direct path exactly 4 VMEM instructions per wavefront.
   auto prefetch = [&](int t, int buf) {
     const int k0 = min(t, t1 - 1) * kBN;
     KVStage& st = stage[buf];
+    const long prow = kPaged ? page_row() : 0;
+    const TIn* kb = kPaged ? Kg + prow * ks : Kg;
+    const TIn* vb = kPaged ? Vg + prow * ks : Vg;
+    const int row0 = kPaged ? 0 : k0, nvalid = kPaged ? kvlen - k0 : kvlen;
     if constexpr (kDirect) {
-      stage_direct<kBN>(st.k, (const bf16*)Kg, k0, L, ks, w, lane);
-      stage_direct<kBN>(st.v, (const bf16*)Vg, k0, L, ks, w, lane);
+      stage_direct<kBN>(st.k, (const bf16*)kb, row0, nvalid, ks, w, lane);
+      stage_direct<kBN>(st.v, (const bf16*)vb, row0, nvalid, ks, w, lane);
     } else {
-      stage_regs<kBN>(st.k, Kg, k0, L, ks, hd, tid);
-      stage_regs<kBN>(st.v, Vg, k0, L, ks, hd, tid);
+      stage_regs<kBN>(st.k, kb, row0, nvalid, ks, hd, tid);
+      stage_regs<kBN>(st.v, vb, row0, nvalid, ks, hd, tid);
     }
+    if constexpr (kPaged) load_page(t + 1);
   };
+  if constexpr (kPaged) {
+    if (t0 < t1) load_page(t0);
+  }
 
-  // This lane's query row (column n of S^T) and its Q fragments (B operand).
+  // This lane's query row (column n of S^T), its position, and its Q
+  // fragments (B operand).
   const int qrow = q0 + 32 * w + l32;
+  const int qpos = qoff + qrow;
   bf16x8 qf[4];
   {
     const int qcl = min(qrow, L - 1);
@@ -98,7 +141,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
   wait_vmem_all();  // fragments resident before the loop (see wait_vmem_all)
   issue_fence();
-  prefetch(t0, 0);
+  if (t0 < t1) prefetch(t0, 0);
   issue_fence();
 
   // Online softmax state in the log2 domain, seeded with the sink.
@@ -109,7 +152,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) { o[0][i] = 0.0f; o[1][i] = 0.0f; }
 
-  const int wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
+  const int wq_lo = qoff + q0 + 32 * w, wq_hi = wq_lo + 31;  // positions of this wavefront's rows
   const float sl2 = a.scale_log2;
   const int krow_base = row_perm(l32);
 
@@ -149,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       // key index 32*blk + 16*(r/8) + r%8 (+ kb + 8*h2) is visible iff lo <= idx < hi;
       // hidden raw scores become -inf (the scale is positive, so they stay
       // -inf through the scaling below).
-      const int hi = qrow + 1 - kb - 8 * h2;
+      const int hi = qpos + 1 - kb - 8 * h2;
       const int lo = window > 0 ? hi - window : -0x7fffffff;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
@@ -170,10 +213,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     }
     float mx = __builtin_fmaxf(mx0, mx1);
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-    // Raise the reference max (and rescale the accumulator) only when some
-    // row of the wavefront outgrew it by more than the slack.
-    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
-      const float mnew = fmaxf(m, mx);
+    // Raise a row's reference max (and rescale its accumulator) only when the
+    // row outgrew it by more than the slack; the rescale pass runs when any
+    // row of the wavefront needs it (alpha is exactly 1 for the others), so
+    // every row's result depends on that row's scores alone.
+    const bool raise = mx > m + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float mnew = raise ? fmaxf(m, mx) : m;
       const float alpha = fast_exp2(m - ((mnew == -__builtin_inff()) ? 0.0f : mnew));
       l *= alpha;
 #pragma unroll
@@ -231,12 +277,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t stream) {
   const dim3 grid((max_seqlen + kBM - 1) / kBM * a.num_q_heads * num_seqs);
-  if (dtype == 0 && a.head_dim == kD)
-    hipLaunchKernelGGL((fwd_kernel<bf16, true>), grid, dim3(256), 0, stream, a);
-  else if (dtype == 0)
-    hipLaunchKernelGGL((fwd_kernel<bf16, false>), grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((fwd_kernel<float, false>), grid, dim3(256), 0, stream, a);
+  const bool direct = dtype == 0 && a.head_dim == kD;
+  if (a.block_table) {
+    if (direct)
+      hipLaunchKernelGGL((fwd_kernel<bf16, true, true>), grid, dim3(256), 0, stream, a);
+    else if (dtype == 0)
+      hipLaunchKernelGGL((fwd_kernel<bf16, false, true>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((fwd_kernel<float, false, true>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (direct)
+      hipLaunchKernelGGL((fwd_kernel<bf16, true, false>), grid, dim3(256), 0, stream, a);
+    else if (dtype == 0)
+      hipLaunchKernelGGL((fwd_kernel<bf16, false, false>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((fwd_kernel<float, false, false>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -120,6 +120,45 @@ int sink_attn_fwd(const sink_attn_params *p, const void *q, const void *k, const
                   const float *sinks, void *o, float *lse, void *stream);
 
 /*
+ * Paged key/value cache (inference).  Key j of sequence s lives at row
+ * j % page_size of page block_table[s][j / page_size] of k_cache (value: same
+ * place in v_cache).  The keys and values of the new tokens must already be
+ * in the cache.
+ */
+typedef struct {
+  const void *k_cache;        /* device, [num_pages, page_size, num_kv_heads, head_dim], params.dtype */
+  const void *v_cache;        /* device, same shape and type */
+  const int32_t *block_table; /* device, [num_seqs, max_blocks_per_seq] page ids; entries past a
+                                 sequence's length are not read */
+  const int32_t *kv_lens;     /* device, [num_seqs]: keys per sequence, cached and new,
+                                 q_len <= kv_len <= max_blocks_per_seq * page_size */
+  int32_t num_pages;          /* >= 1 */
+  int32_t page_size;          /* a positive multiple of 64 */
+  int32_t max_blocks_per_seq; /* row length of block_table, >= 1 */
+} sink_attn_paged_kv;
+
+/*
+ * Forward pass over a paged KV cache: prefill of new tokens, or decode (one
+ * new token per sequence).  params.cu_seqlens, total_tokens and max_seqlen
+ * describe the NEW query tokens (q, o, lse as in sink_attn_fwd); the q_len
+ * new tokens of sequence s are its last positions kv_len - q_len .. kv_len - 1,
+ * and each sees the cached and new keys at or before its position (and in
+ * the window).  Results are bit-identical to sink_attn_fwd's rows for the
+ * same positions of the whole sequence: both run the same per-row code.
+ * The device arrays are not read by the host (SINK_ATTN_VALIDATE=1 checks
+ * them and synchronises); an out-of-range page id or length is clamped into
+ * the cache instead of faulting.  Same errors and stream rules as
+ * sink_attn_fwd.
+ * Reference: "GPT-OSS Agentic RL Training: A Practical Retrospective",
+ * sections "Correcting Training-Inference Mismatch via Attention Sinks" (the
+ * inference engine and the training stack must give the same token
+ * probabilities) and "The Role of Attention Sinks" (sinks also serve
+ * streaming inference).
+ */
+int sink_attn_fwd_paged(const sink_attn_params *p, const sink_attn_paged_kv *kv, const void *q,
+                        const float *sinks, void *o, float *lse, void *stream);
+
+/*
  * Bytes of device workspace sink_attn_bwd needs for these parameters
  * (float row statistics, float dK/dV partial sums of the head groups and
  * per-query-tile dS partials, 256-byte aligned sections; the last depends on

@@ -13,6 +13,12 @@ Pins (all in tests/test_oracle_pins.py, CPU only):
                         (varlen packing, GQA == repeated MHA, window >= L).
   forward_rows, backward_rows, backward_keys
                      -> equal to the corresponding entries of forward/backward.
+  gather_paged, forward_paged
+                     -> a paged cache holding whole sequences with q_len ==
+                        kv_len equals forward; new tokens at the end of a
+                        cached context equal the last rows of forward over the
+                        whole sequence; page order does not matter; a length-1
+                        context gives the one-key closed form.
 No function here is "parity unpinned".
 """
 from .sink_attention import (  # noqa: F401
@@ -20,7 +26,9 @@ from .sink_attention import (  # noqa: F401
     backward_keys,
     backward_rows,
     forward,
+    forward_paged,
     forward_rows,
+    gather_paged,
     kv_head_of,
     visible_key_range,
 )

@@ -139,6 +139,47 @@ def forward_rows(q, k, v, sinks, cu_seqlens, scale, window, seq, head, rows):
     return o, lse
 
 
+def gather_paged(cache, block_table, kv_len, seq):
+    """Keys (or values) 0 .. kv_len-1 of one sequence from a paged cache
+    [num_pages, page_size, H, d]: key j is row j % page_size of page
+    block_table[seq, j // page_size]."""
+    cache = _f64(cache)
+    bt = _i64(block_table)
+    ps = cache.shape[1]
+    j = np.arange(int(kv_len))
+    return cache[bt[seq, j // ps], j % ps]  # [kv_len, H, d]
+
+
+def forward_paged(q, k_cache, v_cache, block_table, kv_lens, sinks, cu_seqlens, scale, window=0):
+    """O [T, Hq, d] and LSE [Hq, T] (float64) of new query tokens over a paged
+    KV cache.  The q_len new tokens of sequence s sit at its last positions
+    kv_len - q_len .. kv_len - 1; each row is the definition above evaluated
+    at its position, over the sequence's gathered keys and values."""
+    q, sinks = _f64(q), _f64(sinks)
+    cu, lens = _i64(cu_seqlens), _i64(kv_lens)
+    T, hq, d = q.shape
+    hkv = k_cache.shape[2]
+    o = np.zeros((T, hq, d))
+    lse = np.full((hq, T), np.nan)
+    for s in range(len(cu) - 1):
+        b, e = int(cu[s]), int(cu[s + 1])
+        qlen, kvlen = e - b, int(lens[s])
+        if qlen == 0:
+            continue
+        off = kvlen - qlen
+        ks, vs = gather_paged(k_cache, block_table, kvlen, s), gather_paged(v_cache, block_table, kvlen, s)
+        rows = off + np.arange(qlen)
+        for h in range(hq):
+            g = kv_head_of(h, hq, hkv)
+            qfull = np.zeros((kvlen, d))
+            qfull[off:] = q[b:e, h]  # queries at their positions; earlier rows are not asked for
+            p, _, l, klo = _row_probabilities(qfull, np.ascontiguousarray(ks[:, g]), sinks[h], rows, scale,
+                                              window)
+            o[b:e, h] = p @ vs[klo:klo + p.shape[1], g]
+            lse[h, b:e] = l
+    return o, lse
+
+
 def backward(q, k, v, sinks, dout, cu_seqlens, scale, window=0, kv_heads=None,
              row_block=256):
     """dQ [T,Hq,d], dK [T,Hkv,d], dV [T,Hkv,d], dS [Hq] (float64).

@@ -12,6 +12,10 @@ unless given):
 Tensors of a bf16 workload are rounded to bf16 (round to nearest even) on
 the host with torch; both the GPU and the oracle consume exactly those
 values.  The sinks always stay float32.
+
+``make_paged`` re-lays the keys and values of such an input into a paged
+cache (pages in a seeded random order, unused slots filled with NaN) and
+takes the last rows of each sequence's queries as its new tokens.
 """
 from __future__ import annotations
 
@@ -114,3 +118,48 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tens
     out["sinks"] = torch.from_numpy(rng.standard_normal((hq,), dtype=np.float32))
     out["cu_seqlens"] = torch.from_numpy(w.cu_seqlens())
     return out
+
+
+def make_paged(inputs: Dict[str, torch.Tensor], q_lens: Sequence[int], page_size: int, seed: int,
+               spare_pages: int = 3, max_blocks_extra: int = 1) -> Dict[str, torch.Tensor]:
+    """Paged-cache view of packed ``inputs`` (from ``make_inputs``).
+
+    Sequence s keeps all its L_s keys and values (kv_lens = L_s); its new
+    tokens are its last q_lens[s] query rows.  Pages go to the sequences in
+    the order of ``default_rng(seed).permutation``; slots no sequence uses,
+    and block-table entries past a sequence's pages (-1), must never be
+    read.  Returns q, k_cache, v_cache, block_table, kv_lens, cu_seqlens
+    (of the new tokens), rows (their indices in the packed layout) and
+    sinks.
+    """
+    cu = inputs["cu_seqlens"].numpy().astype(np.int64)
+    lens = np.diff(cu)
+    k, v = inputs["k"], inputs["v"]
+    hkv, d = k.shape[1], k.shape[2]
+    blocks = [(int(L) + page_size - 1) // page_size for L in lens]
+    num_pages = sum(blocks) + spare_pages
+    perm = np.random.default_rng(seed).permutation(num_pages)
+    k_cache = torch.full((num_pages, page_size, hkv, d), float("nan"), dtype=k.dtype)
+    v_cache = torch.full_like(k_cache, float("nan"))
+    max_blocks = max(blocks + [1]) + max_blocks_extra
+    bt = torch.full((len(lens), max_blocks), -1, dtype=torch.int32)
+    nxt = 0
+    rows = []
+    for s, L in enumerate(lens):
+        b0 = int(cu[s])
+        for b in range(blocks[s]):
+            page = int(perm[nxt])
+            nxt += 1
+            n = min(page_size, int(L) - b * page_size)
+            k_cache[page, :n] = k[b0 + b * page_size:b0 + b * page_size + n]
+            v_cache[page, :n] = v[b0 + b * page_size:b0 + b * page_size + n]
+            bt[s, b] = page
+        ql = int(q_lens[s])
+        assert 0 <= ql <= L
+        rows.extend(range(b0 + int(L) - ql, b0 + int(L)))
+    rows_t = torch.tensor(rows, dtype=torch.int64)
+    cu_q = np.zeros(len(lens) + 1, dtype=np.int32)
+    cu_q[1:] = np.cumsum(np.asarray(q_lens, dtype=np.int64))
+    return {"q": inputs["q"][rows_t], "k_cache": k_cache, "v_cache": v_cache, "block_table": bt,
+            "kv_lens": torch.from_numpy(lens.astype(np.int32)), "cu_seqlens": torch.from_numpy(cu_q),
+            "rows": rows_t, "sinks": inputs["sinks"]}

@@ -188,3 +188,53 @@ def test_set_bwd_events_accepts_partial_and_null():
         assert lib.sink_attn_set_bwd_events((ctypes.c_void_p * 4)()) == _lib.SINK_ATTN_OK
     finally:
         assert lib.sink_attn_set_bwd_events(None) == _lib.SINK_ATTN_OK
+
+
+def _paged_kv(**override):
+    kv = _lib.SinkAttnPagedKV()
+    vals = dict(k_cache=FAKE, v_cache=FAKE, block_table=FAKE, kv_lens=FAKE, num_pages=4,
+                page_size=64, max_blocks_per_seq=2)
+    vals.update(override)
+    for name, val in vals.items():
+        setattr(kv, name, val)
+    return kv
+
+
+def _fwd_paged(p, kv, **override):
+    lib = _lib.load()
+    args = dict(q=FAKE, sinks=FAKE, o=FAKE, lse=FAKE)
+    args.update(override)
+    kvp = ctypes.byref(kv) if kv is not None else None
+    return lib.sink_attn_fwd_paged(ctypes.byref(p), kvp, args["q"], args["sinks"], args["o"],
+                                   args["lse"], None)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("page_size", 0), ("page_size", 32), ("page_size", 96), ("num_pages", 0),
+    ("max_blocks_per_seq", 0), ("k_cache", None), ("v_cache", None), ("block_table", None),
+    ("kv_lens", None), ("k_cache", FAKE + 4),
+])
+def test_paged_forward_rejects_bad_cache_description(field, value):
+    p = _good_params()
+    assert _fwd_paged(p, _paged_kv(**{field: value})) == _lib.SINK_ATTN_ERR_INVALID_ARG
+    assert _lib.load().sink_attn_last_error().decode() != ""
+
+
+def test_paged_forward_rejects_null_kv_and_tensors():
+    p = _good_params()
+    assert _fwd_paged(p, None) == _lib.SINK_ATTN_ERR_INVALID_ARG
+    for name in ("q", "sinks", "o", "lse"):
+        assert _fwd_paged(p, _paged_kv(), **{name: None}) == _lib.SINK_ATTN_ERR_INVALID_ARG
+
+
+def test_paged_forward_rejects_oversized_block_table_span():
+    p = _good_params()
+    kv = _paged_kv(page_size=1 << 20, max_blocks_per_seq=1 << 12)
+    assert _fwd_paged(p, kv) == _lib.SINK_ATTN_ERR_UNSUPPORTED
+
+
+def test_paged_forward_with_no_new_tokens_is_a_no_op():
+    p = _good_params(T=0)
+    p.max_seqlen = 0
+    assert _fwd_paged(p, _paged_kv(k_cache=None, v_cache=None), q=None, o=None, lse=None,
+                      sinks=None) == _lib.SINK_ATTN_OK

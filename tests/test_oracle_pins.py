@@ -405,3 +405,58 @@ def test_planted_sign_flip_in_sink_gradient_is_caught(monkeypatch):
                  - np.sum(oracle.forward(q, k, v, sm, cu, 0.6)[0] * do)) / (2 * h)
     assert np.max(np.abs(fd - ds)) > 1e-3
     assert np.max(np.abs(fd - orig_backward(q, k, v, s, do, cu, 0.6)[3])) < 1e-8
+
+
+# ---- paged-cache forward (new tokens at the end of a cached context) ----
+
+from synthetic.workloads import custom_workload, make_inputs, make_paged  # noqa: E402
+
+
+@pytest.mark.parametrize("lengths,q_lens,page_size,window", [
+    ((70, 5, 129), (70, 5, 129), 64, 0),     # whole sequences: the plain forward
+    ((70, 5, 129), (1, 5, 40), 64, 0),       # decode, whole, prefill of 40
+    ((200, 90), (17, 1), 128, 33),           # window, other page size
+])
+def test_paged_forward_equals_forward_rows(lengths, q_lens, page_size, window):
+    w = custom_workload(lengths, 4, 2, 16, window, "f32")
+    inp = make_inputs(w, seed=11)
+    pg = make_paged(inp, q_lens, page_size, seed=3)
+    o_ref, lse_ref = osa.forward(inp["q"], inp["k"], inp["v"], inp["sinks"], inp["cu_seqlens"],
+                                 w.softmax_scale, window)
+    o, lse = osa.forward_paged(pg["q"], pg["k_cache"], pg["v_cache"], pg["block_table"],
+                               pg["kv_lens"], pg["sinks"], pg["cu_seqlens"], w.softmax_scale, window)
+    rows = pg["rows"].numpy()
+    assert np.abs(o - o_ref[rows]).max() < 1e-12
+    assert np.abs(lse - lse_ref[:, rows]).max() < 1e-12
+
+
+def test_paged_gather_follows_the_block_table():
+    w = custom_workload((130, 64), 2, 1, 8, 0, "f32")
+    inp = make_inputs(w, seed=2)
+    a = make_paged(inp, (130, 64), 64, seed=1)
+    b = make_paged(inp, (130, 64), 64, seed=9)  # other page order, same sequences
+    assert not torch.equal(a["block_table"], b["block_table"])
+    for s, (b0, L) in enumerate(((0, 130), (130, 64))):
+        ga = osa.gather_paged(a["k_cache"], a["block_table"], L, s)
+        gb = osa.gather_paged(b["v_cache"], b["block_table"], L, s)
+        assert np.array_equal(ga, inp["k"][b0:b0 + L].double().numpy())
+        assert np.array_equal(gb, inp["v"][b0:b0 + L].double().numpy())
+
+
+def test_paged_single_key_closed_form():
+    # kv_len = q_len = 1: O = sigmoid(x - S) v0, LSE = logaddexp(S, x), x = tau q.k
+    q = torch.tensor([[[0.5, -1.0, 2.0, 0.25]]])
+    k_cache = torch.full((2, 64, 1, 4), float("nan"))
+    v_cache = torch.full((2, 64, 1, 4), float("nan"))
+    k_cache[1, 0, 0] = torch.tensor([1.0, 0.5, -0.5, 2.0])
+    v_cache[1, 0, 0] = torch.tensor([3.0, -2.0, 1.0, 0.5])
+    bt = torch.tensor([[1, -1]], dtype=torch.int32)
+    sinks = torch.tensor([0.3])
+    tau = 0.5
+    o, lse = osa.forward_paged(q, k_cache, v_cache, bt, torch.tensor([1], dtype=torch.int32), sinks,
+                               torch.tensor([0, 1], dtype=torch.int32), tau, 0)
+    x = tau * float(q[0, 0].double() @ k_cache[1, 0, 0].double())
+    sv = float(sinks[0])  # the float32 value the oracle receives
+    p = 1.0 / (1.0 + math.exp(sv - x))
+    assert np.allclose(o[0, 0], p * v_cache[1, 0, 0].double().numpy(), atol=1e-15)
+    assert abs(lse[0, 0] - np.logaddexp(sv, x)) < 1e-15
