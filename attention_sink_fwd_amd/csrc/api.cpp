@@ -54,8 +54,8 @@ int check_params(const sink_attn_params* p) {
     return fail(SINK_ATTN_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   // The tiled kernels run one workgroup of 256 lanes per (128-row tile,
   // query head, sequence); the dispatch's lane count must fit 32 bits.
-  if (((int64_t)p->max_seqlen + 127) / 128 * p->num_q_heads * p->num_seqs >= (int64_t)1 << 24)
-    return fail(SINK_ATTN_ERR_UNSUPPORTED, "ceil(max_seqlen / 128) * num_q_heads * num_seqs must stay below 2^24");
+  if ((((int64_t)p->max_seqlen + 127) / 128 + 1) * p->num_q_heads * p->num_seqs >= (int64_t)1 << 24)
+    return fail(SINK_ATTN_ERR_UNSUPPORTED, "(ceil(max_seqlen / 128) + 1) * num_q_heads * num_seqs must stay below 2^24");
   if (p->causal != 1) return fail(SINK_ATTN_ERR_UNSUPPORTED, "only causal attention is built (causal must be 1)");
   if (p->window < 0) return fail(SINK_ATTN_ERR_INVALID_ARG, "window must be >= 0 (got %d)", p->window);
   if (p->dtype != SINK_ATTN_BF16 && p->dtype != SINK_ATTN_F32)
@@ -97,6 +97,28 @@ int maybe_validate_cu(const sink_attn_params* p, hipStream_t stream) {
     if (_st != SINK_ATTN_OK) return _st; \
   } while (0)
 
+
+// Query heads packed per forward workgroup: SINK_ATTN_FWD_HEADS if set (a
+// divisor of Hq/Hkv and of 32), else the largest power of two up to
+// `preferred` that divides Hq/Hkv (all heads of a KV group share each K/V
+// tile the workgroup loads).
+int resolve_fwd_heads(const sink_attn_params* p, int preferred, int* out) {
+  const int grp = p->num_q_heads / p->num_kv_heads;
+  if (const char* env = std::getenv("SINK_ATTN_FWD_HEADS")) {
+    const int hp = std::atoi(env);
+    if (hp < 1 || grp % hp != 0 || 32 % hp != 0)
+      return fail(SINK_ATTN_ERR_INVALID_ARG, "SINK_ATTN_FWD_HEADS=%s must divide 32 and num_q_heads / num_kv_heads = %d",
+                  env, grp);
+    *out = hp;
+    return SINK_ATTN_OK;
+  }
+  int hp = 1;
+  for (int c = 2; c <= preferred && c <= 32; c *= 2)
+    if (grp % c == 0) hp = c;
+  *out = hp;
+  return SINK_ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -121,6 +143,7 @@ int sink_attn_fwd(const sink_attn_params* p, const void* q, const void* k, const
   a.num_q_heads = p->num_q_heads; a.num_kv_heads = p->num_kv_heads; a.head_dim = p->head_dim;
   a.total_tokens = p->total_tokens; a.window = p->window; a.num_seqs = p->num_seqs;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  SA_CHECK(resolve_fwd_heads(p, 32, &a.heads_per_tile));
   hipError_t e = sinkattn::launch_fwd(a, p->dtype, p->max_seqlen, p->num_seqs, s);
   if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   return SINK_ATTN_OK;
@@ -185,6 +208,7 @@ int sink_attn_fwd_paged(const sink_attn_params* p, const sink_attn_paged_kv* kv,
   a.num_q_heads = p->num_q_heads; a.num_kv_heads = p->num_kv_heads; a.head_dim = p->head_dim;
   a.total_tokens = p->total_tokens; a.window = p->window; a.num_seqs = p->num_seqs;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  SA_CHECK(resolve_fwd_heads(p, 32, &a.heads_per_tile));
   a.block_table = kv->block_table; a.kv_lens = kv->kv_lens;
   a.page_size = kv->page_size; a.max_blocks_per_seq = kv->max_blocks_per_seq; a.num_pages = kv->num_pages;
   hipError_t e = sinkattn::launch_fwd(a, p->dtype, p->max_seqlen, p->num_seqs, s);

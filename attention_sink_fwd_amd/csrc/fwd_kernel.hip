@@ -5,14 +5,16 @@
 // the softmax as a virtual token without a value) and "Implementation in
 // FlashAttention v3" (a fused forward pass that carries the sink).
 //
-// One workgroup = one query head h, one sequence, a tile of 128 query rows;
-// four wavefronts own 32 rows each.  Keys/values of head g(h) stream through
-// a two-stage LDS ring in tiles of 64 keys (direct global->LDS loads into
-// XOR-swizzled rows, issued one tile ahead; one barrier per tile; the small
-// ring leaves room for four workgroups per compute unit).  Per tile
-// a wavefront computes the transposed score block S^T = K Q^T on the matrix
-// cores, so each lane owns one query row and its softmax statistics stay in
-// the lane; the online softmax starts from the sink (reference max m = S_h,
+// One workgroup = one sequence and 128 columns of (query row, query head):
+// hp heads of one KV group g times 128/hp consecutive rows (hp = 1: 128 rows
+// of one head); four wavefronts own 32 columns each.  Keys/values of g stream
+// through a two-stage LDS ring in tiles of 64 keys (direct global->LDS loads
+// into XOR-swizzled rows, issued one tile ahead; one barrier per tile; the
+// small ring leaves room for four workgroups per compute unit), each tile
+// loaded once for all hp heads.  Per tile a wavefront computes the
+// transposed score block S^T = K Q^T on the matrix cores, so each lane owns
+// one (row, head) column and its softmax statistics stay in the lane; the
+// online softmax starts from the sink (reference max m = S_h,
 // running sum l = 1), which is how the virtual token enters without a value
 // vector.  P^T (bf16) feeds O^T += V^T P^T straight from registers; V^T comes
 // from the row-major V tile through transposing LDS reads.  The epilogue
@@ -56,19 +58,24 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int h2 = lane >> 5, l32 = lane & 31;
-  const TileUnit unit = xcd_unit(a.num_q_heads, a.num_seqs);
-  const int seq = unit.seq, hq = unit.head;
-  const int ntiles = (int)gridDim.x / (a.num_q_heads * a.num_seqs);
+  // Column n = 32 w + l32 of the workgroup's score tiles is query row
+  // q0 + n / hp of head hb * hp + n % hp: hp query heads of one KV group
+  // share the workgroup's K/V tiles (hp = 1: 128 rows of one head).
+  const int hp = a.heads_per_tile, rows = kBM / hp;
+  const TileUnit unit = xcd_unit(a.num_q_heads / hp, a.num_seqs);
+  const int seq = unit.seq, hb = unit.head;
+  const int ntiles = (int)gridDim.x / (a.num_q_heads / hp * a.num_seqs);
   const int qt = ntiles - 1 - unit.rank;  // heaviest (last) query tiles first
   const int bos = a.cu_seqlens[seq];
   const int L = a.cu_seqlens[seq + 1] - bos;  // query rows of this sequence
-  const int q0 = qt * kBM;
+  const int q0 = qt * rows;
   if (q0 >= L) return;
 
   const int hd = kDirect ? kD : a.head_dim;  // the direct path is only built for head_dim == kD
-  const int g = hq / (a.num_q_heads / a.num_kv_heads);
+  const int g = hb * hp / (a.num_q_heads / a.num_kv_heads);
   const int qs = a.num_q_heads * hd, ks = a.num_kv_heads * hd;  // row strides (< 2^31 elements)
-  const TIn* __restrict__ Qh = (const TIn*)a.q + (long)bos * qs + hq * hd;
+  const int col = 32 * w + l32;
+  const int hq = hb * hp + col % hp;  // this lane's query head
 
   // Keys of this sequence and the position of query row 0.  A paged
   // sequence's length is clamped to what its block-table row can address.
@@ -84,7 +91,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const TIn* __restrict__ Vg = (const TIn*)a.v + (kPaged ? 0L : (long)bos * ks) + g * hd;
 
   const int window = a.window;
-  const int kend = min(kvlen, qoff + min(L, q0 + kBM));
+  const int kend = min(kvlen, qoff + min(L, q0 + rows));
   const int kbeg = window > 0 ? max(0, qoff + q0 - window + 1) : 0;
   const int t0 = kbeg / kBN, t1 = (kend + kBN - 1) / kBN;  // t0 < t1 unless a paged length was bad
 
@@ -128,8 +135,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
   // This lane's query row (column n of S^T), its position, and its Q
   // fragments (B operand).
-  const int qrow = q0 + 32 * w + l32;
+  const int qrow = q0 + col / hp;
   const int qpos = qoff + qrow;
+  const TIn* __restrict__ Qh = (const TIn*)a.q + (long)bos * qs + hq * hd;
   bf16x8 qf[4];
   {
     const int qcl = min(qrow, L - 1);
@@ -152,7 +160,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) { o[0][i] = 0.0f; o[1][i] = 0.0f; }
 
-  const int wq_lo = qoff + q0 + 32 * w, wq_hi = wq_lo + 31;  // positions of this wavefront's rows
+  // Positions of this wavefront's first and last rows; a wavefront whose
+  // rows all lie past the sequence only takes part in the loads.
+  const int wq_lo = qoff + q0 + 32 * w / hp, wq_hi = qoff + q0 + (32 * w + 31) / hp;
+  const bool live = q0 + 32 * w / hp < L;
   const float sl2 = a.scale_log2;
   const int krow_base = row_perm(l32);
 
@@ -172,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     const KVStage& st = stage[buf];
     if (++buf == kStages) buf = 0;
     const int kb = t * kBN;
-    if (kb > wq_hi) continue;                                      // all keys after all rows
+    if (!live || kb > wq_hi) continue;                             // no rows, or all keys after all rows
     if (window > 0 && wq_lo - (kb + kBN - 1) >= window) continue;  // all keys left of window
 
     // S^T = K Q^T for two 32-key blocks; register r of block blk holds key
@@ -276,7 +287,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t stream) {
-  const dim3 grid((max_seqlen + kBM - 1) / kBM * a.num_q_heads * num_seqs);
+  const int hp = a.heads_per_tile, rows = kBM / hp;
+  const dim3 grid((max_seqlen + rows - 1) / rows * (a.num_q_heads / hp) * num_seqs);
   const bool direct = dtype == 0 && a.head_dim == kD;
   if (a.block_table) {
     if (direct)

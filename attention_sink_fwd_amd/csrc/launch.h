@@ -15,7 +15,8 @@ struct FwdArgs {
   float* lse;
   const int32_t* cu_seqlens;
   int num_q_heads, num_kv_heads, head_dim, total_tokens, window, num_seqs;
-  float scale_log2;  // softmax_scale * log2(e)
+  int heads_per_tile;  // query heads of one KV head packed in a workgroup (divides Hq/Hkv and 32)
+  float scale_log2;    // softmax_scale * log2(e)
   // Paged key/value source (block_table == nullptr: k, v are packed like q).
   // k, v then point at the caches [num_pages, page_size, Hkv, d].
   const int32_t* block_table;  // [num_seqs, max_blocks_per_seq]

@@ -135,6 +135,75 @@ def calibrate_copy(nbytes=1 << 30):
                       "bytes_written_per_launch": nbytes, "launches": 3}), flush=True)
 
 
+def paged_decode(args):
+    """One decode step over a paged KV cache: 64 sequences with 4096 cached
+    keys each (64-key pages in a seeded random order), one new token per
+    sequence, GPT-OSS attention shape.  Reports the rate at which the step
+    reads the cache (each sequence's keys and values once per KV head)
+    against the HBM peak.  Inputs are synthetic (seeded normal values)."""
+    import torch
+
+    import attention_sink_fwd_amd as sa
+
+    nseq, ctx, hq, hkv, d, ps = 64, 4096, 64, 8, 64, 64
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    pages = nseq * ctx // ps
+    k_cache = torch.randn((pages, ps, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+    v_cache = torch.randn((pages, ps, hkv, d), generator=gen, device=dev).to(torch.bfloat16)
+    perm = torch.randperm(pages, generator=gen, device=dev).to(torch.int32)
+    block_table = perm.view(nseq, ctx // ps).contiguous()
+    kv_lens = torch.full((nseq,), ctx, dtype=torch.int32, device=dev)
+    q = torch.randn((nseq, hq, d), generator=gen, device=dev).to(torch.bfloat16)
+    sinks = torch.randn((hq,), generator=gen, device=dev)
+    cu = torch.arange(nseq + 1, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((hq, nseq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    hip = Hip()
+
+    def step():
+        sa.sink_attn_fwd_paged(q, k_cache, v_cache, block_table, kv_lens, sinks, cu, 1, None, 0,
+                               o=o, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(hip.event(), hip.event()) for _ in range(K)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        hip.record(a, sh)
+        step()
+        hip.record(b, sh)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = sum(hip.ms(a, b) for a, b in evs) / K
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    kv_bytes = 2.0 * nseq * ctx * hkv * d * 2  # K and V, bf16, read once per KV head
+    io_bytes = 2.0 * nseq * hq * d * 2 + nseq * hq * 4 + kv_bytes
+    ms = (t1 - t0) * 1000.0 / K
+    gbs = io_bytes / (kern_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "sink-attn paged decode step, KV-cache read GB/s (64 seqs x 4096 ctx, Hq64/Hkv8/d64)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "paged_decode_b64_ctx4096_hq64_hkv8_d64_page64", "num_seqs": nseq,
+                   "context": ctx, "page_size": ps, "new_tokens_per_seq": 1},
+        "tokens_per_s": round(nseq / (kern_ms * 1e-3), 1),
+        "roofline": {"kernel": "fwd_paged", "kernel_ms": round(kern_ms, 5), "bound": "hbm",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": io_bytes,
+                     "traffic": traffic_for_current_kernel("fwd_paged")},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +211,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2, help="workload id 1-5 (default 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--paged-decode", action="store_true",
+                    help="time one decode step over a paged KV cache instead (own JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a known-size copy kernel (for rocprofv3 counter scaling)")
     args = ap.parse_args()
@@ -154,6 +225,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.paged_decode:
+        paged_decode(args)
         return
 
     import torch

@@ -238,3 +238,12 @@ def test_paged_forward_with_no_new_tokens_is_a_no_op():
     p.max_seqlen = 0
     assert _fwd_paged(p, _paged_kv(k_cache=None, v_cache=None), q=None, o=None, lse=None,
                       sinks=None) == _lib.SINK_ATTN_OK
+
+
+@pytest.mark.parametrize("value", ["0", "3", "64", "x"])
+def test_bad_fwd_heads_override_is_rejected(monkeypatch, value):
+    monkeypatch.setenv("SINK_ATTN_FWD_HEADS", value)
+    p = _good_params()  # Hq/Hkv = 4
+    assert _fwd(p) == _lib.SINK_ATTN_ERR_INVALID_ARG
+    assert "SINK_ATTN_FWD_HEADS" in _lib.load().sink_attn_last_error().decode()
+    assert _fwd_paged(p, _paged_kv()) == _lib.SINK_ATTN_ERR_INVALID_ARG

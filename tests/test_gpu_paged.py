@@ -53,12 +53,18 @@ def test_paged_forward_matches_oracle(lengths, q_lens, hq, hkv, d, window, dtype
     assert eo <= TOL_O and el <= TOL_LSE
 
 
+@pytest.mark.parametrize("fwd_heads", [None, 1, 2])
 @pytest.mark.parametrize("lengths,q_lens,hq,hkv,d,window,dtype,ps", CASES)
-def test_paged_forward_is_bit_identical_to_training_rows(lengths, q_lens, hq, hkv, d, window, dtype,
-                                                         ps):
+def test_paged_forward_is_bit_identical_to_training_rows(monkeypatch, fwd_heads, lengths, q_lens,
+                                                         hq, hkv, d, window, dtype, ps):
     import attention_sink_fwd_amd as sa
 
-    say("case bits", lengths, q_lens, d, window, dtype, ps)
+    if fwd_heads is not None:
+        if (hq // hkv) % fwd_heads:
+            pytest.skip("head count does not divide the group")
+        # the same packing for both calls; None: each call's own default
+        monkeypatch.setenv("SINK_ATTN_FWD_HEADS", str(fwd_heads))
+    say("case bits", lengths, q_lens, d, window, dtype, ps, "fwd_heads", fwd_heads)
     w = custom_workload(lengths, hq, hkv, d, window, dtype)
     inp = make_inputs(w, seed=sum(lengths) + 3 * d)
     dev = {k: v.to("cuda:0") for k, v in inp.items()}

@@ -161,6 +161,34 @@ def test_backward_is_bitwise_reproducible(monkeypatch, heads, window):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("lengths,hq,hkv,window,dtype", [
+    ((300, 5, 190), 8, 2, 0, "bf16"),
+    ((333, 129), 8, 1, 128, "bf16"),
+    ((200, 70), 4, 2, 9, "f32"),
+])
+def test_forward_head_packing_keeps_every_bit(monkeypatch, lengths, hq, hkv, window, dtype):
+    """Rows computed with several query heads per workgroup equal the rows
+    computed one head per workgroup, bit for bit, and match the oracle."""
+    import attention_sink_fwd_amd as sa
+
+    w = custom_workload(lengths, hq, hkv, 64 if dtype == "bf16" else 40, window, dtype)
+    inp = make_inputs(w, seed=41)
+    d = {k: v.to("cuda:0") for k, v in inp.items()}
+    outs = []
+    for hp in (1, 2, hq // hkv):
+        monkeypatch.setenv("SINK_ATTN_FWD_HEADS", str(hp))
+        say("case head packing", lengths, "heads per workgroup", hp)
+        outs.append(sa.sink_attn_fwd(d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens"],
+                                     w.max_seqlen, w.softmax_scale, window))
+    torch.cuda.synchronize()
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
+    o_ref, lse_ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["sinks"], inp["cu_seqlens"],
+                                    w.softmax_scale, window)
+    assert max_abs(outs[-1][0].double().cpu().numpy(), o_ref) <= TOL_O
+    assert max_abs(outs[-1][1].double().cpu().numpy(), lse_ref) <= TOL_LSE
+
+
 def test_empty_batch_zeroes_dsinks():
     import attention_sink_fwd_amd as sa
     dev = "cuda:0"
