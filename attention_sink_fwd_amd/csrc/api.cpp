@@ -98,16 +98,16 @@ int maybe_validate_cu(const sink_attn_params* p, hipStream_t stream) {
   } while (0)
 
 
-// Query heads packed per forward workgroup: SINK_ATTN_FWD_HEADS if set (a
+// Query heads packed per forward or dQ workgroup: SINK_ATTN_PACK_HEADS if set (a
 // divisor of Hq/Hkv and of 32), else the largest power of two up to
 // `preferred` that divides Hq/Hkv (all heads of a KV group share each K/V
 // tile the workgroup loads).
-int resolve_fwd_heads(const sink_attn_params* p, int preferred, int* out) {
+int resolve_pack_heads(const sink_attn_params* p, int preferred, int* out) {
   const int grp = p->num_q_heads / p->num_kv_heads;
-  if (const char* env = std::getenv("SINK_ATTN_FWD_HEADS")) {
+  if (const char* env = std::getenv("SINK_ATTN_PACK_HEADS")) {
     const int hp = std::atoi(env);
     if (hp < 1 || grp % hp != 0 || 32 % hp != 0)
-      return fail(SINK_ATTN_ERR_INVALID_ARG, "SINK_ATTN_FWD_HEADS=%s must divide 32 and num_q_heads / num_kv_heads = %d",
+      return fail(SINK_ATTN_ERR_INVALID_ARG, "SINK_ATTN_PACK_HEADS=%s must divide 32 and num_q_heads / num_kv_heads = %d",
                   env, grp);
     *out = hp;
     return SINK_ATTN_OK;
@@ -143,7 +143,7 @@ int sink_attn_fwd(const sink_attn_params* p, const void* q, const void* k, const
   a.num_q_heads = p->num_q_heads; a.num_kv_heads = p->num_kv_heads; a.head_dim = p->head_dim;
   a.total_tokens = p->total_tokens; a.window = p->window; a.num_seqs = p->num_seqs;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
-  SA_CHECK(resolve_fwd_heads(p, 32, &a.heads_per_tile));
+  SA_CHECK(resolve_pack_heads(p, 32, &a.heads_per_tile));
   hipError_t e = sinkattn::launch_fwd(a, p->dtype, p->max_seqlen, p->num_seqs, s);
   if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   return SINK_ATTN_OK;
@@ -208,7 +208,7 @@ int sink_attn_fwd_paged(const sink_attn_params* p, const sink_attn_paged_kv* kv,
   a.num_q_heads = p->num_q_heads; a.num_kv_heads = p->num_kv_heads; a.head_dim = p->head_dim;
   a.total_tokens = p->total_tokens; a.window = p->window; a.num_seqs = p->num_seqs;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
-  SA_CHECK(resolve_fwd_heads(p, 32, &a.heads_per_tile));
+  SA_CHECK(resolve_pack_heads(p, 32, &a.heads_per_tile));
   a.block_table = kv->block_table; a.kv_lens = kv->kv_lens;
   a.page_size = kv->page_size; a.max_blocks_per_seq = kv->max_blocks_per_seq; a.num_pages = kv->num_pages;
   hipError_t e = sinkattn::launch_fwd(a, p->dtype, p->max_seqlen, p->num_seqs, s);
@@ -235,17 +235,19 @@ int resolve_dkdv_heads(const sink_attn_params* p, int* out) {
   return SINK_ATTN_OK;
 }
 
-sinkattn::BwdWorkspace workspace_layout(const sink_attn_params* p, int dkdv_heads) {
+sinkattn::BwdWorkspace workspace_layout(const sink_attn_params* p, int dkdv_heads, int pack_heads) {
   return sinkattn::bwd_workspace_layout(p->total_tokens, p->num_q_heads, p->num_kv_heads, p->head_dim, p->max_seqlen,
-                                        p->num_seqs, dkdv_heads);
+                                        p->num_seqs, dkdv_heads, pack_heads);
 }
 
 }  // namespace
 
 size_t sink_attn_bwd_workspace_size(const sink_attn_params* p) {
-  int hg = 0;
-  if (check_params(p) != SINK_ATTN_OK || resolve_dkdv_heads(p, &hg) != SINK_ATTN_OK) return 0;
-  return workspace_layout(p, hg).total;
+  int hg = 0, hp = 0;
+  if (check_params(p) != SINK_ATTN_OK || resolve_dkdv_heads(p, &hg) != SINK_ATTN_OK ||
+      resolve_pack_heads(p, 32, &hp) != SINK_ATTN_OK)
+    return 0;
+  return workspace_layout(p, hg, hp).total;
 }
 
 int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const void* v, const float* sinks,
@@ -266,9 +268,10 @@ int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const
     if (!lse) return fail(SINK_ATTN_ERR_INVALID_ARG, "lse is NULL");
   }
   if (!dsinks) return fail(SINK_ATTN_ERR_INVALID_ARG, "dsinks is NULL");
-  int dkdv_heads = 0;
+  int dkdv_heads = 0, pack_heads = 0;
   SA_CHECK(resolve_dkdv_heads(p, &dkdv_heads));
-  const sinkattn::BwdWorkspace ws = workspace_layout(p, dkdv_heads);
+  SA_CHECK(resolve_pack_heads(p, 32, &pack_heads));
+  const sinkattn::BwdWorkspace ws = workspace_layout(p, dkdv_heads, pack_heads);
   if (workspace_bytes < ws.total)
     return fail(SINK_ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, ws.total);
   if (ws.total > 0 && !workspace) return fail(SINK_ATTN_ERR_INVALID_ARG, "workspace is NULL");
@@ -294,6 +297,7 @@ int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const
   a.scale = p->softmax_scale;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   a.dkdv_heads = dkdv_heads;
+  a.heads_per_tile = pack_heads;
   hipError_t e = sinkattn::launch_bwd(a, p->dtype, p->max_seqlen, p->num_seqs, s,
                                        g_bwd_events_on ? g_bwd_events : nullptr);
   if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));

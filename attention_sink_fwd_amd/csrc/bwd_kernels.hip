@@ -57,14 +57,20 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(BwdArgs a, int conv_block
   const int tid = threadIdx.x;
   const int Hq = a.num_q_heads;
   if ((int)blockIdx.x >= conv_blocks) {
-    // dS_h = sum of the head's per-tile partials, one wavefront per head,
-    // fixed order.
-    const int h = (blockIdx.x - conv_blocks) * 4 + (tid >> 6);
+    // dS_h = sum of the head's per-tile partials, one workgroup per head, in
+    // a fixed order (strided per thread, then a fixed tree).
+    __shared__ float part[kFlatThreads];
+    const int h = blockIdx.x - conv_blocks;
     if (h >= Hq) return;
     float s = 0.0f;
-    for (int j = tid & 63; j < parts; j += 64) s += a.dsink_part[(long)h * parts + j];
-    s = wave_sum(s);
-    if ((tid & 63) == 0) a.dsinks[h] = s;
+    for (int j = tid; j < parts; j += kFlatThreads) s += a.dsink_part[(long)h * parts + j];
+    part[tid] = s;
+    __syncthreads();
+    for (int n = kFlatThreads / 2; n > 0; n >>= 1) {
+      if (tid < n) part[tid] += part[tid + n];
+      __syncthreads();
+    }
+    if (tid == 0) a.dsinks[h] = part[0];
     return;
   }
   // dK, dV = the head groups' partial sums, in group order.
@@ -350,28 +356,35 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int h2 = lane >> 5, l32 = lane & 31;
   // The direct path is only built for head_dim == kD.
   const int hd = kDirect ? kD : a.head_dim, T = a.total_tokens, window = a.window;
-  const TileUnit unit = xcd_unit(a.num_q_heads, a.num_seqs);
-  const int seq = unit.seq, hq = unit.head;
-  const int ntiles = (int)gridDim.x / (a.num_q_heads * a.num_seqs);
+  // Column n = 32 w + l32 is query row q0 + n / hp of head hb * hp + n % hp
+  // (hp query heads of one KV group share the workgroup's K/V tiles).
+  const int hp = a.heads_per_tile, rows = kQT / hp;
+  const TileUnit unit = xcd_unit(a.num_q_heads / hp, a.num_seqs);
+  const int seq = unit.seq, hb = unit.head;
+  const int ntiles = (int)gridDim.x / (a.num_q_heads / hp * a.num_seqs);
   const int qt = ntiles - 1 - unit.rank;  // heaviest (last) query tiles first
-  float* __restrict__ dsink_slot = a.dsink_part + ((long)hq * a.num_seqs + seq) * ntiles + qt;
+  // dS partial of head h for this tile: dsink_part[(h * num_seqs + seq) * ntiles + qt]
+  float* __restrict__ dsink_slots = a.dsink_part + ((long)hb * hp * a.num_seqs + seq) * ntiles + qt;
+  const long slot_stride = (long)a.num_seqs * ntiles;
   const int bos = a.cu_seqlens[seq];
   const int L = a.cu_seqlens[seq + 1] - bos;
-  const int q0 = qt * kQT;
+  const int q0 = qt * rows;
   if (q0 >= L) {
-    if (tid == 0) *dsink_slot = 0.0f;
+    if (tid < hp) dsink_slots[tid * slot_stride] = 0.0f;
     return;
   }
 
-  const int g = hq / (a.num_q_heads / a.num_kv_heads);
+  const int g = hb * hp / (a.num_q_heads / a.num_kv_heads);
   const int qs = a.num_q_heads * hd, ks = a.num_kv_heads * hd;
+  const int col = 32 * w + l32;
+  const int hq = hb * hp + col % hp;  // this lane's query head
   const TIn* __restrict__ Qh = (const TIn*)a.q + (long)bos * qs + hq * hd;
   const TIn* __restrict__ dOh = (const TIn*)a.dout + (long)bos * qs + hq * hd;
   const TIn* __restrict__ Oh = (const TIn*)a.o + (long)bos * qs + hq * hd;
   const TIn* __restrict__ Kg = (const TIn*)a.k + (long)bos * ks + g * hd;
   const TIn* __restrict__ Vg = (const TIn*)a.v + (long)bos * ks + g * hd;
 
-  const int kend = min(L, q0 + kQT);
+  const int kend = min(L, q0 + rows);
   const int kbeg = window > 0 ? max(0, q0 - window + 1) : 0;
   const int t0 = kbeg / kKT, t1 = (kend + kKT - 1) / kKT;
 
@@ -390,7 +403,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   // This lane's query row (column n of the transposed products) and its Q and
   // dO fragments (B operands); the lane holds half of the row's d values.
-  const int qrow = q0 + 32 * w + l32;
+  const int qrow = q0 + col / hp;
   const int qcl = min(qrow, L - 1);
   const float lse = a.lse[(long)hq * T + bos + qcl];
   const float sink = a.sinks[hq];
@@ -427,7 +440,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   const float sl2 = a.scale_log2;
   const int krow_base = row_perm(l32);
-  const int wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
+  // First and last rows of this wavefront; one whose rows all lie past the
+  // sequence only takes part in the loads.
+  const int wq_lo = q0 + 32 * w / hp, wq_hi = q0 + (32 * w + 31) / hp;
+  const bool live = wq_lo < L;
 
   int buf = 0;
   for (int t = t0; t < t1; ++t) {
@@ -442,7 +458,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const KStage& st = stage[buf];
     const int kb = t * kKT;
     if (++buf == kStages) buf = 0;
-    if (kb > wq_hi) continue;                                      // all keys after all rows
+    if (!live || kb > wq_hi) continue;                             // no rows, or all keys after all rows
     if (window > 0 && wq_lo - (kb + kKT - 1) >= window) continue;  // all keys left of window
 
     // S^T and dP^T for two 32-key blocks; register r of block blk holds key
@@ -501,11 +517,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     a.ndelta[(long)hq * T + bos + qrow] = nD;
   }
   {
-    __shared__ float wsum[4];
-    const float sw = wave_sum(own_row ? -__expf(sink - lse) * D : 0.0f);
-    if (lane == 0) wsum[w] = sw;
+    // Sum per head: lanes with equal lane % hp hold the same head.
+    __shared__ float wsum[4][32];
+    float sw = own_row ? -__expf(sink - lse) * D : 0.0f;
+    for (int off = hp; off < 64; off *= 2) sw += __shfl_xor(sw, off);
+    if (lane < hp) wsum[w][lane] = sw;
     __syncthreads();
-    if (tid == 0) *dsink_slot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    if (tid < hp) dsink_slots[tid * slot_stride] = (wsum[0][tid] + wsum[1][tid]) + (wsum[2][tid] + wsum[3][tid]);
   }
   if (qrow < L) {
     TIn* dq = (TIn*)a.dq + (long)(bos + qrow) * qs + hq * hd;
@@ -531,10 +549,13 @@ int flat_blocks(long work_items) {
 
 }  // namespace
 
-int bwd_dsink_parts(int max_seqlen, int num_seqs) { return (max_seqlen + kQT - 1) / kQT * num_seqs; }
+int bwd_dsink_parts(int max_seqlen, int num_seqs, int heads_per_tile) {
+  const int rows = kQT / heads_per_tile;
+  return (max_seqlen + rows - 1) / rows * num_seqs;
+}
 
 BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d, int max_seqlen, int num_seqs,
-                                  int dkdv_heads) {
+                                  int dkdv_heads, int heads_per_tile) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const int P = hq / hkv / dkdv_heads;  // head groups per KV head
   BwdWorkspace w;
@@ -542,7 +563,7 @@ BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d, int 
   w.nlse = w.ndelta;
   w.dk_part = P > 1 ? up((size_t)P * total_tokens * hkv * d * sizeof(float)) : 0;
   w.dv_part = w.dk_part;
-  w.dsink_part = up((size_t)bwd_dsink_parts(max_seqlen, num_seqs) * hq * sizeof(float));
+  w.dsink_part = up((size_t)bwd_dsink_parts(max_seqlen, num_seqs, heads_per_tile) * hq * sizeof(float));
   w.total = w.ndelta + w.nlse + w.dk_part + w.dv_part + w.dsink_part;
   return w;
 }
@@ -572,13 +593,14 @@ int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, 
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t stream,
                       const hipEvent_t* events) {
   const int T = a.total_tokens, Hq = a.num_q_heads;
-  const int parts = T > 0 ? bwd_dsink_parts(max_seqlen, num_seqs) : 0;
+  const int parts = T > 0 ? bwd_dsink_parts(max_seqlen, num_seqs, a.heads_per_tile) : 0;
   const long chunks = (long)T * 2 * a.num_kv_heads * a.head_dim / 8;
   const bool dkdv_partials = a.dkdv_heads * a.num_kv_heads != Hq;
   const int conv_blocks = (T > 0 && dkdv_partials) ? flat_blocks(chunks) : 0;
-  const int post_blocks = conv_blocks + (Hq + 3) / 4;
+  const int post_blocks = conv_blocks + Hq;
   const dim3 grid_kv((max_seqlen + kBN - 1) / kBN * (Hq / a.dkdv_heads) * num_seqs);
-  const dim3 grid_q((max_seqlen + kQT - 1) / kQT * Hq * num_seqs);
+  const int qrows = kQT / a.heads_per_tile;
+  const dim3 grid_q((max_seqlen + qrows - 1) / qrows * (Hq / a.heads_per_tile) * num_seqs);
   const bool direct = dtype == 0 && a.head_dim == kD;
   auto mark = [&](int i) { return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess; };
   hipError_t e;

@@ -43,7 +43,8 @@ struct BwdArgs {
   float* dv_part;  // workspace: float dV partial sums, same shape (both unused when P == 1)
   float* dsink_part;  // workspace: per-query-tile dS partials, [Hq, num_seqs, query tiles]
   int num_q_heads, num_kv_heads, head_dim, total_tokens, window, num_seqs;
-  int dkdv_heads;  // query heads per dK/dV workgroup (divides Hq / Hkv)
+  int dkdv_heads;      // query heads per dK/dV workgroup (divides Hq / Hkv)
+  int heads_per_tile;  // query heads of one KV head packed in a dQ workgroup (divides Hq/Hkv and 32)
   float scale;
   float scale_log2;
 };
@@ -53,7 +54,7 @@ struct BwdWorkspace {
   size_t ndelta, nlse, dk_part, dv_part, dsink_part, total;
 };
 BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d, int max_seqlen, int num_seqs,
-                                  int dkdv_heads);
+                                  int dkdv_heads, int heads_per_tile);
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s);
 // Query heads per dK/dV workgroup for a problem shape (a divisor of Hq/Hkv),

@@ -60,10 +60,11 @@
  * compute units); SINK_ATTN_DKDV_HEADS=n (a divisor of num_q_heads /
  * num_kv_heads) overrides it, for tests and tuning.  The workspace size
  * depends on it: query sink_attn_bwd_workspace_size under the same setting.
- * The forward kernels pack the query heads of one KV head into a workgroup
- * (up to 32, a power of two dividing num_q_heads / num_kv_heads), so each
- * key/value tile is loaded once for all of them; SINK_ATTN_FWD_HEADS=n
- * overrides the count.  The packing does not change any output bit.
+ * The forward and dQ kernels pack the query heads of one KV head into a
+ * workgroup (up to 32, a power of two dividing num_q_heads / num_kv_heads),
+ * so each key/value tile is loaded once for all of them;
+ * SINK_ATTN_PACK_HEADS=n overrides the count (the workspace size depends on
+ * it too).  The packing does not change any bit of O or LSE.
  *
  * Streams.  All work is enqueued on `stream` (a hipStream_t; NULL is the
  * default stream) and is asynchronous.  Entry points are thread-safe.

@@ -146,7 +146,9 @@ def test_workspace_size_and_too_small():
     T, hq, hkv, d = 1000, 8, 2, 64
     p = _good_params(T, hq, hkv, d)
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    parts = (T + 127) // 128  # one dS partial per 128-row query tile and head
+    # one dS partial per dQ tile and head; the dQ kernel packs the 4 heads of
+    # a KV group, so a tile holds 128 / 4 rows
+    parts = (T + 31) // 32
     # dK/dV partial sums: one plane per head group; this small shape takes one
     # head per group (P = hq / hkv planes)
     want = 2 * up(4 * hq * T) + 2 * up(4 * (hq // hkv) * T * hkv * d) + up(4 * parts * hq)
@@ -163,7 +165,19 @@ def test_workspace_follows_dkdv_heads(monkeypatch, heads, planes):
     T, hq, hkv, d = 1000, 8, 2, 64
     p = _good_params(T, hq, hkv, d)
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    want = 2 * up(4 * hq * T) + 2 * up(4 * planes * T * hkv * d) + up(4 * ((T + 127) // 128) * hq)
+    want = 2 * up(4 * hq * T) + 2 * up(4 * planes * T * hkv * d) + up(4 * ((T + 31) // 32) * hq)
+    assert lib.sink_attn_bwd_workspace_size(ctypes.byref(p)) == want
+
+
+@pytest.mark.parametrize("pack,rows", [(1, 128), (2, 64), (4, 32)])
+def test_workspace_follows_pack_heads(monkeypatch, pack, rows):
+    monkeypatch.setenv("SINK_ATTN_PACK_HEADS", str(pack))
+    monkeypatch.setenv("SINK_ATTN_DKDV_HEADS", "4")
+    lib = _lib.load()
+    T, hq, hkv, d = 1000, 8, 2, 64
+    p = _good_params(T, hq, hkv, d)
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    want = 2 * up(4 * hq * T) + up(4 * ((T + rows - 1) // rows) * hq)
     assert lib.sink_attn_bwd_workspace_size(ctypes.byref(p)) == want
 
 
@@ -242,8 +256,8 @@ def test_paged_forward_with_no_new_tokens_is_a_no_op():
 
 @pytest.mark.parametrize("value", ["0", "3", "64", "x"])
 def test_bad_fwd_heads_override_is_rejected(monkeypatch, value):
-    monkeypatch.setenv("SINK_ATTN_FWD_HEADS", value)
+    monkeypatch.setenv("SINK_ATTN_PACK_HEADS", value)
     p = _good_params()  # Hq/Hkv = 4
     assert _fwd(p) == _lib.SINK_ATTN_ERR_INVALID_ARG
-    assert "SINK_ATTN_FWD_HEADS" in _lib.load().sink_attn_last_error().decode()
+    assert "SINK_ATTN_PACK_HEADS" in _lib.load().sink_attn_last_error().decode()
     assert _fwd_paged(p, _paged_kv()) == _lib.SINK_ATTN_ERR_INVALID_ARG

@@ -63,7 +63,7 @@ def test_paged_forward_is_bit_identical_to_training_rows(monkeypatch, fwd_heads,
         if (hq // hkv) % fwd_heads:
             pytest.skip("head count does not divide the group")
         # the same packing for both calls; None: each call's own default
-        monkeypatch.setenv("SINK_ATTN_FWD_HEADS", str(fwd_heads))
+        monkeypatch.setenv("SINK_ATTN_PACK_HEADS", str(fwd_heads))
     say("case bits", lengths, q_lens, d, window, dtype, ps, "fwd_heads", fwd_heads)
     w = custom_workload(lengths, hq, hkv, d, window, dtype)
     inp = make_inputs(w, seed=sum(lengths) + 3 * d)

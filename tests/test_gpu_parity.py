@@ -176,7 +176,7 @@ def test_forward_head_packing_keeps_every_bit(monkeypatch, lengths, hq, hkv, win
     d = {k: v.to("cuda:0") for k, v in inp.items()}
     outs = []
     for hp in (1, 2, hq // hkv):
-        monkeypatch.setenv("SINK_ATTN_FWD_HEADS", str(hp))
+        monkeypatch.setenv("SINK_ATTN_PACK_HEADS", str(hp))
         say("case head packing", lengths, "heads per workgroup", hp)
         outs.append(sa.sink_attn_fwd(d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens"],
                                      w.max_seqlen, w.softmax_scale, window))
@@ -187,6 +187,29 @@ def test_forward_head_packing_keeps_every_bit(monkeypatch, lengths, hq, hkv, win
                                     w.softmax_scale, window)
     assert max_abs(outs[-1][0].double().cpu().numpy(), o_ref) <= TOL_O
     assert max_abs(outs[-1][1].double().cpu().numpy(), lse_ref) <= TOL_LSE
+
+
+@pytest.mark.parametrize("window", [0, 21])
+def test_backward_head_packing_keeps_gradients(monkeypatch, window):
+    """dQ, dK, dV do not depend on how many query heads a dQ workgroup packs
+    (bit for bit); dS only through the order of its partial sums."""
+    import attention_sink_fwd_amd as sa
+
+    w = custom_workload((260, 3, 129), 8, 2, 64, window, "bf16")
+    d = {k: v.to("cuda:0") for k, v in make_inputs(w, seed=8).items()}
+    res = []
+    for hp in (1, 2, 4):
+        monkeypatch.setenv("SINK_ATTN_PACK_HEADS", str(hp))
+        say("case backward packing", hp, "window", window)
+        o, lse = sa.sink_attn_fwd(d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens"], w.max_seqlen,
+                                  w.softmax_scale, window)
+        res.append(sa.sink_attn_bwd(d["q"], d["k"], d["v"], d["sinks"], o, lse, d["dout"],
+                                    d["cu_seqlens"], w.max_seqlen, w.softmax_scale, window))
+    torch.cuda.synchronize()
+    for r in res[1:]:
+        for a, b in zip(r[:3], res[0][:3]):
+            assert torch.equal(a, b)
+        assert rel_l2(r[3].double().cpu().numpy(), res[0][3].double().cpu().numpy()) < 1e-5
 
 
 def test_empty_batch_zeroes_dsinks():
