@@ -212,6 +212,32 @@ def test_backward_head_packing_keeps_gradients(monkeypatch, window):
         assert rel_l2(r[3].double().cpu().numpy(), res[0][3].double().cpu().numpy()) < 1e-5
 
 
+def test_autograd_wrapper_gives_the_entry_points_gradients():
+    """torch autograd through sink_attention: O and every gradient equal the
+    direct C-ABI calls bit for bit, and the oracle within tolerance."""
+    import attention_sink_fwd_amd as sa
+
+    w = custom_workload((150, 40), 8, 2, 64, 0, "bf16")
+    inp = make_inputs(w, seed=77)
+    say("case autograd wrapper", w.lengths)
+    d = {k: v.to("cuda:0") for k, v in inp.items()}
+    leaves = {n: d[n].clone().requires_grad_(True) for n in ("q", "k", "v", "sinks")}
+    o = sa.sink_attention(leaves["q"], leaves["k"], leaves["v"], leaves["sinks"], d["cu_seqlens"],
+                          w.max_seqlen)
+    (o.float() * d["dout"].float()).sum().backward()
+    o2, lse2 = sa.sink_attn_fwd(d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens"], w.max_seqlen)
+    dq, dk, dv, ds = sa.sink_attn_bwd(d["q"], d["k"], d["v"], d["sinks"], o2, lse2, d["dout"],
+                                      d["cu_seqlens"], w.max_seqlen)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o2)
+    for name, ref in (("q", dq), ("k", dk), ("v", dv), ("sinks", ds)):
+        assert torch.equal(leaves[name].grad, ref), name
+    gpu = {"o": o2.double().cpu().numpy(), "lse": lse2.double().cpu().numpy(),
+           "dq": dq.double().cpu().numpy(), "dk": dk.double().cpu().numpy(),
+           "dv": dv.double().cpu().numpy(), "ds": ds.double().cpu().numpy()}
+    check_full(gpu, _oracle_full(inp, w.softmax_scale, 0), "autograd wrapper")
+
+
 def test_empty_batch_zeroes_dsinks():
     import attention_sink_fwd_amd as sa
     dev = "cuda:0"
