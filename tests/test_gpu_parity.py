@@ -57,6 +57,11 @@ SMALL = [
     ((257,), 4, 2, 40, 0, "f32", "normal"),
     ((200, 3), 4, 4, 64, 9, "f32", "mixed"),
     ((520,), 16, 2, 64, 0, "bf16", "normal"),
+    # groups that are not a power of two (3 and 6 query heads per KV head)
+    ((260, 33), 6, 2, 64, 0, "bf16", "normal"),
+    ((300,), 12, 2, 64, 50, "bf16", "mixed"),
+    ((97, 131), 6, 1, 32, 0, "f32", "normal"),
+    ((129,), 1, 1, 64, 0, "bf16", "normal"),
 ]
 
 
