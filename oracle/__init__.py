@@ -19,6 +19,11 @@ Pins (all in tests/test_oracle_pins.py, CPU only):
                         cached context equal the last rows of forward over the
                         whole sequence; page order does not matter; a length-1
                         context gives the one-key closed form.
+  token_logps, token_logps_grad (oracle/token_logps.py)
+                     -> torch log_softmax + gather in float64 and its autograd;
+                        constant rows give -ln V; a per-row shift changes
+                        nothing; the gradient rows sum to zero; finite
+                        differences.
 No function here is "parity unpinned".
 """
 from .sink_attention import (  # noqa: F401
@@ -32,3 +37,4 @@ from .sink_attention import (  # noqa: F401
     kv_head_of,
     visible_key_range,
 )
+from .token_logps import token_logps, token_logps_grad  # noqa: F401

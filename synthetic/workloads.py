@@ -163,3 +163,26 @@ def make_paged(inputs: Dict[str, torch.Tensor], q_lens: Sequence[int], page_size
     return {"q": inputs["q"][rows_t], "k_cache": k_cache, "v_cache": v_cache, "block_table": bt,
             "kv_lens": torch.from_numpy(lens.astype(np.int32)), "cu_seqlens": torch.from_numpy(cu_q),
             "rows": rows_t, "sinks": inputs["sinks"]}
+
+
+def make_logits(num_rows: int, vocab: int, dtype: str, seed: int, scale: float = 3.0,
+                row_stride: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Seeded logits for the per-token log-probability kernels.
+
+    One ``default_rng(seed)`` stream: logits ``standard_normal`` float32 times
+    ``scale`` (a spread like a language model's next-token logits), then the
+    token ids ``integers(0, vocab)``, then the upstream gradient
+    ``standard_normal``.  With ``row_stride`` > vocab the rows sit in a wider
+    buffer (the extra columns are NaN and must never be read).  Returns
+    logits (a [num_rows, vocab] view), ids int32, grad float32.
+    """
+    rng = np.random.default_rng(seed)
+    x = torch.from_numpy(rng.standard_normal((num_rows, vocab), dtype=np.float32) * np.float32(scale))
+    ids = torch.from_numpy(rng.integers(0, vocab, size=num_rows).astype(np.int32))
+    grad = torch.from_numpy(rng.standard_normal(num_rows, dtype=np.float32))
+    x = x.to(torch.bfloat16) if dtype == "bf16" else x
+    if row_stride is not None and row_stride > vocab:
+        buf = torch.full((num_rows, row_stride), float("nan"), dtype=x.dtype)
+        buf[:, :vocab] = x
+        x = buf[:, :vocab]
+    return {"logits": x, "ids": ids, "grad": grad}
