@@ -8,5 +8,8 @@ from .binding import (  # noqa: F401
     sink_attn_bwd_workspace_size,
     sink_attn_fwd,
     sink_attn_fwd_paged,
+    token_logps,
+    token_logps_bwd,
+    token_logps_fwd,
 )
 from ._lib import LIB_PATH, SinkAttnError, load  # noqa: F401

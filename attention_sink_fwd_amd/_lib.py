@@ -28,6 +28,8 @@ EXPORTED_SYMBOLS = (
     "sink_attn_set_bwd_events",
     "sink_attn_status_string",
     "sink_attn_last_error",
+    "token_logps_fwd",
+    "token_logps_bwd",
 )
 
 
@@ -91,6 +93,11 @@ def load() -> ctypes.CDLL:
     lib.sink_attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.sink_attn_set_bwd_events.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
     lib.sink_attn_set_bwd_events.restype = ctypes.c_int
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.token_logps_fwd.argtypes = [vp, i32, i32, i32, i32, i64, i64, vp, vp, vp, vp]
+    lib.token_logps_fwd.restype = ctypes.c_int
+    lib.token_logps_bwd.argtypes = [vp, i32, i32, i32, i32, i64, i64, vp, vp, vp, vp, i64, i64, vp]
+    lib.token_logps_bwd.restype = ctypes.c_int
     lib.sink_attn_status_string.argtypes = [ctypes.c_int]
     lib.sink_attn_status_string.restype = ctypes.c_char_p
     lib.sink_attn_last_error.argtypes = []

@@ -173,3 +173,76 @@ class _SinkAttention(torch.autograd.Function):
 def sink_attention(q, k, v, sinks, cu_seqlens, max_seqlen, softmax_scale=None, window=0):
     """Differentiable packed sink attention: O with gradients for q, k, v and sinks."""
     return _SinkAttention.apply(q, k, v, sinks, cu_seqlens, max_seqlen, softmax_scale, window)
+
+
+def _logits_layout(logits: torch.Tensor, name: str = "logits"):
+    """(batch, seq, vocab, batch_stride, row_stride) of a [N, V] or [B, n, V]
+    GPU tensor whose last dimension is contiguous."""
+    if logits.dim() not in (2, 3) or not logits.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor [num_rows, vocab] or [batch, seq, vocab]")
+    if logits.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {logits.dtype}")
+    if logits.stride(-1) != 1:
+        raise ValueError(f"{name} must be contiguous along the vocabulary")
+    if logits.dim() == 2:
+        return 1, logits.shape[0], logits.shape[1], 0, logits.stride(0)
+    return logits.shape[0], logits.shape[1], logits.shape[2], logits.stride(0), logits.stride(1)
+
+
+def _row_vector(t, name, dtype, shape):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_cuda:
+        raise ValueError(f"{name} must be a {dtype} GPU tensor of shape {tuple(shape)}")
+    return t.contiguous()
+
+
+def token_logps_fwd(logits, ids, want_lse=True, stream=None):
+    """Per-token log-probabilities log_softmax(logits)[..., ids] (float32, the
+    shape of ids = logits.shape[:-1]) and, if want_lse, the row log-sum-exp.
+    logits may be a strided view such as logits[:, :-1, :]; it is read in place."""
+    lib = _lib.load()
+    b, n, vocab, bs, rs = _logits_layout(logits)
+    lead = logits.shape[:-1]
+    ids = _row_vector(ids, "ids", torch.int32, lead)
+    logps = torch.empty(lead, dtype=torch.float32, device=logits.device)
+    lse = torch.empty(lead, dtype=torch.float32, device=logits.device) if want_lse else None
+    _lib.check(lib.token_logps_fwd(_ptr(logits), _DTYPES[logits.dtype], b, n, vocab, bs, rs, _ptr(ids),
+                                   _ptr(logps), _ptr(lse), _stream(stream)))
+    return logps, lse
+
+
+def token_logps_bwd(logits, ids, lse, grad_logps, grad_logits=None, stream=None):
+    """dL/dlogits (dtype and shape of logits) for upstream grad_logps.
+    Without grad_logits the result is a new tensor with the logits' strides."""
+    lib = _lib.load()
+    b, n, vocab, bs, rs = _logits_layout(logits)
+    lead = logits.shape[:-1]
+    ids = _row_vector(ids, "ids", torch.int32, lead)
+    lse = _row_vector(lse, "lse", torch.float32, lead)
+    grad_logps = _row_vector(grad_logps, "grad_logps", torch.float32, lead)
+    if grad_logits is None:
+        grad_logits = torch.empty_strided(logits.shape, logits.stride(), dtype=logits.dtype, device=logits.device)
+    if grad_logits.dtype != logits.dtype or grad_logits.shape != logits.shape:
+        raise ValueError("grad_logits must match logits in dtype and shape")
+    _, _, _, gbs, grs = _logits_layout(grad_logits, "grad_logits")
+    _lib.check(lib.token_logps_bwd(_ptr(logits), _DTYPES[logits.dtype], b, n, vocab, bs, rs, _ptr(ids),
+                                   _ptr(lse), _ptr(grad_logps), _ptr(grad_logits), gbs, grs,
+                                   _stream(stream)))
+    return grad_logits
+
+
+class _TokenLogps(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, logits, ids):
+        logps, lse = token_logps_fwd(logits, ids)
+        ctx.save_for_backward(logits, ids, lse)
+        return logps
+
+    @staticmethod
+    def backward(ctx, grad):
+        logits, ids, lse = ctx.saved_tensors
+        return token_logps_bwd(logits, ids, lse, grad.float()), None
+
+
+def token_logps(logits, ids):
+    """Differentiable per-token log-probabilities (gradient flows into logits)."""
+    return _TokenLogps.apply(logits, ids)

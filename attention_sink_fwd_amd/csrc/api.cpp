@@ -14,13 +14,15 @@
 #include <vector>
 
 #include "launch.h"
+#include "status.h"
 
 namespace {
-
 thread_local char g_last_error[512] = "";
 thread_local hipEvent_t g_bwd_events[4] = {nullptr, nullptr, nullptr, nullptr};
 thread_local bool g_bwd_events_on = false;
+}  // namespace
 
+namespace sinkattn {
 int fail(int status, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -28,6 +30,12 @@ int fail(int status, const char* fmt, ...) {
   va_end(ap);
   return status;
 }
+void clear_error() { g_last_error[0] = '\0'; }
+}  // namespace sinkattn
+
+namespace {
+
+using sinkattn::fail;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -149,6 +157,8 @@ int sink_attn_fwd(const sink_attn_params* p, const void* q, const void* k, const
   return SINK_ATTN_OK;
 }
 
+}  // extern "C"
+
 namespace {
 
 // Optional host-side check of the paged cache description against the device
@@ -177,6 +187,8 @@ int maybe_validate_paged(const sink_attn_params* p, const sink_attn_paged_kv* kv
 }
 
 }  // namespace
+
+extern "C" {
 
 int sink_attn_fwd_paged(const sink_attn_params* p, const sink_attn_paged_kv* kv, const void* q, const float* sinks,
                         void* o, float* lse, void* stream) {
@@ -216,6 +228,8 @@ int sink_attn_fwd_paged(const sink_attn_params* p, const sink_attn_paged_kv* kv,
   return SINK_ATTN_OK;
 }
 
+}  // extern "C"
+
 namespace {
 
 // Query heads per dK/dV workgroup: SINK_ATTN_DKDV_HEADS if set (it must
@@ -241,6 +255,8 @@ sinkattn::BwdWorkspace workspace_layout(const sink_attn_params* p, int dkdv_head
 }
 
 }  // namespace
+
+extern "C" {
 
 size_t sink_attn_bwd_workspace_size(const sink_attn_params* p) {
   int hg = 0, hp = 0;

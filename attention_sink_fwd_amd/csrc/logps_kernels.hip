@@ -1,0 +1,189 @@
+// Per-token log-probabilities (fused log-softmax + gather) and their
+// gradient, on gfx950.
+//
+// Method: MiniMind tutorial page "强化学习:GRPO 与 PPO", Part 7 "Rollout
+// 引擎", subsection "LogProb 计算": the log-probability of a sampled token is
+// log_softmax(logits)[id] over the vocabulary; RL losses need it for every
+// generated position, and its gradient flows back into the logits.
+//
+// Both kernels stream each row of the logits once (HBM-bound: a GPT-OSS row
+// of 201,088 bf16 logits is 402 KB).  One workgroup per row; each thread
+// walks 8-element chunks of the row, four chunks in flight, keeping an
+// online (max, sum of exp) pair in float; the 256 pairs are merged in a
+// fixed butterfly/tree order, so every row's result is reproducible bit for
+// bit.  The gradient kernel recomputes p = exp(x - lse) from the forward's
+// lse and writes g * ([v == id] - p) in the logits' type.
+//
+// The logits are read, and the gradient written, with non-temporal accesses:
+// each byte is touched once, and keeping the stream out of the caches
+// measured 6.9 TB/s instead of 5.7 for the forward on MI355X (the backward,
+// a read+write stream, runs at the chip's copy rate either way).
+#include <type_traits>
+
+#include "device_common.h"
+#include "logps_launch.h"
+
+namespace sinkattn {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;  // chunks of 8 elements in flight per thread
+
+// One element as float, and one float stored in the logits' type.
+__device__ __forceinline__ float load1f(const bf16* p) { return (float)*p; }
+__device__ __forceinline__ float load1f(const float* p) { return *p; }
+__device__ __forceinline__ void store1(bf16* p, float v) { *p = (bf16)v; }
+__device__ __forceinline__ void store1(float* p, float v) { *p = v; }
+
+// 8 consecutive elements (16-byte aligned), read or written past the caches.
+__device__ __forceinline__ f32x8 ld8(const bf16* p) {
+  return __builtin_convertvector(__builtin_nontemporal_load((const bf16x8*)p), f32x8);
+}
+__device__ __forceinline__ f32x8 ld8(const float* p) {
+  const f32x4 a = __builtin_nontemporal_load((const f32x4*)p);
+  const f32x4 b = __builtin_nontemporal_load((const f32x4*)(p + 4));
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ void st8(bf16* p, const f32x8& v) {
+  __builtin_nontemporal_store(__builtin_convertvector(v, bf16x8), (bf16x8*)p);
+}
+__device__ __forceinline__ void st8(float* p, const f32x8& v) {
+  __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, (f32x4*)p);
+  __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, (f32x4*)(p + 4));
+}
+
+// Merge two (max, sum of exp(x - max)) pairs; an empty pair has max -inf.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float M = __builtin_fmaxf(m, m2);
+  if (M == -__builtin_inff()) return;  // both empty
+  s = s * fast_exp2((m - M) * kLog2e) + s2 * fast_exp2((m2 - M) * kLog2e);
+  m = M;
+}
+
+// Fold 8 values into the running pair.
+__device__ __forceinline__ void lse_add8(float& m, float& s, const f32x8& x) {
+  float cm = __builtin_fmaxf(__builtin_fmaxf(x[0], x[1]), x[2]);
+  cm = __builtin_fmaxf(__builtin_fmaxf(cm, x[3]), x[4]);
+  cm = __builtin_fmaxf(__builtin_fmaxf(cm, x[5]), x[6]);
+  cm = __builtin_fmaxf(cm, x[7]);
+  const float M = __builtin_fmaxf(m, cm);
+  if (M == -__builtin_inff()) return;  // nothing finite yet
+  const float nm = -M * kLog2e;
+  float e[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = fast_exp2(__builtin_fmaf(x[i], kLog2e, nm));
+  const float add = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  s = s * fast_exp2((m - M) * kLog2e) + add;
+  m = M;
+}
+
+// Element offset of row i = b * seq + t.
+__device__ __forceinline__ long row_offset(int i, int seq, long batch_stride, long row_stride) {
+  const int b = i / seq;
+  return b * batch_stride + (long)(i - b * seq) * row_stride;
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void logps_fwd_kernel(LogpsArgs a) {
+  __shared__ float wm[kThreads / 64], ws[kThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int row = blockIdx.x;
+  const TIn* __restrict__ x = (const TIn*)a.logits + row_offset(row, a.seq, a.batch_stride, a.row_stride);
+  const int V = a.vocab, nfull = V / 8;
+
+  float m = -__builtin_inff(), s = 0.0f;
+  int c = tid;
+  for (; c + (kUnroll - 1) * kThreads < nfull; c += kUnroll * kThreads) {
+    f32x8 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = ld8(x + 8L * (c + u * kThreads));
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) lse_add8(m, s, v[u]);
+  }
+  for (; c < nfull; c += kThreads) lse_add8(m, s, ld8(x + 8L * c));
+  if (tid < V - 8 * nfull) {  // the last vocab % 8 elements, one per thread
+    const float t = load1f(x + 8L * nfull + tid);
+    lse_merge(m, s, t, 1.0f);
+  }
+
+  // Fixed-order merge: butterfly within the wavefront, then the waves in order.
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+    lse_merge(m, s, m2, s2);
+  }
+  if (lane == 0) {
+    wm[w] = m;
+    ws[w] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float M = wm[0], S = ws[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) lse_merge(M, S, wm[i], ws[i]);
+    const float lse = M + __log2f(S) * kLn2;
+    const int id = a.ids[row];
+    const float xid = (id >= 0 && id < V) ? load1f(x + id) : __builtin_nanf("");
+    a.logps[row] = xid - lse;
+    if (a.lse_out) a.lse_out[row] = lse;
+  }
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void logps_bwd_kernel(LogpsArgs a) {
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const TIn* __restrict__ x = (const TIn*)a.logits + row_offset(row, a.seq, a.batch_stride, a.row_stride);
+  TIn* __restrict__ gx =
+      (TIn*)a.grad_logits + row_offset(row, a.seq, a.grad_batch_stride, a.grad_row_stride);
+  const int V = a.vocab, nfull = V / 8;
+  const float g = a.grad_logps[row];
+  const float nl = -a.lse_in[row] * kLog2e;
+  const int id = a.ids[row];
+
+  // One chunk: g * ([v == id] - exp(x - lse)).
+  auto grad8 = [&](int c, const f32x8& v) {
+    f32x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = fast_exp2(__builtin_fmaf(v[i], kLog2e, nl));
+      r[i] = (8 * c + i == id) ? g - g * p : -g * p;
+    }
+    st8(gx + 8L * c, r);
+  };
+  int c = tid;
+  for (; c + (kUnroll - 1) * kThreads < nfull; c += kUnroll * kThreads) {
+    f32x8 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = ld8(x + 8L * (c + u * kThreads));
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) grad8(c + u * kThreads, v[u]);
+  }
+  for (; c < nfull; c += kThreads) grad8(c, ld8(x + 8L * c));
+  if (tid < V - 8 * nfull) {
+    const int e = 8 * nfull + tid;
+    const float p = fast_exp2(__builtin_fmaf(load1f(x + e), kLog2e, nl));
+    store1(gx + e, (e == id) ? g - g * p : -g * p);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_logps_fwd(const LogpsArgs& a, int dtype, hipStream_t stream) {
+  if (dtype == 0)
+    hipLaunchKernelGGL(logps_fwd_kernel<bf16>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(logps_fwd_kernel<float>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_logps_bwd(const LogpsArgs& a, int dtype, hipStream_t stream) {
+  if (dtype == 0)
+    hipLaunchKernelGGL(logps_bwd_kernel<bf16>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(logps_bwd_kernel<float>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace sinkattn

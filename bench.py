@@ -204,6 +204,78 @@ def paged_decode(args):
     }), flush=True)
 
 
+def token_logps(args):
+    """One step of per-token log-probabilities and their gradient: 8192
+    positions over GPT-OSS's 201,088-entry vocabulary in bfloat16 (3.3 GB of
+    logits), seeded normal logits.  Each kernel is bracketed with HIP events
+    on its stream; the rate counts the bytes each kernel must move (logits
+    read once by each, the gradient written once, the per-row vectors)."""
+    import torch
+
+    import attention_sink_fwd_amd as sa
+    from synthetic.workloads import make_logits_device
+
+    rows, vocab = 8192, 201088
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = make_logits_device(rows, vocab, "bf16", seed=1234, device="cuda:0")
+    x, ids, g = d["logits"], d["ids"], d["grad"]
+    logps = torch.empty((rows,), dtype=torch.float32, device=dev)
+    lse = torch.empty_like(logps)
+    gx = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    lib = sa._lib.load()
+    hip = Hip()
+
+    def step(ev=None):
+        if ev:
+            hip.record(ev[0], sh)
+        sa._lib.check(lib.token_logps_fwd(x.data_ptr(), 0, 1, rows, vocab, 0, vocab, ids.data_ptr(),
+                                          logps.data_ptr(), lse.data_ptr(), sh))
+        if ev:
+            hip.record(ev[1], sh)
+        sa._lib.check(lib.token_logps_bwd(x.data_ptr(), 0, 1, rows, vocab, 0, vocab, ids.data_ptr(),
+                                          lse.data_ptr(), g.data_ptr(), gx.data_ptr(), 0, vocab, sh))
+        if ev:
+            hip.record(ev[2], sh)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(hip.event(), hip.event(), hip.event()) for _ in range(K)]
+    t0 = time.perf_counter()
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    fwd_ms = sum(hip.ms(a, b) for a, b, _ in evs) / K
+    bwd_ms = sum(hip.ms(b, c) for _, b, c in evs) / K
+    for ev in evs:
+        for e in ev:
+            hip.destroy(e)
+    xb = float(rows) * vocab * 2
+    fwd_bytes = xb + rows * (4 + 4 + 4)          # logits, ids in; logp, lse out
+    bwd_bytes = 2 * xb + rows * (4 + 4 + 4)      # logits in, grad out; ids, lse, g in
+    step_gbs = (fwd_bytes + bwd_bytes) / ((fwd_ms + bwd_ms) * 1e-3) / 1e9
+    dom, dom_ms, dom_bytes = ("logps_bwd", bwd_ms, bwd_bytes) if bwd_ms >= fwd_ms else \
+        ("logps_fwd", fwd_ms, fwd_bytes)
+    ach = dom_bytes / (dom_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "per-token log-prob fwd+bwd, HBM GB/s (8192 positions x 201088 vocab, bf16)",
+        "value": round(step_gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1000.0 / K, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "token_logps_rows8192_vocab201088", "rows": rows, "vocab": vocab},
+        "kernel_ms": {"logps_fwd": round(fwd_ms, 5), "logps_bwd": round(bwd_ms, 5)},
+        "roofline": {"kernel": dom, "kernel_ms": round(dom_ms, 5), "bound": "hbm",
+                     "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(ach / PEAK_HBM_GBS, 4), "algorithmic_bytes": dom_bytes,
+                     "traffic": traffic_for_current_kernel(dom)},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +285,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--paged-decode", action="store_true",
                     help="time one decode step over a paged KV cache instead (own JSON line)")
+    ap.add_argument("--token-logps", action="store_true",
+                    help="time the per-token log-probability kernels instead")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a known-size copy kernel (for rocprofv3 counter scaling)")
     args = ap.parse_args()
@@ -225,6 +299,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.token_logps:
+        token_logps(args)
         return
     if args.paged_decode:
         paged_decode(args)

@@ -186,3 +186,26 @@ def make_logits(num_rows: int, vocab: int, dtype: str, seed: int, scale: float =
         buf[:, :vocab] = x
         x = buf[:, :vocab]
     return {"logits": x, "ids": ids, "grad": grad}
+
+
+def make_logits_device(num_rows: int, vocab: int, dtype: str, seed: int, device: str,
+                       scale: float = 3.0) -> Dict[str, torch.Tensor]:
+    """Full-size logits drawn on the GPU (a CPU draw of a 200k-entry
+    vocabulary for thousands of rows takes minutes).
+
+    One ``torch.Generator(device)`` seeded with ``seed``: logits ``randn``
+    float32 times ``scale``, then ids ``randint(0, vocab)`` (int32), then the
+    upstream gradient ``randn``.  Rows are contiguous (vocab must be a
+    multiple of 8).  Sampled rows copied to the host are the oracle's inputs.
+    """
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x = torch.empty((num_rows, vocab), dtype=tdt, device=device)
+    chunk = max(1, (1 << 28) // vocab)  # bound the float32 temporary
+    for r in range(0, num_rows, chunk):
+        n = min(chunk, num_rows - r)
+        x[r:r + n] = (torch.randn((n, vocab), generator=gen, device=device) * scale).to(tdt)
+    ids = torch.randint(0, vocab, (num_rows,), generator=gen, device=device, dtype=torch.int32)
+    grad = torch.randn((num_rows,), generator=gen, device=device)
+    return {"logits": x, "ids": ids, "grad": grad}

@@ -9,13 +9,17 @@ import pytest
 from attention_sink_fwd_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "sink_attn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sink_attn_\w+)\s*\(", text)))
+    names = set()
+    for header in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+        # function declarations: a return type, then name( ... );
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -261,3 +265,81 @@ def test_bad_fwd_heads_override_is_rejected(monkeypatch, value):
     assert _fwd(p) == _lib.SINK_ATTN_ERR_INVALID_ARG
     assert "SINK_ATTN_PACK_HEADS" in _lib.load().sink_attn_last_error().decode()
     assert _fwd_paged(p, _paged_kv()) == _lib.SINK_ATTN_ERR_INVALID_ARG
+
+
+
+# ---- per-token log-probabilities ----
+
+def _logps_fwd(**override):
+    lib = _lib.load()
+    a = dict(logits=FAKE, dtype=0, batch=2, seq=2, vocab=100, bstride=208, stride=104, ids=FAKE, logps=FAKE,
+             lse=None)
+    a.update(override)
+    return lib.token_logps_fwd(a["logits"], a["dtype"], a["batch"], a["seq"], a["vocab"], a["bstride"],
+                               a["stride"], a["ids"], a["logps"], a["lse"], None)
+
+
+def _logps_bwd(**override):
+    lib = _lib.load()
+    a = dict(logits=FAKE, dtype=0, batch=2, seq=2, vocab=100, bstride=208, stride=104, ids=FAKE, lse=FAKE,
+             g=FAKE, gx=FAKE, gbstride=208, gstride=104)
+    a.update(override)
+    return lib.token_logps_bwd(a["logits"], a["dtype"], a["batch"], a["seq"], a["vocab"], a["bstride"],
+                               a["stride"], a["ids"], a["lse"], a["g"], a["gx"], a["gbstride"], a["gstride"],
+                               None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dtype", 3, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("batch", -1, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("seq", -1, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("seq", 1 << 23, _lib.SINK_ATTN_ERR_UNSUPPORTED),   # 2 x 2^23 rows
+    ("vocab", 0, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("stride", 96, _lib.SINK_ATTN_ERR_INVALID_ARG),     # below vocab
+    ("stride", 108, _lib.SINK_ATTN_ERR_INVALID_ARG),    # not a multiple of 8
+    ("bstride", 212, _lib.SINK_ATTN_ERR_INVALID_ARG),   # not a multiple of 8
+    ("bstride", -208, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("logits", None, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("logits", FAKE + 8, _lib.SINK_ATTN_ERR_INVALID_ARG),
+    ("ids", None, _lib.SINK_ATTN_ERR_INVALID_ARG),
+])
+def test_logps_rejects_bad_arguments(field, value, status):
+    assert _logps_fwd(**{field: value}) == status
+    assert _lib.load().sink_attn_last_error().decode() != ""
+    assert _logps_bwd(**{field: value}) == status
+
+
+def test_logps_output_pointers_are_checked():
+    assert _logps_fwd(logps=None) == _lib.SINK_ATTN_ERR_INVALID_ARG
+    for name in ("lse", "g", "gx"):
+        assert _logps_bwd(**{name: None}) == _lib.SINK_ATTN_ERR_INVALID_ARG
+    assert _logps_bwd(gstride=99) == _lib.SINK_ATTN_ERR_INVALID_ARG
+    assert _logps_bwd(gbstride=204) == _lib.SINK_ATTN_ERR_INVALID_ARG
+    assert _logps_bwd(gx=FAKE + 4) == _lib.SINK_ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("gbstride,gstride,ok", [
+    (208, 104, True),     # batch-major, packed
+    (0, 104, False),      # every batch on the same rows
+    (200, 104, False),    # batch 1 starts inside batch 0's last row
+    (104, 208, True),     # position-major ([seq, batch, vocab] storage)
+    (96, 208, False),     # rows of one position overlap
+    (104, 200, False),    # position 1 starts inside position 0's last row
+])
+def test_logps_gradient_rows_must_not_overlap(gbstride, gstride, ok):
+    # lse=None stops an accepted layout at the next check, before any launch
+    assert _logps_bwd(gbstride=gbstride, gstride=gstride, lse=None) == _lib.SINK_ATTN_ERR_INVALID_ARG
+    msg = _lib.load().sink_attn_last_error().decode()
+    assert ("overlap" not in msg and "lse" in msg) if ok else ("overlap" in msg)
+
+
+def test_logps_input_rows_may_overlap():
+    # reading is harmless: a zero batch stride (the same rows for every batch) is accepted
+    assert _logps_fwd(bstride=0, logps=None) == _lib.SINK_ATTN_ERR_INVALID_ARG  # only logps is missing
+    assert "logps" in _lib.load().sink_attn_last_error().decode()
+
+
+def test_logps_zero_rows_is_a_no_op():
+    for b, n in ((0, 4), (4, 0)):
+        assert _logps_fwd(batch=b, seq=n, logits=None, ids=None, logps=None) == _lib.SINK_ATTN_OK
+        assert _logps_bwd(batch=b, seq=n, logits=None, ids=None, lse=None, g=None, gx=None) == _lib.SINK_ATTN_OK
