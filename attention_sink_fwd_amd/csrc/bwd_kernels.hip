@@ -13,8 +13,8 @@
 //  1. bwd_dq_kernel    one workgroup per (sequence, query head, 128-row query
 //                      tile).  First the row statistics: D_i = dO_i . O_i,
 //                      and the sink term -p_sink,i D_i summed over the tile
-//                      into a per-tile partial; -D_i and -LSE_i / scale go to
-//                      the workspace for the next kernel.  Then it loops over
+//                      into a per-tile partial; -D_i and -LSE_i log2(e) go
+//                      to the workspace for the next kernel.  Then it loops over
 //                      the visible 64-key tiles: recomputes S and dP in
 //                      transposed form and accumulates dQ = scale * dS K in
 //                      registers; writes dQ once.
@@ -32,6 +32,13 @@
 //
 // No float atomics anywhere: every gradient is a fixed-order sum, so the
 // backward pass is bitwise reproducible run to run.
+//
+// The score product's register-resident operand (Q in the dQ kernel, K in
+// the dK/dV kernel) is multiplied by scale * log2(e) once, when it is loaded,
+// and the score accumulators start from -LSE_i log2(e): they then hold
+// log2 P directly, so P = exp2(acc) needs no per-score multiply.  The scaled
+// operand is rounded to bf16 once (relative 2^-9 per element, about 2e-3 in
+// the exponent for d = 64: below the bf16 rounding P itself gets).
 //
 // dQ is not accumulated with float atomics across key tiles: on this chip
 // float atomics retire at about 0.3 G element-operations per microsecond,
@@ -94,7 +101,7 @@ constexpr int kD = 64;    // padded head dimension
 struct __attribute__((aligned(16))) QStage {
   bf16 q[kBM * kD];     // Q tile, swizzled [q][d]
   bf16 dout[kBM * kD];  // dO tile, swizzled [q][d]
-  float nlse[kBM];      // -LSE/scale of the tile rows
+  float nlse[kBM];      // -LSE log2(e) of the tile rows
   float ndelta[kBM];    // -D of the tile rows
   float spare[kBM];     // landing area that keeps every wavefront's load count equal
 };
@@ -183,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int d0 = 16 * c + 8 * h2;
-      kf[c] = d0 < hd ? load8(Kg + krow * ks + d0) : zero8();
+      kf[c] = d0 < hd ? __builtin_convertvector(load8f(Kg + krow * ks + d0) * a.scale_log2, bf16x8) : zero8();
       vf[c] = d0 < hd ? load8(Vg + krow * ks + d0) : zero8();
     }
   }
@@ -198,7 +205,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) { dk[0][i] = dk[1][i] = dv[0][i] = dv[1][i] = 0.0f; }
 
-  const float sl2 = a.scale_log2;
   const int qrow_base = row_perm(l32);
 
   // One step: consume query tile ct (of some head) from `st`, prefetch two
@@ -224,8 +230,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         // S and dP for query rows 32*mb .. 32*mb+31 of the tile; register r
         // holds row 32*mb + 16*(r/8) + 8*h2 + r%8 (A rows permuted), so each
         // half of the registers covers 8 consecutive rows.  The accumulators
-        // start from the row statistics -LSE/scale and -D, so that
-        // P = exp2(S * scale * log2 e) and dS = P * dP need one multiply each.
+        // start from the row statistics -LSE log2(e) and -D, and K is
+        // pre-scaled by scale * log2(e), so P = exp2(s) and dS = P * dP.
         const int qr = qrow_base + 32 * mb;
         const int ql0 = 32 * mb + 8 * h2;
         f32x16 s, dp;
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
               const int r = 8 * hb + i;
-              float p = fast_exp2(s[r] * sl2);
+              float p = fast_exp2(s[r]);
               if constexpr (decltype(masked)::value) {
                 const int idx = 16 * hb + i;
                 p = (idx >= lo && idx < hi) ? p : 0.0f;
@@ -343,8 +349,8 @@ struct __attribute__((aligned(16))) KStage {
 };
 
 // Row statistics and dQ for one 128-row query tile of one head.  Transposed
-// products keep each query row on a lane: S^T = K Q^T and dP^T = V dO^T (accumulators seeded
-// with -LSE/scale and -D of the lane's row), P^T = exp2(S^T scale log2 e),
+// products keep each query row on a lane: S^T = K Q^T and dP^T = V dO^T (Q pre-scaled by
+// scale log2 e; accumulators seeded with -LSE log2 e and -D of the lane's row), P^T = exp2(S^T),
 // dS^T = P^T dP^T, dQ^T += K^T dS^T with K^T from the row-major K tile
 // through transposing reads.  dQ is written once, in the output type.
 template <typename TIn, bool kDirect>
@@ -412,7 +418,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int d0 = 16 * c + 8 * h2;
-    qf[c] = d0 < hd ? load8(Qh + qcl * qs + d0) : zero8();
+    qf[c] = d0 < hd ? __builtin_convertvector(load8f(Qh + qcl * qs + d0) * a.scale_log2, bf16x8) : zero8();
     if (d0 < hd) {
       const f32x8 x = load8f(dOh + qcl * qs + d0), y = load8f(Oh + qcl * qs + d0);
 #pragma unroll
@@ -432,13 +438,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   // kernel (stored after the loop, so the loop's load waits do not cover
   // them).
   const float D = dpart + __shfl_xor(dpart, 32);
-  const float nlse = -lse / a.scale, nD = -D;
+  const float nlse = -lse * kLog2e, nD = -D;
 
   f32x16 acc[2];  // dQ^T: register r of block db holds d = 32*db + 8*(r/4) + 4*h2 + r%4
 #pragma unroll
   for (int i = 0; i < 16; ++i) { acc[0][i] = 0.0f; acc[1][i] = 0.0f; }
 
-  const float sl2 = a.scale_log2;
   const int krow_base = row_perm(l32);
   // First and last rows of this wavefront; one whose rows all lie past the
   // sequence only takes part in the loads.
@@ -487,7 +492,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int r = 8 * (c & 1) + i;
-          float p = fast_exp2(s[c >> 1][r] * sl2);
+          float p = fast_exp2(s[c >> 1][r]);
           if constexpr (decltype(masked)::value) {
             const int idx = 16 * c + i;
             p = (idx >= lo && idx < hi) ? p : 0.0f;

@@ -134,7 +134,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   }
 
   // This lane's query row (column n of S^T), its position, and its Q
-  // fragments (B operand).
+  // fragments (B operand), pre-scaled by scale * log2(e) so that the score
+  // products come out in the log2 domain (one bf16 rounding of scale * q).
   const int qrow = q0 + col / hp;
   const int qpos = qoff + qrow;
   const TIn* __restrict__ Qh = (const TIn*)a.q + (long)bos * qs + hq * hd;
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int d0 = 16 * c + 8 * h2;
-      qf[c] = d0 < hd ? load8(Qh + qcl * qs + d0) : zero8();
+      qf[c] = d0 < hd ? __builtin_convertvector(load8f(Qh + qcl * qs + d0) * a.scale_log2, bf16x8) : zero8();
     }
   }
   wait_vmem_all();  // fragments resident before the loop (see wait_vmem_all)
@@ -156,15 +157,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const float sink = a.sinks[hq];
   float m = sink * kLog2e;                                          // -inf stays -inf
   float l = (h2 == 0 && sink != -__builtin_inff()) ? 1.0f : 0.0f;  // counted once per row
-  f32x16 o[2];
+  f32x16 o[2], negm;  // negm: every entry -m (0 while m = -inf), the score accumulators' seed
 #pragma unroll
-  for (int i = 0; i < 16; ++i) { o[0][i] = 0.0f; o[1][i] = 0.0f; }
+  for (int i = 0; i < 16; ++i) { o[0][i] = 0.0f; o[1][i] = 0.0f; negm[i] = (m == -__builtin_inff()) ? 0.0f : -m; }
 
   // Positions of this wavefront's first and last rows; a wavefront whose
   // rows all lie past the sequence only takes part in the loads.
   const int wq_lo = qoff + q0 + 32 * w / hp, wq_hi = qoff + q0 + (32 * w + 31) / hp;
   const bool live = q0 + 32 * w / hp < L;
-  const float sl2 = a.scale_log2;
   const int krow_base = row_perm(l32);
 
   int buf = 0;
@@ -186,23 +186,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     if (!live || kb > wq_hi) continue;                             // no rows, or all keys after all rows
     if (window > 0 && wq_lo - (kb + kBN - 1) >= window) continue;  // all keys left of window
 
-    // S^T = K Q^T for two 32-key blocks; register r of block blk holds key
+    // S^T = K Q^T - m for two 32-key blocks (log2 domain; the accumulators
+    // start from -m); register r of block blk holds key
     // kb + 32*blk + 16*(r/8) + 8*h2 + r%8 (A rows permuted).
     f32x16 s[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[blk][i] = 0.0f;
       const int kr = krow_base + 32 * blk;
+      s[blk] = mfma32(frag_row(st.k, kr, 8 * h2), qf[0], negm);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) s[blk] = mfma32(frag_row(st.k, kr, 16 * c + 8 * h2), qf[c], s[blk]);
+      for (int c = 1; c < 4; ++c) s[blk] = mfma32(frag_row(st.k, kr, 16 * c + 8 * h2), qf[c], s[blk]);
     }
 
     const bool need_mask = (kb + kBN - 1 > wq_lo) || (window > 0 && wq_hi - kb >= window);
     if (need_mask) {
       // key index 32*blk + 16*(r/8) + r%8 (+ kb + 8*h2) is visible iff lo <= idx < hi;
-      // hidden raw scores become -inf (the scale is positive, so they stay
-      // -inf through the scaling below).
+      // hidden scores become -inf.
       const int hi = qpos + 1 - kb - 8 * h2;
       const int lo = window > 0 ? hi - window : -0x7fffffff;
 #pragma unroll
@@ -214,8 +213,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         }
       }
     }
-    // Row max of the raw scores (two chains of three-way maxima), then the
-    // other half of the row, then into the log2 domain (scale > 0).
+    // Row max of the tile's shifted scores (two chains of three-way maxima),
+    // then the other half of the row.
     float mx0 = -__builtin_inff(), mx1 = -__builtin_inff();
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
@@ -223,21 +222,29 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, s[1][r]), s[1][r + 1]);
     }
     float mx = __builtin_fmaxf(mx0, mx1);
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-    // Raise a row's reference max (and rescale its accumulator) only when the
-    // row outgrew it by more than the slack; the rescale pass runs when any
-    // row of the wavefront needs it (alpha is exactly 1 for the others), so
-    // every row's result depends on that row's scores alone.
-    const bool raise = mx > m + kRescaleSlack;
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    // Raise a row's reference max (shift its scores, rescale its accumulator)
+    // only when the row outgrew it by more than the slack, or on its first
+    // finite score; the pass runs when any row of the wavefront needs it
+    // (shift 0 and alpha exactly 1 for the others), so every row's result
+    // depends on that row's scores alone.
+    const bool first = m == -__builtin_inff();
+    const bool raise = first ? (mx > -__builtin_inff()) : (mx > kRescaleSlack);
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      const float mnew = raise ? fmaxf(m, mx) : m;
-      const float alpha = fast_exp2(m - ((mnew == -__builtin_inff()) ? 0.0f : mnew));
+      const float shift = raise ? mx : 0.0f;  // while m = -inf the scores are unshifted
+      const float alpha = fast_exp2(-shift);  // l and O are still 0 while m = -inf
       l *= alpha;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) { o[0][i] *= alpha; o[1][i] *= alpha; }
-      m = mnew;
+      for (int i = 0; i < 16; ++i) {
+        o[0][i] *= alpha;
+        o[1][i] *= alpha;
+        s[0][i] -= shift;
+        s[1][i] -= shift;
+      }
+      m = raise ? (first ? mx : m + mx) : m;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) negm[i] = (m == -__builtin_inff()) ? 0.0f : -m;
     }
-    const float nmuse = (m == -__builtin_inff()) ? 0.0f : -m;
     // P = exp2(S * scale * log2 e - m) as P^T fragments (chunk c covers keys
     // 16c .. 16c+15 of the tile); the row sum adds the rounded values, two per
     // dot product, in two chains.
@@ -247,7 +254,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     for (int c = 0; c < 4; ++c) {
       f32x8 v;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = fast_exp2(__builtin_fmaf(s[c >> 1][8 * (c & 1) + i], sl2, nmuse));
+      for (int i = 0; i < 8; ++i) v[i] = fast_exp2(s[c >> 1][8 * (c & 1) + i]);
       pf[c] = __builtin_convertvector(v, bf16x8);
       ls0 = dot2_bf16(__builtin_shufflevector(pf[c], pf[c], 0, 1), ls0);
       ls1 = dot2_bf16(__builtin_shufflevector(pf[c], pf[c], 2, 3), ls1);

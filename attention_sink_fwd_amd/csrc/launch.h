@@ -38,7 +38,7 @@ struct BwdArgs {
   void* dv;
   float* dsinks;
   float* ndelta;  // workspace: -D_i = -(dO_i . O_i), [Hq, T]
-  float* nlse;    // workspace: -LSE_i / scale, [Hq, T]
+  float* nlse;    // workspace: -LSE_i log2(e), [Hq, T]
   float* dk_part;  // workspace: float dK partial sums, [P, T, Hkv, d], P = (Hq/Hkv) / dkdv_heads
   float* dv_part;  // workspace: float dV partial sums, same shape (both unused when P == 1)
   float* dsink_part;  // workspace: per-query-tile dS partials, [Hq, num_seqs, query tiles]
