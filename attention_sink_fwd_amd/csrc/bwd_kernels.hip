@@ -110,8 +110,9 @@ constexpr int kStages = 3;
 // dK and dV for one 128-key tile and `dkdv_heads` query heads of one KV
 // group.  The workgroup walks (head, query tile) steps through one LDS ring,
 // so K, V and the dK, dV accumulators stay in registers across its heads.
-// When it covers the whole group it writes dK, dV directly; otherwise its
-// partial sums go to the float accumulators with atomics.
+// When it covers the whole group it writes dK, dV directly; otherwise it
+// stores its float partial sums to its own plane, which the post kernel adds
+// to the others in a fixed order.
 template <typename TIn, bool kDirect>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // Three separate LDS objects (not an array): with every access naming its
