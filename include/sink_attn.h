@@ -97,7 +97,7 @@ typedef struct {
   const int32_t *cu_seqlens; /* device, [num_seqs + 1] */
   int32_t num_seqs;          /* >= 1 */
   int32_t max_seqlen;        /* >= every sequence length; 0 allowed only if total_tokens == 0;
-                                ceil(max_seqlen / 128) * Hq * num_seqs < 2^24 (one
+                                (ceil(max_seqlen / 128) + 1) * Hq * num_seqs < 2^24 (one
                                 workgroup per 128-row tile, head and sequence) */
   int32_t total_tokens;      /* T = cu_seqlens[num_seqs] */
   int32_t num_q_heads;       /* 1 <= Hq <= 8192 */
