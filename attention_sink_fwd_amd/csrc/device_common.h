@@ -207,25 +207,32 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Work order of the tiled kernels (1-D launch of n = tiles * heads * seqs
-// workgroups; units count head-major, then sequence, then tile rank).  The
-// dispatcher places workgroup b on XCD b % 8, and each XCD has its own L2.
-// When the heads split evenly over the 8 XCDs, workgroup b takes unit
-//   u = x * (n / 8) + b / 8,   x = b % 8,
-// so every XCD runs whole heads (tiles that share Q, dO or K, V hit one L2)
-// with equal work.  Otherwise u = b: tiles of every head are dealt round-robin
-// over the XCDs, which keeps the work even at the cost of L2 sharing.
+// workgroups).  The dispatcher places workgroup b on XCD b % 8, and each XCD
+// has its own L2.  When the heads split evenly over the 8 XCDs, XCD x owns
+// heads [x * H/8, (x+1) * H/8) (tiles that share K, V or Q, dO hit one L2)
+// and its workgroups b = x + 8 i take, in order of i: sequence after
+// sequence; within a sequence, tile rank after tile rank (rank 0 is each
+// kernel's heaviest tile); within a rank, head after head.  So every head's
+// heavy tiles start first and the light ones fill the end: ordering by head
+// first (all ranks of one head, then the next) left the last heads' heavy
+// tiles for the end of the launch, a tail that cost the dK/dV kernel 12 % at
+// one 4096-token sequence.  Otherwise (heads not a multiple of 8) the same
+// order runs over the whole grid, dealt round-robin over the XCDs.
 struct TileUnit {
   int head, seq, rank;
 };
 __device__ __forceinline__ TileUnit xcd_unit(int num_heads, int num_seqs) {
   const int b = blockIdx.x, n = gridDim.x;
-  const int u = (num_heads & 7) == 0 ? (b & 7) * (n >> 3) + (b >> 3) : b;
   const int tiles = n / (num_heads * num_seqs);
+  const bool split = (num_heads & 7) == 0;
+  const int hx = split ? num_heads >> 3 : num_heads;  // heads of this XCD's share
+  const int i = split ? b >> 3 : b;                   // dispatch index within the share
+  const int per_seq = tiles * hx;
   TileUnit t;
-  t.rank = u % tiles;
-  const int r = u / tiles;
-  t.seq = r % num_seqs;
-  t.head = r / num_seqs;
+  t.seq = i / per_seq;
+  const int r = i - t.seq * per_seq;
+  t.rank = r / hx;
+  t.head = (split ? (b & 7) * hx : 0) + r % hx;
   return t;
 }
 
