@@ -157,9 +157,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const float sink = a.sinks[hq];
   float m = sink * kLog2e;                                          // -inf stays -inf
   float l = (h2 == 0 && sink != -__builtin_inff()) ? 1.0f : 0.0f;  // counted once per row
-  f32x16 o[2], negm;  // negm: every entry -m (0 while m = -inf), the score accumulators' seed
+  f32x16 o[2];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) { o[0][i] = 0.0f; o[1][i] = 0.0f; negm[i] = (m == -__builtin_inff()) ? 0.0f : -m; }
+  for (int i = 0; i < 16; ++i) { o[0][i] = 0.0f; o[1][i] = 0.0f; }
+  float nm = (m == -__builtin_inff()) ? 0.0f : -m;  // the score accumulators' seed
 
   // Positions of this wavefront's first and last rows; a wavefront whose
   // rows all lie past the sequence only takes part in the loads.
@@ -190,6 +191,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     // start from -m); register r of block blk holds key
     // kb + 32*blk + 16*(r/8) + 8*h2 + r%8 (A rows permuted).
     f32x16 s[2];
+    f32x16 negm;  // built per tile: a loop-long copy would cost a wave of occupancy
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negm[i] = nm;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int kr = krow_base + 32 * blk;
@@ -242,8 +246,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         s[1][i] -= shift;
       }
       m = raise ? (first ? mx : m + mx) : m;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) negm[i] = (m == -__builtin_inff()) ? 0.0f : -m;
+      nm = (m == -__builtin_inff()) ? 0.0f : -m;
     }
     // P = exp2(S * scale * log2 e - m) as P^T fragments (chunk c covers keys
     // 16c .. 16c+15 of the tile); the row sum adds the rounded values, two per
