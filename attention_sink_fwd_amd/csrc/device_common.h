@@ -152,6 +152,19 @@ __device__ __forceinline__ void lds_dma16(const void* g, const void* lds_base) {
   const unsigned m0 = (unsigned)(uintptr_t)(SA_LDS const void*)lds_base;
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
 }
+// Same load with the global address split into a wavefront-uniform 64-bit
+// base (SGPR pair) and a 32-bit per-lane byte offset: the offsets of a tile's
+// rows can then stay fixed across a loop while only the scalar base moves.
+__device__ __forceinline__ void lds_dma16_s(uint32_t voff, const void* sbase, const void* lds_base) {
+  const unsigned m0 = (unsigned)(uintptr_t)(SA_LDS const void*)lds_base;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4_s(uint32_t voff, const void* sbase, const void* lds_base) {
+  const unsigned m0 = (unsigned)(uintptr_t)(SA_LDS const void*)lds_base;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void lds_dma4(const void* g, const void* lds_base) {
   const unsigned m0 = (unsigned)(uintptr_t)(SA_LDS const void*)lds_base;
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory", "m0");

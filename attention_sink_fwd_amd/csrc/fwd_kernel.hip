@@ -20,13 +20,15 @@
 // from the row-major V tile through transposing LDS reads.  The epilogue
 // writes O = acc / l and LSE = m + ln(l) (natural log, sink included).
 //
-// A row's reference max m is only raised when a tile's max exceeds it by
-// more than kRescaleSlack (log2 units); otherwise the tile is exponentiated
-// against the old m (values up to 2^kRescaleSlack), and when no row of the
-// wavefront needs it the 32-register accumulator rescale is skipped.  The
-// result is the same softmax: m cancels between O's numerator and l.  The
-// decision is per row, so a row's bits do not depend on the other rows that
-// share its wavefront.
+// A row's reference max m is only raised when the tile's exponentials at the
+// old m sum to 2^7 or more over either half of the row (32 keys); otherwise
+// the tile is used at the old m.  The result is the same softmax: m cancels
+// between O's numerator and l.  The common case needs no row maximum: the
+// exponentials and their half-row sums are formed first, and only a
+// wavefront with a row to raise does more.  A raise moves m up by an integer
+// (the ceiling of log2 of the row's largest P), so rescaling P, l and O is
+// exact.  Every decision depends on the row alone, so a row's bits do not
+// depend on the other rows that share its wavefront.
 #include <type_traits>
 
 #include "device_common.h"
@@ -39,8 +41,11 @@ namespace {
 constexpr int kBM = 128;  // query rows per workgroup
 constexpr int kBN = 64;   // keys per LDS tile
 constexpr int kD = 64;    // padded head dimension
-constexpr int kStages = 2;
-constexpr float kRescaleSlack = 8.0f;
+constexpr float kHalfSumLimit = 128.0f;  // a half row's sum over a tile (old m) that raises m
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
 
 struct __attribute__((aligned(16))) KVStage {
   bf16 k[kBN * kD];  // K tile, swizzled [key][d]
@@ -52,8 +57,10 @@ struct __attribute__((aligned(16))) KVStage {
 // tokens of the sequence itself (query row i at position i).  The arithmetic
 // per query row is the same in both, so a row gets the same bits either way.
 template <typename TIn, bool kDirect, bool kPaged>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
-  __shared__ KVStage stage[kStages];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDirect ? 4 : 2))) void fwd_kernel(FwdArgs a) {
+  // Two-stage ring; the loop is unrolled by two, so every access names its
+  // stage at compile time and LDS addresses fold into instruction offsets.
+  __shared__ KVStage stage[2];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
@@ -111,27 +118,59 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     return (long)min(max(pid, 0), a.num_pages - 1) * a.page_size + k0_next % a.page_size;
   };
 
-  // Prefetch key tile t (clamped to the last tile) into stage buf; on the
-  // direct path exactly 4 VMEM instructions per wavefront.
-  auto prefetch = [&](int t, int buf) {
+  // Direct loads: this wavefront stages rows 16 w .. 16 w + 15 of each tile
+  // (two 8-row blocks); lane l moves 16 bytes of row r = 8 blk + l / 8 into
+  // its swizzled slot.  The byte offsets within a full tile are fixed for the
+  // whole loop; only the tile's base address (scalar) moves.
+  uint32_t voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * (2 * w + i) + (lane >> 3);
+    voff[i] = (uint32_t)(r * ks + 8 * ((lane & 7) ^ swz_f(r))) * (uint32_t)sizeof(bf16);
+  }
+
+  // Prefetch key tile t (clamped to the last tile) into `st`; on the direct
+  // path exactly 4 VMEM instructions per wavefront.  Rows past the keys of
+  // the sequence repeat its last key (they are masked).
+  auto prefetch = [&](int t, KVStage& st) {
     const int k0 = min(t, t1 - 1) * kBN;
-    KVStage& st = stage[buf];
-    const long prow = kPaged ? page_row() : 0;
-    const TIn* kb = kPaged ? Kg + prow * ks : Kg;
-    const TIn* vb = kPaged ? Vg + prow * ks : Vg;
-    const int row0 = kPaged ? 0 : k0, nvalid = kPaged ? kvlen - k0 : kvlen;
+    const long prow = kPaged ? page_row() : (long)k0;  // row of the tile's first key
+    const int rem = kvlen - k0;                        // keys from the tile's first on
     if constexpr (kDirect) {
-      stage_direct<kBN>(st.k, (const bf16*)kb, row0, nvalid, ks, w, lane);
-      stage_direct<kBN>(st.v, (const bf16*)vb, row0, nvalid, ks, w, lane);
+      const bf16* kb = (const bf16*)Kg + prow * ks;
+      const bf16* vb = (const bf16*)Vg + prow * ks;
+      if (rem >= kBN) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) lds_dma16_s(voff[i], kb, st.k + 512 * (2 * w + i));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) lds_dma16_s(voff[i], vb, st.v + 512 * (2 * w + i));
+      } else {
+        // rows r >= rem read row rem - 1 instead: r - (rem - 1) rows fewer
+        uint32_t cl[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int over = 8 * (2 * w + i) + (lane >> 3) - (rem - 1);
+          cl[i] = voff[i] - (uint32_t)(max(over, 0) * ks) * (uint32_t)sizeof(bf16);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) lds_dma16_s(cl[i], kb, st.k + 512 * (2 * w + i));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) lds_dma16_s(cl[i], vb, st.v + 512 * (2 * w + i));
+      }
     } else {
-      stage_regs<kBN>(st.k, kb, row0, nvalid, ks, hd, tid);
-      stage_regs<kBN>(st.v, vb, row0, nvalid, ks, hd, tid);
+      stage_regs<kBN>(st.k, Kg + prow * ks, 0, rem, ks, hd, tid);
+      stage_regs<kBN>(st.v, Vg + prow * ks, 0, rem, ks, hd, tid);
     }
     if constexpr (kPaged) load_page(t + 1);
   };
   if constexpr (kPaged) {
     if (t0 < t1) load_page(t0);
   }
+
+  // The first tile is requested before the Q fragments, so the two loads
+  // overlap.
+  if (t0 < t1) prefetch(t0, stage[0]);
+  issue_fence();
 
   // This lane's query row (column n of S^T), its position, and its Q
   // fragments (B operand), pre-scaled by scale * log2(e) so that the score
@@ -148,9 +187,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       qf[c] = d0 < hd ? __builtin_convertvector(load8f(Qh + qcl * qs + d0) * a.scale_log2, bf16x8) : zero8();
     }
   }
-  wait_vmem_all();  // fragments resident before the loop (see wait_vmem_all)
-  issue_fence();
-  if (t0 < t1) prefetch(t0, 0);
+  wait_vmem_all();  // fragments and the first tile resident before the loop (see wait_vmem_all)
   issue_fence();
 
   // Online softmax state in the log2 domain, seeded with the sink.
@@ -168,103 +205,162 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const bool live = q0 + 32 * w / hp < L;
   const int krow_base = row_perm(l32);
 
-  int buf = 0;
-  for (int t = t0; t < t1; ++t) {
+  // One key tile: consume `st`, prefetch the next tile into `nx` (the stage
+  // consumed one tile earlier).
+  auto tile = [&](int t, const KVStage& st, KVStage& nx) {
     // This wavefront's part of tile t has landed; the barrier makes every
-    // part visible and ends all reads of the stage the next prefetch
-    // overwrites (tile t-1).
+    // part visible and ends all reads of `nx` (tile t-1).
     if constexpr (kDirect) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    {
-      int nb = buf + 1;
-      if (nb >= kStages) nb -= kStages;
-      prefetch(t + 1, nb);
-      issue_fence();
-    }
-    const KVStage& st = stage[buf];
-    if (++buf == kStages) buf = 0;
+    prefetch(t + 1, nx);
+    issue_fence();
     const int kb = t * kBN;
-    if (!live || kb > wq_hi) continue;                             // no rows, or all keys after all rows
-    if (window > 0 && wq_lo - (kb + kBN - 1) >= window) continue;  // all keys left of window
+    if (!live || kb > wq_hi) return;                             // no rows, or all keys after all rows
+    if (window > 0 && wq_lo - (kb + kBN - 1) >= window) return;  // all keys left of window
 
     // S^T = K Q^T - m for two 32-key blocks (log2 domain; the accumulators
     // start from -m); register r of block blk holds key
-    // kb + 32*blk + 16*(r/8) + 8*h2 + r%8 (A rows permuted).
-    f32x16 s[2];
-    f32x16 negm;  // built per tile: a loop-long copy would cost a wave of occupancy
-#pragma unroll
-    for (int i = 0; i < 16; ++i) negm[i] = nm;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int kr = krow_base + 32 * blk;
-      s[blk] = mfma32(frag_row(st.k, kr, 8 * h2), qf[0], negm);
-#pragma unroll
-      for (int c = 1; c < 4; ++c) s[blk] = mfma32(frag_row(st.k, kr, 16 * c + 8 * h2), qf[c], s[blk]);
-    }
-
+    // kb + 32*blk + 16*(r/8) + 8*h2 + r%8 (A rows permuted).  Hidden scores
+    // are -inf.
     const bool need_mask = (kb + kBN - 1 > wq_lo) || (window > 0 && wq_hi - kb >= window);
-    if (need_mask) {
-      // key index 32*blk + 16*(r/8) + r%8 (+ kb + 8*h2) is visible iff lo <= idx < hi;
-      // hidden scores become -inf.
-      const int hi = qpos + 1 - kb - 8 * h2;
-      const int lo = window > 0 ? hi - window : -0x7fffffff;
+    f32x16 s[2];
+    auto scores = [&]() {
+      f32x16 negm;  // built per tile: a loop-long copy would cost a wave of occupancy
+#pragma unroll
+      for (int i = 0; i < 16; ++i) negm[i] = nm;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
+        const int kr = krow_base + 32 * blk;
+        s[blk] = mfma32(frag_row(st.k, kr, 8 * h2), qf[0], negm);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int idx = 32 * blk + 16 * (r >> 3) + (r & 7);
-          s[blk][r] = (idx >= lo && idx < hi) ? s[blk][r] : -__builtin_inff();
+        for (int c = 1; c < 4; ++c) s[blk] = mfma32(frag_row(st.k, kr, 16 * c + 8 * h2), qf[c], s[blk]);
+      }
+      if (need_mask) {
+        // key index 32*blk + 16*(r/8) + r%8 (+ kb + 8*h2) is visible iff lo <= idx < hi
+        const int hi = qpos + 1 - kb - 8 * h2;
+        const int lo = window > 0 ? hi - window : -0x7fffffff;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int idx = 32 * blk + 16 * (r >> 3) + (r & 7);
+            s[blk][r] = (idx >= lo && idx < hi) ? s[blk][r] : -__builtin_inff();
+          }
         }
       }
-    }
-    // Row max of the tile's shifted scores (two chains of three-way maxima),
-    // then the other half of the row.
-    float mx0 = -__builtin_inff(), mx1 = -__builtin_inff();
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      mx0 = __builtin_fmaxf(__builtin_fmaxf(mx0, s[0][r]), s[0][r + 1]);
-      mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, s[1][r]), s[1][r + 1]);
-    }
-    float mx = __builtin_fmaxf(mx0, mx1);
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-    // Raise a row's reference max (shift its scores, rescale its accumulator)
-    // only when the row outgrew it by more than the slack, or on its first
-    // finite score; the pass runs when any row of the wavefront needs it
-    // (shift 0 and alpha exactly 1 for the others), so every row's result
-    // depends on that row's scores alone.
-    const bool first = m == -__builtin_inff();
-    const bool raise = first ? (mx > -__builtin_inff()) : (mx > kRescaleSlack);
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      const float shift = raise ? mx : 0.0f;  // while m = -inf the scores are unshifted
-      const float alpha = fast_exp2(-shift);  // l and O are still 0 while m = -inf
-      l *= alpha;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        o[0][i] *= alpha;
-        o[1][i] *= alpha;
-        s[0][i] -= shift;
-        s[1][i] -= shift;
-      }
-      m = raise ? (first ? mx : m + mx) : m;
-      nm = (m == -__builtin_inff()) ? 0.0f : -m;
-    }
+    };
     // P = exp2(S * scale * log2 e - m) as P^T fragments (chunk c covers keys
-    // 16c .. 16c+15 of the tile); the row sum adds the rounded values, two per
-    // dot product, in two chains.
+    // 16c .. 16c+15 of the tile); this half row's sum adds the rounded values,
+    // two per dot product, in two chains.
     bf16x8 pf[4];
-    float ls0 = 0.0f, ls1 = 0.0f;
+    float ls;
+    auto exponentiate = [&]() {
+      float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      f32x8 v;
+      for (int c = 0; c < 4; ++c) {
+        f32x8 v;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = fast_exp2(s[c >> 1][8 * (c & 1) + i]);
-      pf[c] = __builtin_convertvector(v, bf16x8);
-      ls0 = dot2_bf16(__builtin_shufflevector(pf[c], pf[c], 0, 1), ls0);
-      ls1 = dot2_bf16(__builtin_shufflevector(pf[c], pf[c], 2, 3), ls1);
-      ls0 = dot2_bf16(__builtin_shufflevector(pf[c], pf[c], 4, 5), ls0);
-      ls1 = dot2_bf16(__builtin_shufflevector(pf[c], pf[c], 6, 7), ls1);
+        for (int i = 0; i < 8; ++i) v[i] = fast_exp2(s[c >> 1][8 * (c & 1) + i]);
+        pf[c] = __builtin_convertvector(v, bf16x8);
+        ls0 = dot2_bf16(__builtin_shufflevector(pf[c], pf[c], 0, 1), ls0);
+        ls1 = dot2_bf16(__builtin_shufflevector(pf[c], pf[c], 2, 3), ls1);
+        ls0 = dot2_bf16(__builtin_shufflevector(pf[c], pf[c], 4, 5), ls0);
+        ls1 = dot2_bf16(__builtin_shufflevector(pf[c], pf[c], 6, 7), ls1);
+      }
+      ls = ls0 + ls1;
+    };
+    scores();
+    exponentiate();
+    // Raising a row.  A row is raised when either half of it sums to
+    // kHalfSumLimit or more over the tile at the old m: its P values, l, O
+    // and m are then shifted by k = ceil(log2 of its largest P), an integer,
+    // so the shift is an exact power of two and applies to the bf16 P bits
+    // directly (exponent field minus k; values that would leave the normal
+    // range become 0).  Rows whose reference is still -inf (sink -inf, first
+    // finite score) or whose tile overflowed (an infinite or NaN P) are
+    // shifted by their exact tile maximum instead, which needs the scores
+    // again (the tile is still in LDS; keeping the scores live would cost a
+    // wave of occupancy).  Every decision depends on the row alone; a
+    // wavefront in which no row qualifies skips all of this.
+    if (__builtin_amdgcn_ballot_w64(m == -__builtin_inff() || !(ls < kHalfSumLimit)) != 0) {
+      // Largest P of the row as bf16 bits (non-negative values order like
+      // their bit patterns).
+      auto row_pmax = [&]() -> unsigned {
+        // (Each vector element is copied to a scalar before its bit cast:
+        // this compiler's bit cast of a vector element reads element 0.)
+        u16x2 mx2 = {0, 0};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const u32x4 d = __builtin_bit_cast(u32x4, pf[c]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const unsigned x = d[e];
+            mx2 = __builtin_elementwise_max(mx2, __builtin_bit_cast(u16x2, x));
+          }
+        }
+        const unsigned pm = mx2[0] > mx2[1] ? mx2[0] : mx2[1];
+        const unsigned po = (unsigned)__shfl_xor((int)pm, 32);
+        return pm > po ? pm : po;
+      };
+      unsigned pm = row_pmax();
+      const bool exact = m == -__builtin_inff() || pm >= 0x7f80u;
+      if (__builtin_amdgcn_ballot_w64(exact) != 0) {
+        issue_fence();  // forces the tile to be read again (no copy of the scores kept live)
+        scores();       // the same values as before
+        float mx0 = -__builtin_inff(), mx1 = -__builtin_inff();
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          mx0 = __builtin_fmaxf(__builtin_fmaxf(mx0, s[0][r]), s[0][r + 1]);
+          mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, s[1][r]), s[1][r + 1]);
+        }
+        float mx = __builtin_fmaxf(mx0, mx1);
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+        const bool first = m == -__builtin_inff();
+        const bool raise = exact && mx > -__builtin_inff();
+        const float shift = raise ? mx : 0.0f;  // while m = -inf the scores are unshifted
+        const float alpha = fast_exp2(-shift);  // l and O are still 0 while m = -inf
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          o[0][i] *= alpha;
+          o[1][i] *= alpha;
+          s[0][i] -= shift;
+          s[1][i] -= shift;
+        }
+        m = raise ? (first ? mx : m + mx) : m;
+        nm = (m == -__builtin_inff()) ? 0.0f : -m;
+        exponentiate();  // same values for the other rows
+        pm = row_pmax();
+      }
+      const float lhalf = __builtin_fmaxf(ls, __shfl_xor(ls, 32));
+      const int k = (int)(pm >> 7) - 127 + ((pm & 0x7fu) != 0u);  // ceil(log2(largest P))
+      const int kk = !(lhalf < kHalfSumLimit) ? k : 0;
+      if (__builtin_amdgcn_ballot_w64(kk != 0) != 0) {
+        const float alpha = __builtin_ldexpf(1.0f, -kk);
+        l *= alpha;
+        ls *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          o[0][i] *= alpha;
+          o[1][i] *= alpha;
+        }
+        const short sub = (short)(kk << 7);
+        const i16x2 sub2 = {sub, sub}, zero2 = {0, 0};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          u32x4 d = __builtin_bit_cast(u32x4, pf[c]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const unsigned x = d[e];
+            d[e] = __builtin_bit_cast(unsigned, __builtin_elementwise_max(__builtin_bit_cast(i16x2, x) - sub2, zero2));
+          }
+          pf[c] = __builtin_bit_cast(bf16x8, d);
+        }
+        m += (float)kk;
+        nm = -m;
+      }
     }
-    l += ls0 + ls1;
+    l += ls;
 
     // O^T += V^T P^T.
 #pragma unroll
@@ -272,6 +368,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) o[db] = mfma32(frag_tr_swz(st.v, 16 * c, 32 * db, lane), pf[c], o[db]);
     }
+  };
+  for (int t = t0; t < t1; t += 2) {
+    tile(t, stage[0], stage[1]);
+    if (t + 1 < t1) tile(t + 1, stage[1], stage[0]);
   }
 
   const float lt = l + __shfl_xor(l, 32);
