@@ -395,18 +395,48 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int kbeg = window > 0 ? max(0, q0 - window + 1) : 0;
   const int t0 = kbeg / kKT, t1 = (kend + kKT - 1) / kKT;
 
-  // Direct path: 2 + 2 VMEM instructions per wavefront per key tile.
-  auto prefetch = [&](int t, int buf) {
+  // Direct loads: this wavefront stages rows 16 w .. 16 w + 15 of each tile
+  // (two 8-row blocks); lane l moves 16 bytes of row r = 8 blk + l / 8 into
+  // its swizzled slot.  The byte offsets within a full tile are fixed for the
+  // whole loop; only the tile's base address (scalar) moves.
+  uint32_t voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * (2 * w + i) + (lane >> 3);
+    voff[i] = (uint32_t)(r * ks + 8 * ((lane & 7) ^ swz_f(r))) * (uint32_t)sizeof(bf16);
+  }
+  // Prefetch key tile t (clamped to the last tile) into `st`.  Direct path:
+  // 2 + 2 VMEM instructions per wavefront; rows past the sequence repeat its
+  // last key (they are masked).
+  auto prefetch = [&](int t, KStage& st) {
     const int k0 = min(t, t1 - 1) * kKT;
-    KStage& st = stage[buf];
+    const int rem = L - k0;  // keys from the tile's first on
     if constexpr (kDirect) {
-      stage_direct<kKT>(st.k, (const bf16*)Kg, k0, L, ks, w, lane);
-      stage_direct<kKT>(st.v, (const bf16*)Vg, k0, L, ks, w, lane);
+      const bf16* kb = (const bf16*)Kg + (long)k0 * ks;
+      const bf16* vb = (const bf16*)Vg + (long)k0 * ks;
+      uint32_t off[2] = {voff[0], voff[1]};
+      if (rem < kKT) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int over = 8 * (2 * w + i) + (lane >> 3) - (rem - 1);
+          off[i] = voff[i] - (uint32_t)(max(over, 0) * ks) * (uint32_t)sizeof(bf16);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) lds_dma16_s(off[i], kb, st.k + 512 * (2 * w + i));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) lds_dma16_s(off[i], vb, st.v + 512 * (2 * w + i));
     } else {
       stage_regs<kKT>(st.k, Kg, k0, L, ks, hd, tid);
       stage_regs<kKT>(st.v, Vg, k0, L, ks, hd, tid);
     }
   };
+  // The first two tiles are requested before the row fragments, so the
+  // loads overlap.
+  prefetch(t0, stage[0]);
+  issue_fence();
+  prefetch(t0 + 1, stage[1]);
+  issue_fence();
 
   // This lane's query row (column n of the transposed products) and its Q and
   // dO fragments (B operands); the lane holds half of the row's d values.
@@ -429,11 +459,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       of[c] = zero8();
     }
   }
-  wait_vmem_all();  // fragments resident before the loop (see wait_vmem_all)
-  issue_fence();
-  prefetch(t0, 0);
-  issue_fence();
-  prefetch(t0 + 1, 1);
+  wait_vmem_all();  // fragments and the first two tiles resident (see wait_vmem_all)
   issue_fence();
   // Row statistics: the accumulator seeds of this kernel and of the dK/dV
   // kernel (stored after the loop, so the loop's load waits do not cover
@@ -451,21 +477,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int wq_lo = q0 + 32 * w / hp, wq_hi = q0 + (32 * w + 31) / hp;
   const bool live = wq_lo < L;
 
-  int buf = 0;
-  for (int t = t0; t < t1; ++t) {
+  // One key tile: consume `st`, prefetch tile t + 2 into `nx` (the stage
+  // consumed one tile earlier).
+  auto step = [&](int t, const KStage& st, KStage& nx) {
+    // Only tile t + 1 may still be in flight; the barrier makes tile t
+    // visible and ends every read of `nx`.
     if constexpr (kDirect) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     lds_barrier();
-    {
-      int nb = buf + 2;
-      if (nb >= kStages) nb -= kStages;
-      prefetch(t + 2, nb);
-      issue_fence();
-    }
-    const KStage& st = stage[buf];
+    prefetch(t + 2, nx);
+    issue_fence();
     const int kb = t * kKT;
-    if (++buf == kStages) buf = 0;
-    if (!live || kb > wq_hi) continue;                             // no rows, or all keys after all rows
-    if (window > 0 && wq_lo - (kb + kKT - 1) >= window) continue;  // all keys left of window
+    if (!live || kb > wq_hi) return;                             // no rows, or all keys after all rows
+    if (window > 0 && wq_lo - (kb + kKT - 1) >= window) return;  // all keys left of window
 
     // S^T and dP^T for two 32-key blocks; register r of block blk holds key
     // kb + 32*blk + 16*(r/8) + 8*h2 + r%8 (A rows permuted).
@@ -513,6 +536,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[db] = mfma32(frag_tr_swz(st.k, 16 * c, 32 * db, lane), df[c], acc[db]);
     }
+  };
+  // Unrolled by the ring size, so every stage is named at compile time.
+  for (int t = t0; t < t1; t += kStages) {
+    step(t, stage[0], stage[2]);
+    if (t + 1 < t1) step(t + 1, stage[1], stage[0]);
+    if (t + 2 < t1) step(t + 2, stage[2], stage[1]);
   }
 
   // Statistics for the dK/dV kernel, and the sink's softmax-Jacobian entry
