@@ -154,15 +154,42 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // Prefetch cursor: head pj, query tile pt of step pf; it stops at the last
   // step, so the ring's look-ahead past the end re-loads that tile.
   int pf = 0, pj = 0, pt = qt0;
-  // Direct path: exactly kPrefetchOps VMEM instructions per wavefront.
+  // Direct loads: this wavefront stages rows 16 w .. 16 w + 15 of the Q and
+  // dO tiles (two 8-row blocks; lane l moves 16 bytes of row 8 blk + l / 8
+  // into its swizzled slot) and one statistics row; the byte offsets within
+  // a full tile are fixed for the whole loop, only the tile's base address
+  // (scalar) moves.
+  uint32_t voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * (2 * w + i) + (lane >> 3);
+    voff[i] = (uint32_t)(r * qs + 8 * ((lane & 7) ^ swz_f(r))) * (uint32_t)sizeof(bf16);
+  }
+  // Direct path: exactly kPrefetchOps VMEM instructions per wavefront.  Rows
+  // past the sequence repeat its last row (they are masked).
   auto prefetch = [&](QStage& st) {
     const int q0 = pt * kBM;
     if constexpr (kDirect) {
-      stage_direct<kBM>(st.q, (const bf16*)Qh + pj * hd, q0, L, qs, w, lane);
-      stage_direct<kBM>(st.dout, (const bf16*)dOh + pj * hd, q0, L, qs, w, lane);
-      const float* src = ((w == 1) ? nD_h : nlse_h) + (long)pj * T;
+      const int rem = L - q0;  // rows from the tile's first on
+      const bf16* qb = (const bf16*)Qh + pj * hd + (long)q0 * qs;
+      const bf16* ob = (const bf16*)dOh + pj * hd + (long)q0 * qs;
+      uint32_t off[2] = {voff[0], voff[1]};
+      uint32_t soff = (uint32_t)lane * (uint32_t)sizeof(float);
+      if (rem < kBM) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int over = 8 * (2 * w + i) + (lane >> 3) - (rem - 1);
+          off[i] = voff[i] - (uint32_t)(max(over, 0) * qs) * (uint32_t)sizeof(bf16);
+        }
+        soff = (uint32_t)min(lane, rem - 1) * (uint32_t)sizeof(float);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) lds_dma16_s(off[i], qb, st.q + 512 * (2 * w + i));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) lds_dma16_s(off[i], ob, st.dout + 512 * (2 * w + i));
+      const float* src = ((w == 1) ? nD_h : nlse_h) + (long)pj * T + q0;
       float* dst = (w == 0) ? st.nlse : (w == 1 ? st.ndelta : st.spare);
-      lds_dma4(src + min(q0 + lane, L - 1), dst);
+      lds_dma4_s(soff, src, dst);
     } else {
       stage_regs<kBM>(st.q, Qh + pj * hd, q0, L, qs, hd, tid);
       stage_regs<kBM>(st.dout, dOh + pj * hd, q0, L, qs, hd, tid);
@@ -181,6 +208,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
+  // The first two query tiles are requested before the K and V fragments,
+  // so the loads overlap.
+  prefetch(st0);
+  issue_fence();
+  prefetch(st1);
+  issue_fence();
+
   // This wavefront's K and V fragments: B operands of S = Q K^T and
   // dP = dO V^T (lane = key column, 8 consecutive d per register group).
   const int wk_lo = k0 + 32 * w, wk_hi = wk_lo + 31;
@@ -195,11 +229,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       vf[c] = d0 < hd ? load8(Vg + krow * ks + d0) : zero8();
     }
   }
-  wait_vmem_all();  // fragments resident before the loop (see wait_vmem_all)
-  issue_fence();
-  prefetch(st0);
-  issue_fence();
-  prefetch(st1);
+  wait_vmem_all();  // fragments and the first two tiles resident (see wait_vmem_all)
   issue_fence();
 
   f32x16 dk[2], dv[2];
