@@ -225,9 +225,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDirect ? 4
     const bool need_mask = (kb + kBN - 1 > wq_lo) || (window > 0 && wq_hi - kb >= window);
     f32x16 s[2];
     auto scores = [&]() {
-      f32x16 negm;  // built per tile: a loop-long copy would cost a wave of occupancy
+      // Built per tile (a loop-long copy would cost a wave of occupancy), by
+      // 64-bit moves of a pair holding -m twice.
+      typedef double f64x8 __attribute__((ext_vector_type(8)));
+      const unsigned nmb = __builtin_bit_cast(unsigned, nm);
+      const double nm2 = __builtin_bit_cast(double, ((unsigned long long)nmb << 32) | nmb);
+      f64x8 negm2;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) negm[i] = nm;
+      for (int i = 0; i < 8; ++i) {
+        double x;
+        asm volatile("v_mov_b64 %0, %1" : "=v"(x) : "v"(nm2));
+        negm2[i] = x;
+      }
+      const f32x16 negm = __builtin_bit_cast(f32x16, negm2);
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         const int kr = krow_base + 32 * blk;
