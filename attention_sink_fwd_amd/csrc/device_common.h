@@ -189,13 +189,13 @@ __device__ __forceinline__ void stage_direct(bf16* tile, const bf16* g, int row0
 }
 
 // Same tile through registers: any input type, zero for rows >= nvalid and
-// columns >= hd.
-template <int kRows, typename TIn>
+// columns >= hd; kThreads lanes share the tile.
+template <int kRows, typename TIn, int kThreads = 256>
 __device__ __forceinline__ void stage_regs(bf16* tile, const TIn* g, int row0, int nvalid, int stride, int hd,
                                            int tid) {
 #pragma unroll
-  for (int i = 0; i < kRows / 32; ++i) {
-    const int c = tid + 256 * i;
+  for (int i = 0; i < kRows * 8 / kThreads; ++i) {
+    const int c = tid + kThreads * i;
     const int r = c >> 3, j = (c & 7) ^ swz_f(r);
     const bool ok = row0 + r < nvalid && 8 * j < hd;
     *(bf16x8*)(tile + 8 * c) = ok ? load8(g + (row0 + r) * stride + 8 * j) : zero8();

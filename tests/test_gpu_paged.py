@@ -109,3 +109,35 @@ def test_paged_decode_full_size_bits_and_sampled_oracle():
     got_o = o[:, heads].double().cpu().numpy()
     got_l = lse[heads].double().cpu().numpy()
     assert max_abs(got_o, o_ref) <= TOL_O and max_abs(got_l, lse_ref) <= TOL_LSE
+
+
+@pytest.mark.parametrize("d,window,dtype", [(64, 0, "bf16"), (64, 500, "bf16"), (40, 0, "f32")])
+def test_long_sequence_forward_bits_and_sampled_oracle(d, window, dtype):
+    """A batch whose longest sequence reaches 16384 tokens runs the training
+    forward with eight wavefronts per workgroup (the paged forward keeps
+    four): the rows must still match the paged forward bit for bit, and
+    sampled rows the oracle."""
+    import attention_sink_fwd_amd as sa
+
+    lengths, q_lens = (16400, 37), (300, 37)
+    w = custom_workload(lengths, 4, 2, d, window, dtype)
+    say("case long forward", lengths, d, window, dtype)
+    inp = make_inputs(w, seed=16400 + d + window)
+    dev = {k: v.to("cuda:0") for k, v in inp.items()}
+    o_t, lse_t = sa.sink_attn_fwd(dev["q"], dev["k"], dev["v"], dev["sinks"], dev["cu_seqlens"],
+                                  w.max_seqlen, w.softmax_scale, window)
+    pg = make_paged(inp, q_lens, 64, seed=17)
+    o, lse = _run(pg, w)
+    rows = pg["rows"].to("cuda:0")
+    assert torch.equal(o, o_t[rows]) and torch.equal(lse, lse_t[:, rows])
+    sample = np.array([0, 1, 63, 64, 255, 256, 8191, 16383, 16384, 16398, 16399])
+    got_o = o_t.double().cpu().numpy()
+    got_l = lse_t.double().cpu().numpy()
+    e_o = e_l = 0.0
+    for h in (0, 3):
+        o_r, l_r = oracle.forward_rows(inp["q"], inp["k"], inp["v"], inp["sinks"], inp["cu_seqlens"],
+                                       w.softmax_scale, window, 0, h, sample)
+        e_o = max(e_o, max_abs(got_o[sample, h], o_r))
+        e_l = max(e_l, max_abs(got_l[h, sample], l_r))
+    say(f"  sampled rows: o={e_o:.2e} lse={e_l:.2e}")
+    assert e_o <= TOL_O and e_l <= TOL_LSE
