@@ -289,11 +289,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
     // so the shift is an exact power of two and applies to the bf16 P bits
     // directly (exponent field minus k; values that would leave the normal
     // range become 0).  Rows whose reference is still -inf (sink -inf, first
-    // finite score) or whose tile overflowed (an infinite or NaN P) are
-    // shifted by their exact tile maximum instead, which needs the scores
-    // again (the tile is still in LDS; keeping the scores live would cost a
-    // wave of occupancy).  Every decision depends on the row alone; a
-    // wavefront in which no row qualifies skips all of this.
+    // finite score) or whose tile overflowed (an infinite or NaN P, or a
+    // half-row sum past the float range) are shifted by their exact tile
+    // maximum instead, which needs the scores again (the tile is still in
+    // LDS; keeping the scores live would cost a wave of occupancy).  Every
+    // decision depends on the row alone; a wavefront in which no row
+    // qualifies skips all of this.
     if (__builtin_amdgcn_ballot_w64(m == -__builtin_inff() || !(ls < kHalfSumLimit)) != 0) {
       // Largest P of the row as bf16 bits (non-negative values order like
       // their bit patterns).
@@ -315,7 +316,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
         return pm > po ? pm : po;
       };
       unsigned pm = row_pmax();
-      const bool exact = m == -__builtin_inff() || pm >= 0x7f80u;
+      float lhalf = __builtin_fmaxf(ls, __shfl_xor(ls, 32));
+      // (the sum can overflow even where every value is finite)
+      const bool exact = m == -__builtin_inff() || pm >= 0x7f80u || !(lhalf < __builtin_inff());
       if (__builtin_amdgcn_ballot_w64(exact) != 0) {
         issue_fence();  // forces the tile to be read again (no copy of the scores kept live)
         scores();       // the same values as before
@@ -343,8 +346,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
         nm = (m == -__builtin_inff()) ? 0.0f : -m;
         exponentiate();  // same values for the other rows
         pm = row_pmax();
+        lhalf = __builtin_fmaxf(ls, __shfl_xor(ls, 32));
       }
-      const float lhalf = __builtin_fmaxf(ls, __shfl_xor(ls, 32));
       const int k = (int)(pm >> 7) - 127 + ((pm & 0x7fu) != 0u);  // ceil(log2(largest P))
       const int kk = !(lhalf < kHalfSumLimit) ? k : 0;
       if (__builtin_amdgcn_ballot_w64(kk != 0) != 0) {

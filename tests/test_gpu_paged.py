@@ -141,3 +141,26 @@ def test_long_sequence_forward_bits_and_sampled_oracle(d, window, dtype):
         e_l = max(e_l, max_abs(got_l[h, sample], l_r))
     say(f"  sampled rows: o={e_o:.2e} lse={e_l:.2e}")
     assert e_o <= TOL_O and e_l <= TOL_LSE
+
+
+@pytest.mark.parametrize("factor", [8.0, 80.0])
+def test_paged_rows_bit_identical_under_large_logit_jumps(factor):
+    """The forward's raise decisions (integer shifts, exact-maximum path on an
+    overflowing tile) depend on each row alone: paged rows equal the
+    training rows bit for bit on inputs that trigger both."""
+    import attention_sink_fwd_amd as sa
+    from tests.test_gpu_parity import large_logit_inputs
+
+    w, inp, scale = large_logit_inputs(factor, 0)
+    say("case paged large logits", factor)
+    dev = {k: v.to("cuda:0") for k, v in inp.items()}
+    o_t, lse_t = sa.sink_attn_fwd(dev["q"], dev["k"], dev["v"], dev["sinks"], dev["cu_seqlens"],
+                                  w.max_seqlen, scale, 0)
+    pg = make_paged(inp, (180, 77), 64, seed=19)
+    d = {k: v.to("cuda:0") for k, v in pg.items() if k != "rows"}
+    o, lse = sa.sink_attn_fwd_paged(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["kv_lens"],
+                                    d["sinks"], d["cu_seqlens"], 180, scale, 0)
+    torch.cuda.synchronize()
+    rows = pg["rows"].to("cuda:0")
+    assert torch.isfinite(o_t).all() and torch.isfinite(lse_t).all()
+    assert torch.equal(o, o_t[rows]) and torch.equal(lse, lse_t[:, rows])

@@ -109,6 +109,34 @@ def test_grouped_dkdv_workgroups_match_oracle(monkeypatch, heads, lengths, hq, h
     check_full(gpu, ref, label)
 
 
+def large_logit_inputs(factor, window, seed=77):
+    """Keys 100..119 and 250..259 (packed rows) scaled by `factor`: the scores
+    of later rows jump far above the running maximum.  softmax_scale is
+    0.125 / log2(e), so the forward's scaled query operand (q * scale *
+    log2 e = q / 8) is exact in bf16 and the large scores carry no rounding
+    beyond the float accumulation."""
+    w = custom_workload((300, 130), 8, 2, 64, window, "bf16")
+    inp = make_inputs(w, seed=seed + int(factor) + window)
+    k = inp["k"].float()
+    k[100:120] *= factor
+    k[250:260] *= factor
+    inp["k"] = k.to(inp["k"].dtype)
+    return w, inp, 0.125 / math.log2(math.e)
+
+
+@pytest.mark.parametrize("factor", [8.0, 80.0])
+@pytest.mark.parametrize("window", [0, 40])
+def test_large_logit_jumps_match_oracle(factor, window):
+    """Score jumps of about 20 (factor 8) and over 128 (factor 80) log2 units
+    above a row's running maximum: the forward raises its reference by an
+    integer power of two, or (an overflowing tile) by the exact tile maximum."""
+    w, inp, scale = large_logit_inputs(factor, window)
+    label = f"large logits x{factor} W={window}"
+    say("case", label)
+    gpu = run_gpu(inp, w.max_seqlen, scale, window)
+    check_full(gpu, _oracle_full(inp, scale, window), label)
+
+
 def test_workload1_tiny_fp32_matches_oracle():
     w = WORKLOADS[1]
     say("case workload 1", w.name)
