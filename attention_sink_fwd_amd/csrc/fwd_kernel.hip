@@ -21,7 +21,7 @@
 // writes O = acc / l and LSE = m + ln(l) (natural log, sink included).
 //
 // A row's reference max m is only raised when the tile's exponentials at the
-// old m sum to 2^7 or more over either half of the row (32 keys); otherwise
+// old m sum to 2^12 or more over either half of the row (32 keys); otherwise
 // the tile is used at the old m.  The result is the same softmax: m cancels
 // between O's numerator and l.  The common case needs no row maximum: the
 // exponentials and their half-row sums are formed first, and only a
@@ -40,7 +40,7 @@ namespace {
 
 constexpr int kBN = 64;   // keys per LDS tile
 constexpr int kD = 64;    // padded head dimension
-constexpr float kHalfSumLimit = 128.0f;  // a half row's sum over a tile (old m) that raises m
+constexpr float kHalfSumLimit = 4096.0f;  // a half row's sum over a tile (old m) that raises m
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
