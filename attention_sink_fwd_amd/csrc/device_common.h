@@ -160,6 +160,12 @@ __device__ __forceinline__ void lds_dma16_s(uint32_t voff, const void* sbase, co
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
                : "memory", "m0");
 }
+// Non-temporal form (data read once: kept out of the caches' retention).
+__device__ __forceinline__ void lds_dma16_s_nt(uint32_t voff, const void* sbase, const void* lds_base) {
+  const unsigned m0 = (unsigned)(uintptr_t)(SA_LDS const void*)lds_base;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void lds_dma4_s(uint32_t voff, const void* sbase, const void* lds_base) {
   const unsigned m0 = (unsigned)(uintptr_t)(SA_LDS const void*)lds_base;
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)

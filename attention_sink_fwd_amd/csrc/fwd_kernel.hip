@@ -142,10 +142,18 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
       const bf16* kb = (const bf16*)Kg + prow * ks;
       const bf16* vb = (const bf16*)Vg + prow * ks;
       if (rem >= kBN) {
+        if constexpr (kPaged) {
+          // a cache is read once per KV head: non-temporal
 #pragma unroll
-        for (int i = 0; i < kBlk; ++i) lds_dma16_s(voff[i], kb, st.k + 512 * (kBlk * w + i));
+          for (int i = 0; i < kBlk; ++i) lds_dma16_s_nt(voff[i], kb, st.k + 512 * (kBlk * w + i));
 #pragma unroll
-        for (int i = 0; i < kBlk; ++i) lds_dma16_s(voff[i], vb, st.v + 512 * (kBlk * w + i));
+          for (int i = 0; i < kBlk; ++i) lds_dma16_s_nt(voff[i], vb, st.v + 512 * (kBlk * w + i));
+        } else {
+#pragma unroll
+          for (int i = 0; i < kBlk; ++i) lds_dma16_s(voff[i], kb, st.k + 512 * (kBlk * w + i));
+#pragma unroll
+          for (int i = 0; i < kBlk; ++i) lds_dma16_s(voff[i], vb, st.v + 512 * (kBlk * w + i));
+        }
       } else {
         // rows r >= rem read row rem - 1 instead: r - (rem - 1) rows fewer
         uint32_t cl[kBlk];
