@@ -119,7 +119,7 @@ def test_long_sequence_forward_bits_and_sampled_oracle(d, window, dtype):
     sampled rows the oracle."""
     import attention_sink_fwd_amd as sa
 
-    lengths, q_lens = (16400, 37), (300, 37)
+    lengths, q_lens = (16400, 37, 0, 130), (300, 37, 0, 130)
     w = custom_workload(lengths, 4, 2, d, window, dtype)
     say("case long forward", lengths, d, window, dtype)
     inp = make_inputs(w, seed=16400 + d + window)
@@ -139,7 +139,16 @@ def test_long_sequence_forward_bits_and_sampled_oracle(d, window, dtype):
                                        w.softmax_scale, window, 0, h, sample)
         e_o = max(e_o, max_abs(got_o[sample, h], o_r))
         e_l = max(e_l, max_abs(got_l[h, sample], l_r))
-    say(f"  sampled rows: o={e_o:.2e} lse={e_l:.2e}")
+    # the short sequences of the same launch, every element
+    cu = inp["cu_seqlens"].numpy()
+    for sq in (1, 3):
+        b, e = int(cu[sq]), int(cu[sq + 1])
+        c1 = np.array([0, e - b])
+        o_r, l_r = oracle.forward(inp["q"][b:e], inp["k"][b:e], inp["v"][b:e], inp["sinks"], c1,
+                                  w.softmax_scale, window)
+        e_o = max(e_o, max_abs(got_o[b:e], o_r))
+        e_l = max(e_l, max_abs(got_l[:, b:e], l_r))
+    say(f"  sampled rows and short sequences: o={e_o:.2e} lse={e_l:.2e}")
     assert e_o <= TOL_O and e_l <= TOL_LSE
 
 
