@@ -42,14 +42,19 @@ class Hip:
     def __init__(self):
         self.lib = ctypes.CDLL("libamdhip64.so")
         vp = ctypes.c_void_p
-        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(vp)]
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
         self.lib.hipEventRecord.argtypes = [vp, vp]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
         self.lib.hipEventDestroy.argtypes = [vp]
 
+    # Timing-only events: without a system-scope release (hipEventDisableSystemFence),
+    # recording one does not write back and invalidate L2 between the kernels
+    # it separates; the host reads them only after a device synchronisation.
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
     def event(self):
         e = ctypes.c_void_p()
-        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        assert self.lib.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) == 0
         return e
 
     def record(self, e, stream):
