@@ -197,11 +197,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
       qf[c] = d0 < hd ? __builtin_convertvector(load8f(Qh + qcl * qs + d0) * a.scale_log2, bf16x8) : zero8();
     }
   }
+  const float sink = a.sinks[hq];  // requested with the fragments: one wait covers both
   wait_vmem_all();  // fragments and the first tile resident before the loop (see wait_vmem_all)
   issue_fence();
 
   // Online softmax state in the log2 domain, seeded with the sink.
-  const float sink = a.sinks[hq];
   float m = sink * kLog2e;                                          // -inf stays -inf
   float l = (h2 == 0 && sink != -__builtin_inff()) ? 1.0f : 0.0f;  // counted once per row
   f32x16 o[2];
@@ -398,8 +398,38 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
   }
 
   const float lt = l + __shfl_xor(l, 32);
-  if (qrow < L) {
-    const float inv = 1.0f / lt;
+  const float inv = 1.0f / lt;
+  if constexpr (kDirect) {
+    // O goes out through LDS: a lane holds 4-value pieces of d for its own
+    // column, so direct stores would write 8 bytes per lane scattered over 32
+    // rows.  Each wavefront writes its 32 x 64 block of O^T into its own 4 KB
+    // of the (now idle) stage buffers, 16-byte chunks XOR-swizzled by column,
+    // and reads it back so that 8 lanes store the 128 contiguous bytes of one
+    // column (a row of O for one head) with 16-byte stores.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last, redundant tile load has landed
+    lds_barrier();                                      // and no wavefront still reads a stage
+    bf16* ep = (bf16*)&stage[0] + w * (32 * kD);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const f32x4 v = {o[db][4 * gi] * inv, o[db][4 * gi + 1] * inv, o[db][4 * gi + 2] * inv,
+                         o[db][4 * gi + 3] * inv};
+        const int chunk = 4 * db + gi;  // d = 8 * chunk + 4 * h2 + 0..3
+        *(bf16x4*)(ep + l32 * kD + ((chunk ^ (l32 & 7)) << 3) + 4 * h2) = __builtin_convertvector(v, bf16x4);
+      }
+    }
+    issue_fence();  // the reads below take other lanes' writes (LDS keeps a wavefront's order)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 8 * i + (lane >> 3), j = lane & 7;  // column of this wavefront, 16-byte chunk
+      const bf16x8 x = *(const bf16x8*)(ep + c * kD + ((j ^ (c & 7)) << 3));
+      const int n = 32 * w + c;
+      const int row = q0 + n / hp;
+      if (row < L) *(bf16x8*)((bf16*)a.o + (long)(bos + row) * qs + (hb * hp + n % hp) * kD + 8 * j) = x;
+    }
+    if (qrow < L && h2 == 0) a.lse[(long)hq * a.total_tokens + bos + qrow] = (m + __log2f(lt)) * kLn2;
+  } else if (qrow < L) {
     TIn* O = (TIn*)a.o + (long)(bos + qrow) * qs + hq * hd;
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
