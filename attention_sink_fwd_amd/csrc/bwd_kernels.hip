@@ -587,10 +587,38 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     float sw = own_row ? -__expf(sink - lse) * D : 0.0f;
     for (int off = hp; off < 64; off *= 2) sw += __shfl_xor(sw, off);
     if (lane < hp) wsum[w][lane] = sw;
+    // (the ring's last, redundant tile loads land before the barrier, so the
+    // stage buffers are idle after it)
+    if constexpr (kDirect) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid < hp) dsink_slots[tid * slot_stride] = (wsum[0][tid] + wsum[1][tid]) + (wsum[2][tid] + wsum[3][tid]);
   }
-  if (qrow < L) {
+  if constexpr (kDirect) {
+    // dQ goes out through LDS, as the forward's O: each wavefront writes its
+    // 32 x 64 block of dQ^T into its own 4 KB of the idle stage buffers
+    // (16-byte chunks XOR-swizzled by column) and reads it back so that 8
+    // lanes store the 128 contiguous bytes of one row of one head.
+    bf16* ep = (bf16*)&stage[0] + w * (32 * kD);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const f32x4 v = {acc[db][4 * gi] * a.scale, acc[db][4 * gi + 1] * a.scale, acc[db][4 * gi + 2] * a.scale,
+                         acc[db][4 * gi + 3] * a.scale};
+        const int chunk = 4 * db + gi;  // d = 8 * chunk + 4 * h2 + 0..3
+        *(bf16x4*)(ep + l32 * kD + ((chunk ^ (l32 & 7)) << 3) + 4 * h2) = __builtin_convertvector(v, bf16x4);
+      }
+    }
+    issue_fence();  // the reads below take other lanes' writes (LDS keeps a wavefront's order)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 8 * i + (lane >> 3), j = lane & 7;  // column of this wavefront, 16-byte chunk
+      const bf16x8 x = *(const bf16x8*)(ep + c * kD + ((j ^ (c & 7)) << 3));
+      const int n = 32 * w + c;
+      const int row = q0 + n / hp;
+      if (row < L) *(bf16x8*)((bf16*)a.dq + (long)(bos + row) * qs + (hb * hp + n % hp) * kD + 8 * j) = x;
+    }
+  } else if (qrow < L) {
     TIn* dq = (TIn*)a.dq + (long)(bos + qrow) * qs + hq * hd;
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
