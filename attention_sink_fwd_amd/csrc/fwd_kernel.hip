@@ -341,7 +341,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
         const bool first = m == -__builtin_inff();
         const bool raise = exact && mx > -__builtin_inff();
         const float shift = raise ? mx : 0.0f;  // while m = -inf the scores are unshifted
-        const float alpha = fast_exp2(-shift);  // l and O are still 0 while m = -inf
+        // While m = -inf, l and O are exactly 0 and stay so: no rescale (a
+        // first tile whose largest score is below -128 would give
+        // exp2(-shift) = inf and 0 * inf = NaN).
+        const float alpha = first ? 1.0f : fast_exp2(-shift);
         l *= alpha;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {

@@ -173,3 +173,25 @@ def test_paged_rows_bit_identical_under_large_logit_jumps(factor):
     rows = pg["rows"].to("cuda:0")
     assert torch.isfinite(o_t).all() and torch.isfinite(lse_t).all()
     assert torch.equal(o, o_t[rows]) and torch.equal(lse, lse_t[:, rows])
+
+
+@pytest.mark.parametrize("window", [0, 40])
+def test_paged_rows_bit_identical_with_minus_inf_sink_and_very_negative_scores(window):
+    """Sink -inf and a first key tile scoring about -160 log2 units: the
+    paged rows equal the training rows bit for bit and are finite."""
+    import attention_sink_fwd_amd as sa
+    from tests.test_gpu_parity import very_negative_first_tile_inputs
+
+    w, inp, scale = very_negative_first_tile_inputs(window)
+    say("case paged, sink -inf, very negative first tile, window", window)
+    dev = {k: v.to("cuda:0") for k, v in inp.items()}
+    o_t, lse_t = sa.sink_attn_fwd(dev["q"], dev["k"], dev["v"], dev["sinks"], dev["cu_seqlens"],
+                                  w.max_seqlen, scale, window)
+    pg = make_paged(inp, (180, 77), 64, seed=23)
+    d = {k: v.to("cuda:0") for k, v in pg.items() if k != "rows"}
+    o, lse = sa.sink_attn_fwd_paged(d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["kv_lens"],
+                                    d["sinks"], d["cu_seqlens"], 180, scale, window)
+    torch.cuda.synchronize()
+    rows = pg["rows"].to("cuda:0")
+    assert torch.isfinite(o_t).all() and torch.isfinite(lse_t).all()
+    assert torch.equal(o, o_t[rows]) and torch.equal(lse, lse_t[:, rows])

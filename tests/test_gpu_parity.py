@@ -137,6 +137,37 @@ def test_large_logit_jumps_match_oracle(factor, window):
     check_full(gpu, _oracle_full(inp, scale, window), label)
 
 
+def very_negative_first_tile_inputs(window, seed=91):
+    """Sink -inf, queries near (1, ..., 1), the first 64 keys of each
+    sequence equal to -0.6 * (1, ..., 1) and softmax_scale = 4 / log2(e):
+    every row's first key tile scores between about -175 and -135 log2 units
+    (q . k * scale * log2 e = 4 q . k, exact in the bf16 scaled query), far
+    below -128.  A row's reference is -inf until that tile, so the forward's
+    first rescale must not form exp2(+150) = inf.  The later keys are
+    0.1 * N(0, 1), so their scores spread over a few log2 units only (keys of
+    ordinary size: a large common key offset would amplify the bf16 rounding
+    of dS into dQ rows whose exact value cancels)."""
+    w = custom_workload((300, 130), 8, 2, 64, window, "bf16")
+    inp = make_inputs(w, seed=seed + window)
+    inp["q"] = (1.0 + 0.25 * inp["q"].float()).to(torch.bfloat16)
+    k = 0.1 * inp["k"].float()
+    for b in (0, 300):
+        k[b:b + 64] = -0.6
+    inp["k"] = k.to(torch.bfloat16)
+    inp["sinks"] = torch.full((8,), -math.inf)
+    return w, inp, 4.0 / math.log2(math.e)
+
+
+@pytest.mark.parametrize("window", [0, 40])
+def test_minus_inf_sink_with_very_negative_first_tile(window):
+    w, inp, scale = very_negative_first_tile_inputs(window)
+    label = f"sink -inf, first tile below -128 log2 units, W={window}"
+    say("case", label)
+    gpu = run_gpu(inp, w.max_seqlen, scale, window)  # also asserts every value is finite
+    check_full(gpu, _oracle_full(inp, scale, window), label)
+    assert np.all(gpu["ds"] == 0.0)
+
+
 def test_workload1_tiny_fp32_matches_oracle():
     w = WORKLOADS[1]
     say("case workload 1", w.name)
