@@ -17,6 +17,8 @@ SINK_ATTN_ERR_UNSUPPORTED = 2
 SINK_ATTN_ERR_WORKSPACE_TOO_SMALL = 3
 SINK_ATTN_ERR_HIP = 4
 
+SINK_ATTN_NOALLOC_SCRATCH_BYTES = 64 << 20  # the fixed workspace of sink_attn_bwd_noalloc
+
 SINK_ATTN_BF16 = 0
 SINK_ATTN_F32 = 1
 
@@ -25,6 +27,7 @@ EXPORTED_SYMBOLS = (
     "sink_attn_fwd_paged",
     "sink_attn_bwd",
     "sink_attn_bwd_workspace_size",
+    "sink_attn_bwd_noalloc",
     "sink_attn_set_bwd_events",
     "sink_attn_status_string",
     "sink_attn_last_error",
@@ -89,6 +92,8 @@ def load() -> ctypes.CDLL:
     lib.sink_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   ctypes.c_size_t, vp]
     lib.sink_attn_bwd.restype = ctypes.c_int
+    lib.sink_attn_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.sink_attn_bwd_noalloc.restype = ctypes.c_int
     lib.sink_attn_bwd_workspace_size.argtypes = [P]
     lib.sink_attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.sink_attn_set_bwd_events.argtypes = [ctypes.POINTER(ctypes.c_void_p)]

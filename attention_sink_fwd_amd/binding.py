@@ -153,6 +153,31 @@ def sink_attn_bwd(q, k, v, sinks, o, lse, dout, cu_seqlens, max_seqlen, softmax_
     return dq, dk, dv, dsinks
 
 
+def sink_attn_bwd_noalloc(q, k, v, sinks, o, lse, dout, cu_seqlens, max_seqlen, softmax_scale=None,
+                          window=0, dq=None, dk=None, dv=None, dsinks=None, stream=None):
+    """sink_attn_bwd with the library's fixed device buffer as workspace (no
+    workspace argument; the C call allocates nothing -- pass dq, dk, dv,
+    dsinks to keep this wrapper from allocating them)."""
+    lib = _lib.load()
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    _need(q, "q"); _need(k, "k", q.dtype, (T, hkv, d)); _need(v, "v", q.dtype, (T, hkv, d))
+    _need(o, "o", q.dtype, q.shape); _need(dout, "dout", q.dtype, q.shape)
+    _need(lse, "lse", torch.float32, (hq, T)); _need(sinks, "sinks", torch.float32, (hq,))
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dsinks = torch.empty_like(sinks) if dsinks is None else dsinks
+    _need(dq, "dq", q.dtype, q.shape); _need(dk, "dk", q.dtype, k.shape)
+    _need(dv, "dv", q.dtype, v.shape); _need(dsinks, "dsinks", torch.float32, (hq,))
+    p = make_params(q, k, cu_seqlens, max_seqlen, softmax_scale, window)
+    _lib.check(lib.sink_attn_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(o),
+                                         _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks),
+                                         _stream(stream)))
+    return dq, dk, dv, dsinks
+
+
 class _SinkAttention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, sinks, cu_seqlens, max_seqlen, softmax_scale, window):

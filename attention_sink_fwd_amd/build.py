@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsinkattn.so")
-SOURCES = ["api.cpp", "logps_api.cpp", "fwd_kernel.hip", "bwd_kernels.hip", "logps_kernels.hip"]
+SOURCES = ["api.cpp", "logps_api.cpp", "fwd_kernel.hip", "bwd_kernels.hip", "logps_kernels.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

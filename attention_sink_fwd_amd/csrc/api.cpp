@@ -13,6 +13,7 @@
 #include <cstring>
 #include <vector>
 
+#include "bwd_api.h"
 #include "launch.h"
 #include "status.h"
 
@@ -256,6 +257,66 @@ sinkattn::BwdWorkspace workspace_layout(const sink_attn_params* p, int dkdv_head
 
 }  // namespace
 
+namespace sinkattn {
+
+int bwd_check(const sink_attn_params* p, const BwdTensors& t) {
+  SA_CHECK(check_params(p));
+  if (p->total_tokens > 0) {  // with no tokens only dsinks is written (zeros)
+    SA_CHECK(check_tensor(t.q, "q"));
+    SA_CHECK(check_tensor(t.k, "k"));
+    SA_CHECK(check_tensor(t.v, "v"));
+    SA_CHECK(check_tensor(t.o, "o"));
+    SA_CHECK(check_tensor(t.dout, "dout"));
+    SA_CHECK(check_tensor(t.dq, "dq"));
+    SA_CHECK(check_tensor(t.dk, "dk"));
+    SA_CHECK(check_tensor(t.dv, "dv"));
+    if (!t.sinks) return fail(SINK_ATTN_ERR_INVALID_ARG, "sinks is NULL");
+    if (!t.lse) return fail(SINK_ATTN_ERR_INVALID_ARG, "lse is NULL");
+  }
+  if (!t.dsinks) return fail(SINK_ATTN_ERR_INVALID_ARG, "dsinks is NULL");
+  return SINK_ATTN_OK;
+}
+
+int bwd_split(const sink_attn_params* p, int* dkdv_heads, int* pack_heads, bool* dkdv_overridden) {
+  *dkdv_overridden = std::getenv("SINK_ATTN_DKDV_HEADS") != nullptr;
+  SA_CHECK(resolve_dkdv_heads(p, dkdv_heads));
+  return resolve_pack_heads(p, 32, pack_heads);
+}
+
+BwdWorkspace bwd_layout(const sink_attn_params* p, int dkdv_heads, int pack_heads) {
+  return workspace_layout(p, dkdv_heads, pack_heads);
+}
+
+int bwd_enqueue(const sink_attn_params* p, const BwdTensors& t, void* workspace, int dkdv_heads, int pack_heads,
+                void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SA_CHECK(maybe_validate_cu(p, s));
+  const BwdWorkspace ws = workspace_layout(p, dkdv_heads, pack_heads);
+  char* wsb = static_cast<char*>(workspace);
+  BwdArgs a{};
+  a.q = t.q; a.k = t.k; a.v = t.v; a.o = t.o; a.dout = t.dout; a.lse = t.lse; a.sinks = t.sinks;
+  a.cu_seqlens = p->cu_seqlens;
+  a.dq = t.dq; a.dk = t.dk; a.dv = t.dv; a.dsinks = t.dsinks;
+  size_t off = 0;
+  auto carve = [&](size_t bytes) { float* f = reinterpret_cast<float*>(wsb + off); off += bytes; return f; };
+  a.ndelta = carve(ws.ndelta);
+  a.nlse = carve(ws.nlse);
+  a.dk_part = carve(ws.dk_part);
+  a.dv_part = carve(ws.dv_part);
+  a.dsink_part = carve(ws.dsink_part);
+  a.num_q_heads = p->num_q_heads; a.num_kv_heads = p->num_kv_heads; a.head_dim = p->head_dim;
+  a.total_tokens = p->total_tokens; a.window = p->window; a.num_seqs = p->num_seqs;
+  a.scale = p->softmax_scale;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.dkdv_heads = dkdv_heads;
+  a.heads_per_tile = pack_heads;
+  hipError_t e = launch_bwd(a, p->dtype, p->max_seqlen, p->num_seqs, s, g_bwd_events_on ? g_bwd_events : nullptr);
+  if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+  return SINK_ATTN_OK;
+}
+
+}  // namespace sinkattn
+
 extern "C" {
 
 size_t sink_attn_bwd_workspace_size(const sink_attn_params* p) {
@@ -270,20 +331,8 @@ int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const
                   const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv, float* dsinks,
                   void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = '\0';
-  SA_CHECK(check_params(p));
-  if (p->total_tokens > 0) {  // with no tokens only dsinks is written (zeros)
-    SA_CHECK(check_tensor(q, "q"));
-    SA_CHECK(check_tensor(k, "k"));
-    SA_CHECK(check_tensor(v, "v"));
-    SA_CHECK(check_tensor(o, "o"));
-    SA_CHECK(check_tensor(dout, "dout"));
-    SA_CHECK(check_tensor(dq, "dq"));
-    SA_CHECK(check_tensor(dk, "dk"));
-    SA_CHECK(check_tensor(dv, "dv"));
-    if (!sinks) return fail(SINK_ATTN_ERR_INVALID_ARG, "sinks is NULL");
-    if (!lse) return fail(SINK_ATTN_ERR_INVALID_ARG, "lse is NULL");
-  }
-  if (!dsinks) return fail(SINK_ATTN_ERR_INVALID_ARG, "dsinks is NULL");
+  const sinkattn::BwdTensors t{q, k, v, sinks, o, lse, dout, dq, dk, dv, dsinks};
+  SA_CHECK(sinkattn::bwd_check(p, t));
   int dkdv_heads = 0, pack_heads = 0;
   SA_CHECK(resolve_dkdv_heads(p, &dkdv_heads));
   SA_CHECK(resolve_pack_heads(p, 32, &pack_heads));
@@ -293,31 +342,7 @@ int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const
   if (ws.total > 0 && !workspace) return fail(SINK_ATTN_ERR_INVALID_ARG, "workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(SINK_ATTN_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  SA_CHECK(maybe_validate_cu(p, s));
-
-  char* wsb = static_cast<char*>(workspace);
-  sinkattn::BwdArgs a{};
-  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.sinks = sinks;
-  a.cu_seqlens = p->cu_seqlens;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.dsinks = dsinks;
-  size_t off = 0;
-  auto carve = [&](size_t bytes) { float* p = reinterpret_cast<float*>(wsb + off); off += bytes; return p; };
-  a.ndelta = carve(ws.ndelta);
-  a.nlse = carve(ws.nlse);
-  a.dk_part = carve(ws.dk_part);
-  a.dv_part = carve(ws.dv_part);
-  a.dsink_part = carve(ws.dsink_part);
-  a.num_q_heads = p->num_q_heads; a.num_kv_heads = p->num_kv_heads; a.head_dim = p->head_dim;
-  a.total_tokens = p->total_tokens; a.window = p->window; a.num_seqs = p->num_seqs;
-  a.scale = p->softmax_scale;
-  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
-  a.dkdv_heads = dkdv_heads;
-  a.heads_per_tile = pack_heads;
-  hipError_t e = sinkattn::launch_bwd(a, p->dtype, p->max_seqlen, p->num_seqs, s,
-                                       g_bwd_events_on ? g_bwd_events : nullptr);
-  if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
-  return SINK_ATTN_OK;
+  return sinkattn::bwd_enqueue(p, t, workspace, dkdv_heads, pack_heads, stream);
 }
 
 int sink_attn_set_bwd_events(void* const* events) {

@@ -1,0 +1,41 @@
+// Host-side pieces of the backward entry points, shared by sink_attn_bwd
+// (api.cpp, caller-supplied workspace) and sink_attn_bwd_noalloc
+// (noalloc.hip, a fixed device buffer).
+#pragma once
+
+#include <stddef.h>
+
+#include "launch.h"
+#include "sink_attn.h"
+
+namespace sinkattn {
+
+struct BwdTensors {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* sinks;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsinks;
+};
+
+// Argument checks of the backward pass (status and sink_attn_last_error text,
+// nothing enqueued on failure).
+int bwd_check(const sink_attn_params* p, const BwdTensors& t);
+// The work split: query heads per dK/dV workgroup and per dQ workgroup (the
+// shape-based choice, or the SINK_ATTN_DKDV_HEADS / SINK_ATTN_PACK_HEADS
+// overrides; *dkdv_overridden tells whether the first was given).
+int bwd_split(const sink_attn_params* p, int* dkdv_heads, int* pack_heads, bool* dkdv_overridden);
+// Workspace sections for a split.
+BwdWorkspace bwd_layout(const sink_attn_params* p, int dkdv_heads, int pack_heads);
+// Carve `workspace` (256-byte aligned, at least bwd_layout(...).total bytes)
+// and enqueue the backward kernels on `stream`.
+int bwd_enqueue(const sink_attn_params* p, const BwdTensors& t, void* workspace, int dkdv_heads, int pack_heads,
+                void* stream);
+
+}  // namespace sinkattn

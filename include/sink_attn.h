@@ -198,6 +198,38 @@ int sink_attn_bwd(const sink_attn_params *p, const void *q, const void *k, const
                   size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of the fixed device buffer that sink_attn_bwd_noalloc uses as its
+ * workspace (64 MiB, one buffer per device).
+ */
+#define SINK_ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * Backward pass that allocates nothing: the same computation, arguments
+ * (less the workspace) and results as sink_attn_bwd, for callers that cannot
+ * allocate device memory -- code under HIP graph capture, tight training or
+ * serving loops, harnesses that forbid hipMalloc.  Its workspace is a buffer
+ * of SINK_ATTN_NOALLOC_SCRATCH_BYTES that the library holds on each device it
+ * runs on (loaded with its code, kept until the process ends); the call makes
+ * no hipMalloc, hipFree or other allocation.  The first call on a device looks
+ * the buffer's address up on the current device, which must be the device of
+ * `stream` (else SINK_ATTN_ERR_INVALID_ARG).
+ *   The work split is sink_attn_bwd's when its workspace fits the buffer (the
+ * results are then bitwise identical); otherwise the dK/dV kernel takes more
+ * query heads per workgroup (fewer float partial sums, only the order of the
+ * dK/dV additions changes), unless SINK_ATTN_DKDV_HEADS fixes the split.  A
+ * shape whose workspace does not fit in any split (about num_q_heads *
+ * total_tokens above 8 million) returns SINK_ATTN_ERR_UNSUPPORTED with the
+ * size it needs, before anything is enqueued.
+ *   All calls on one device share its buffer: calls that overlap in time on
+ * one device (two streams, or two threads) race and give wrong results; calls
+ * ordered on one stream are safe.  The buffer's contents on entry are ignored
+ * (nothing in it needs to start at zero).
+ */
+int sink_attn_bwd_noalloc(const sink_attn_params *p, const void *q, const void *k, const void *v,
+                          const float *sinks, const void *o, const float *lse, const void *dout,
+                          void *dq, void *dk, void *dv, float *dsinks, void *stream);
+
+/*
  * Instrumentation (benchmarks and profilers).  Sets, for the calling thread,
  * four hipEvent_t handles that every later sink_attn_bwd call on this thread
  * records on its stream: events[0] before the dQ kernel (which also derives

@@ -343,3 +343,54 @@ def test_logps_zero_rows_is_a_no_op():
     for b, n in ((0, 4), (4, 0)):
         assert _logps_fwd(batch=b, seq=n, logits=None, ids=None, logps=None) == _lib.SINK_ATTN_OK
         assert _logps_bwd(batch=b, seq=n, logits=None, ids=None, lse=None, g=None, gx=None) == _lib.SINK_ATTN_OK
+
+
+def _bwd_noalloc(p, **override):
+    lib = _lib.load()
+    args = dict(q=FAKE, k=FAKE, v=FAKE, sinks=FAKE, o=FAKE, lse=FAKE, dout=FAKE, dq=FAKE,
+                dk=FAKE, dv=FAKE, dsinks=FAKE)
+    args.update(override)
+    ptr = ctypes.byref(p) if p is not None else None
+    return lib.sink_attn_bwd_noalloc(ptr, args["q"], args["k"], args["v"], args["sinks"], args["o"],
+                                     args["lse"], args["dout"], args["dq"], args["dk"], args["dv"],
+                                     args["dsinks"], None)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "sinks", "o", "lse", "dout", "dq", "dk", "dv",
+                                  "dsinks"])
+def test_noalloc_bwd_null_tensor(name):
+    assert _bwd_noalloc(_good_params(), **{name: None}) == _lib.SINK_ATTN_ERR_INVALID_ARG
+
+
+def test_noalloc_bwd_bad_params():
+    p = _good_params()
+    p.head_dim = 12
+    assert _bwd_noalloc(p) == _lib.SINK_ATTN_ERR_INVALID_ARG
+    assert _bwd_noalloc(None) == _lib.SINK_ATTN_ERR_INVALID_ARG
+
+
+def test_noalloc_bwd_rejects_workspace_beyond_its_buffer():
+    """The row statistics alone (2 floats per query head and token) exceed the
+    fixed buffer: rejected with the size it would need, before any HIP call."""
+    lib = _lib.load()
+    T, hq = 140000, 64
+    assert 2 * 4 * hq * T > _lib.SINK_ATTN_NOALLOC_SCRATCH_BYTES
+    p = _good_params(T=T, hq=hq, hkv=8)
+    assert _bwd_noalloc(p) == _lib.SINK_ATTN_ERR_UNSUPPORTED
+    msg = lib.sink_attn_last_error().decode()
+    assert "needs" in msg and str(_lib.SINK_ATTN_NOALLOC_SCRATCH_BYTES) in msg
+
+
+def test_noalloc_bwd_respects_a_fixed_split_that_does_not_fit(monkeypatch):
+    """With SINK_ATTN_DKDV_HEADS fixing one head per dK/dV workgroup, the
+    float partial sums of 4096 tokens x 64 heads do not fit: rejected rather
+    than silently taking another split."""
+    monkeypatch.setenv("SINK_ATTN_DKDV_HEADS", "1")
+    p = _good_params(T=4096, hq=64, hkv=8)
+    assert _bwd_noalloc(p) == _lib.SINK_ATTN_ERR_UNSUPPORTED
+
+
+def test_noalloc_buffer_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "sink_attn.h")).read()
+    m = re.search(r"#define SINK_ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.SINK_ATTN_NOALLOC_SCRATCH_BYTES
