@@ -11,8 +11,10 @@ Pins (all in tests/test_oracle_pins.py, CPU only):
                         central finite differences; closed forms (S -> -inf,
                         S -> +inf, q = 0, length 1, window 1); invariants
                         (varlen packing, GQA == repeated MHA, window >= L).
-  forward_rows, backward_rows, backward_keys
-                     -> equal to the corresponding entries of forward/backward.
+  forward_rows, backward_rows, backward_keys, backward_keys_blocked
+                     -> equal to the corresponding entries of forward/backward,
+                        and (backward_keys_blocked) to the SDPA reference's
+                        dK, dV and dS directly.
   gather_paged, forward_paged
                      -> a paged cache holding whole sequences with q_len ==
                         kv_len equals forward; new tokens at the end of a
@@ -29,6 +31,7 @@ No function here is "parity unpinned".
 from .sink_attention import (  # noqa: F401
     backward,
     backward_keys,
+    backward_keys_blocked,
     backward_rows,
     forward,
     forward_paged,

@@ -40,6 +40,8 @@ Library primitives used as steps: ``numpy.matmul`` and
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 from scipy.special import logsumexp
 
@@ -274,3 +276,71 @@ def backward_keys(q, k, v, sinks, dout, cu_seqlens, scale, window, seq, kv_head,
                 dk[n] += scale * dx * qh[i]
                 dv[n] += pij * doh[i]
     return dk, dv
+
+
+def backward_keys_blocked(q, k, v, sinks, dout, cu_seqlens, scale, window, seq, kv_head, keys,
+                          heads=None, row_block=512):
+    """dK, dV rows [len(keys), d] of one sequence and KV head, and the sink
+    gradient's share of this sequence for each listed query head.
+
+    The same formulas as ``backward``, restricted to a key set and a head
+    set: every query row of every listed head (default: all heads of the KV
+    group, so dK and dV are complete) is evaluated from its full logit row,
+    ``row_block`` rows at a time.  Rows are not skipped, because dS_h needs
+    every row; with an empty key set only the sink gradients are formed.
+    Written with float64 PyTorch CPU operations (multithreaded) so that rows
+    of 65536 keys stay affordable: the extended logit row (visible keys plus
+    the sink) is shifted by its maximum, exponentiated and normalised.
+    Returns (dk, dv, ds) where ds maps head -> -sum_i p_sink,i D_i over the
+    rows of this sequence.
+    """
+    import torch
+
+    q, k, v, sinks, dout = _f64(q), _f64(k), _f64(v), _f64(sinks), _f64(dout)
+    cu = _i64(cu_seqlens)
+    b, e = int(cu[seq]), int(cu[seq + 1])
+    L = e - b
+    hq, hkv, d = q.shape[1], k.shape[1], q.shape[2]
+    group = hq // hkv
+    heads = range(kv_head * group, (kv_head + 1) * group) if heads is None else heads
+    keys = torch.as_tensor(np.asarray(keys, dtype=np.int64))
+    dk = torch.zeros((len(keys), d), dtype=torch.float64)
+    dv = torch.zeros((len(keys), d), dtype=torch.float64)
+    ds = {}
+    kg = torch.from_numpy(np.ascontiguousarray(k[b:e, kv_head]))
+    vg = torch.from_numpy(np.ascontiguousarray(v[b:e, kv_head]))
+    for h in heads:
+        assert kv_head_of(h, hq, hkv) == kv_head
+        qh = torch.from_numpy(np.ascontiguousarray(q[b:e, h]))
+        doh = torch.from_numpy(np.ascontiguousarray(dout[b:e, h]))
+        sink = float(sinks[h])
+        ds[h] = 0.0
+        for r0 in range(0, L, row_block):
+            r1 = min(L, r0 + row_block)
+            klo = visible_key_range(r0, window)[0]
+            i = torch.arange(r0, r1)[:, None]
+            j = torch.arange(klo, r1)[None, :]
+            hidden = j > i
+            if window > 0:
+                hidden |= (i - j) >= window
+            x = (qh[r0:r1] @ kg[klo:r1].T).mul_(scale)                # x_ij = tau q_i . k_j
+            x.masked_fill_(hidden, -math.inf)
+            m = torch.clamp(x.amax(dim=1), min=sink)                  # max over the extended row
+            m = torch.where(torch.isfinite(m), m, torch.zeros_like(m))
+            x.sub_(m[:, None]).exp_()                                 # e^(x_ij - m_i)
+            e_sink = torch.exp(sink - m)
+            denom = x.sum(dim=1) + e_sink
+            p = x.div_(denom[:, None])                                # P_ij
+            p_sink = e_sink / denom                                   # p_sink,i
+            o_rows = p @ vg[klo:r1]
+            d_rows = (doh[r0:r1] * o_rows).sum(dim=1)                 # D_i = dO_i . O_i
+            ds[h] += float(-(p_sink * d_rows).sum())                  # sink has no value
+            sel = torch.nonzero((keys >= klo) & (keys < r1)).flatten()
+            if len(sel) == 0:
+                continue
+            kj = keys[sel]
+            pk = p[:, kj - klo]                                       # P_ij at the listed keys
+            dx = pk * (doh[r0:r1] @ vg[kj].T - d_rows[:, None])       # softmax Jacobian
+            dk[sel] += scale * (dx.T @ qh[r0:r1])
+            dv[sel] += pk.T @ doh[r0:r1]
+    return dk.numpy(), dv.numpy(), ds

@@ -10,6 +10,8 @@ the relative checks to the same bound on the absolute norm.
 """
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -79,3 +81,15 @@ def check_full(gpu, ref, label=""):
     assert errs["dq"] <= TOL_GRAD and errs["dk"] <= TOL_GRAD and errs["dv"] <= TOL_GRAD, (label, errs)
     assert errs["ds"] <= TOL_DS, (label, errs)
     return errs
+
+
+def record_errors(config: str, compared: str, errs: dict) -> None:
+    """Append one line of error figures to the file named by
+    SINK_ATTN_ERROR_LOG (when set): the per-workload error report."""
+    path = os.environ.get("SINK_ATTN_ERROR_LOG")
+    if not path:
+        return
+    row = {"config": config, "compared": compared}
+    row.update({k: float(v) for k, v in errs.items()})
+    with open(path, "a") as f:
+        f.write(json.dumps(row) + "\n")

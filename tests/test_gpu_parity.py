@@ -12,8 +12,8 @@ import torch
 
 import oracle
 from synthetic.workloads import WORKLOADS, custom_workload, make_inputs
-from tests.parity_util import (TOL_DS, TOL_GRAD, TOL_LSE, TOL_O, check_full, max_abs, rel_l2,
-                               run_gpu, say)
+from tests.parity_util import (TOL_DS, TOL_GRAD, TOL_LSE, TOL_O, check_full, max_abs, record_errors,
+                               rel_l2, run_gpu, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -173,7 +173,10 @@ def test_workload1_tiny_fp32_matches_oracle():
     say("case workload 1", w.name)
     inp = make_inputs(w)
     gpu = run_gpu(inp, w.max_seqlen, w.softmax_scale, w.window)
-    check_full(gpu, _oracle_full(inp, w.softmax_scale, w.window), w.name)
+    ref = _oracle_full(inp, w.softmax_scale, w.window)
+    errs = check_full(gpu, ref, w.name)
+    errs["ds_head_max"] = _ds_head_max(gpu["ds"], ref["ds"])
+    record_errors(w.name, "every element", errs)
 
 
 def test_forward_is_deterministic_and_packing_is_invariant():
@@ -354,9 +357,18 @@ def _check_group(gpu, refs, g, label):
     for n in num:
         errs[n] = math.sqrt(num[n] / den[n])
     say(f"  {label} group {g}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for n in den:
+        errs["_den_" + n] = den[n]
     assert errs["o"] <= TOL_O and errs["lse"] <= TOL_LSE, errs
     assert errs["dq"] <= TOL_GRAD and errs["dk"] <= TOL_GRAD and errs["dv"] <= TOL_GRAD, errs
     return errs
+
+
+def _ds_head_max(got, ref):
+    """Largest per-head relative error of dS (heads whose exact |dS| is below
+    1e-6 count with their absolute error)."""
+    got, ref = np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-6)))
 
 
 def _ds_self_consistency(gpu, inp):
@@ -378,19 +390,77 @@ def test_full_workload_whole_kv_groups(wid):
     hq, hkv = w.num_q_heads, w.num_kv_heads
     ds_ref = np.zeros(hq)
     ds_heads = []
+    group_errs = []
     for g in (0, hkv - 3):
         refs = _kv_group_reference(inp, w.softmax_scale, w.window, g)
-        _check_group(gpu, refs, g, w.name)
+        group_errs.append(_check_group(gpu, refs, g, w.name))
         for r in refs:
             ds_ref[r[3]] += r[9][r[3]]
         ds_heads += r[3]
+    a, b = group_errs
     e = rel_l2(gpu["ds"][ds_heads], ds_ref[ds_heads])
     say(f"  dS over heads {ds_heads[0]}..: {e:.2e}; self-consistency {_ds_self_consistency(gpu, inp):.2e}")
     assert e <= TOL_DS
+    errs = {n: max(a[n], b[n]) for n in ("o", "lse")}
+    errs.update({n: math.sqrt((a[n] ** 2 * a["_den_" + n] + b[n] ** 2 * b["_den_" + n]) /
+                              (a["_den_" + n] + b["_den_" + n])) for n in ("dq", "dk", "dv")})
+    errs["ds"] = e
+    errs["ds_head_max"] = _ds_head_max(gpu["ds"][ds_heads], ds_ref[ds_heads])
+    record_errors(w.name, f"KV groups 0 and {hkv - 3} (query heads {ds_heads[0]}-{ds_heads[7]}, "
+                  f"{ds_heads[8]}-{ds_heads[-1]}), every row and key", errs)
+    if wid == 2:
+        _record_scaled_operand_share(inp, w, gpu)
+
+
+def _rounded_operand(t, scale):
+    """The score operand the kernels keep in registers, mapped back to the
+    input's scale: bf16(t * scale * log2 e) / (scale * log2 e), with the
+    factor formed in float32 as the library does."""
+    c = np.float32(np.float32(scale) * np.float32(1.4426950408889634))
+    x = (t.float() * float(c)).to(torch.bfloat16).double() / float(c)
+    return x
+
+
+def _record_scaled_operand_share(inp, w, gpu):
+    """How far the oracle's own outputs move (KV group 0) when q, or k, is
+    replaced everywhere by the bf16-rounded scaled operand the forward and
+    dQ kernels (q) or the dK/dV kernel (k) multiply with, next to the GPU's
+    total error on the same outputs."""
+    g, grp = 0, w.num_q_heads // w.num_kv_heads
+    heads = list(range(g * grp, (g + 1) * grp))
+    exact = _kv_group_reference(inp, w.softmax_scale, w.window, g)[0]
+    rows = {}
+    for name in ("q", "k"):
+        alt = dict(inp)
+        alt[name] = _rounded_operand(inp[name], w.softmax_scale)
+        r = _kv_group_reference(alt, w.softmax_scale, w.window, g)[0]
+        rows[name] = {
+            "o": max_abs(r[4][:, heads], exact[4][:, heads]),
+            "lse": max_abs(r[5][heads], exact[5][heads]),
+            "dq": rel_l2(r[6][:, heads], exact[6][:, heads]),
+            "dk": rel_l2(r[7][:, g], exact[7][:, g]),
+            "dv": rel_l2(r[8][:, g], exact[8][:, g]),
+            "ds": rel_l2(r[9][heads], exact[9][heads]),
+        }
+    total = {
+        "o": max_abs(gpu["o"][:, heads], exact[4][:, heads]),
+        "lse": max_abs(gpu["lse"][heads], exact[5][heads]),
+        "dq": rel_l2(gpu["dq"][:, heads], exact[6][:, heads]),
+        "dk": rel_l2(gpu["dk"][:, g], exact[7][:, g]),
+        "dv": rel_l2(gpu["dv"][:, g], exact[8][:, g]),
+        "ds": rel_l2(gpu["ds"][heads], exact[9][heads]),
+    }
+    for name, vals in (("oracle, q -> bf16(q scale log2e)", rows["q"]),
+                       ("oracle, k -> bf16(k scale log2e)", rows["k"]), ("GPU", total)):
+        say(f"  KV group 0, {name}: " + " ".join(f"{k}={v:.2e}" for k, v in vals.items()))
+        record_errors(w.name, f"KV group 0 (query heads 0-7): {name}, against the exact oracle", vals)
 
 
 def test_full_workload4_long_context_sampled():
-    """L = 65536 head share: sampled rows (O, LSE, dQ) and late keys (dK, dV)."""
+    """L = 65536 head share against the oracle: sampled rows (O, LSE, dQ) of
+    four heads; dK, dV of one whole KV group (8 query heads) at keys 0-127
+    (reductions over all 65536 rows), a middle tile and the last keys; dS of
+    those 8 heads (every row)."""
     w = WORKLOADS[4]
     say("case workload 4", w.name)
     inp = make_inputs(w)
@@ -410,31 +480,69 @@ def test_full_workload4_long_context_sampled():
         num += float(np.sum((gpu["dq"][rows, h] - dq_r) ** 2))
         den += float(np.sum(dq_r ** 2))
     e_dq = math.sqrt(num / den)
-    keys = np.array([L - 100, L - 64, L - 33, L - 2, L - 1])
-    numk = denk = numv = denv = 0.0
-    for g in (0, 1):
-        dk_r, dv_r = oracle.backward_keys(q, k, v, s, do, cu, w.softmax_scale, 0, 0, g, keys)
-        numk += float(np.sum((gpu["dk"][keys, g] - dk_r) ** 2)); denk += float(np.sum(dk_r ** 2))
-        numv += float(np.sum((gpu["dv"][keys, g] - dv_r) ** 2)); denv += float(np.sum(dv_r ** 2))
-    e_dk, e_dv = math.sqrt(numk / denk), math.sqrt(numv / denv)
-    e_ds = _ds_self_consistency(gpu, inp)
-    say(f"  o={e_o:.2e} lse={e_l:.2e} dq={e_dq:.2e} dk={e_dk:.2e} dv={e_dv:.2e} ds(self)={e_ds:.2e}")
+    say(f"  sampled rows: o={e_o:.2e} lse={e_l:.2e} dq={e_dq:.2e}")
+    # KV group 0: keys 0-127, 32768-32895 and the last 100 keys, every row of
+    # its 8 query heads
+    keys = np.concatenate([np.arange(128), np.arange(32768, 32896), np.arange(L - 100, L)])
+    dk_r, dv_r, ds_g = oracle.backward_keys_blocked(q, k, v, s, do, cu, w.softmax_scale, 0, 0, 0, keys)
+    blocks = {"keys 0-127": slice(0, 128), "keys 32768-32895": slice(128, 256), "last 100 keys": slice(256, None)}
+    for name, sl in blocks.items():
+        say(f"  {name}: dk={rel_l2(gpu['dk'][keys[sl], 0], dk_r[sl]):.2e} "
+            f"dv={rel_l2(gpu['dv'][keys[sl], 0], dv_r[sl]):.2e}")
+    e_dk, e_dv = rel_l2(gpu["dk"][keys, 0], dk_r), rel_l2(gpu["dv"][keys, 0], dv_r)
+    heads = sorted(ds_g)
+    ds_ref = np.array([ds_g[h] for h in heads])
+    e_ds = rel_l2(gpu["ds"][heads], ds_ref)
+    e_ds_head = _ds_head_max(gpu["ds"][heads], ds_ref)
+    say(f"  o={e_o:.2e} lse={e_l:.2e} dq={e_dq:.2e} dk={e_dk:.2e} dv={e_dv:.2e} ds={e_ds:.2e} "
+        f"(worst head {e_ds_head:.2e}); ds self-consistency {_ds_self_consistency(gpu, inp):.2e}")
     assert e_o <= TOL_O and e_l <= TOL_LSE
     assert e_dq <= TOL_GRAD and e_dk <= TOL_GRAD and e_dv <= TOL_GRAD
-    assert e_ds <= 1e-3
+    for sl in blocks.values():
+        assert rel_l2(gpu["dk"][keys[sl], 0], dk_r[sl]) <= TOL_GRAD
+        assert rel_l2(gpu["dv"][keys[sl], 0], dv_r[sl]) <= TOL_GRAD
+    assert e_ds <= TOL_DS
+    record_errors(w.name, "O, LSE, dQ: 24 sampled rows of query heads 0, 7, 8, 15; dK, dV: KV group 0 at keys "
+                  "0-127, 32768-32895 and the last 100; dS: query heads 0-7 (every row)",
+                  {"o": e_o, "lse": e_l, "dq": e_dq, "dk": e_dk, "dv": e_dv, "ds": e_ds, "ds_head_max": e_ds_head})
 
 
 def test_full_workload5_varlen_sampled_sequences():
-    """64 packed sequences: whole KV groups of four sequences, incl. shortest and longest."""
+    """64 packed sequences: whole KV groups of four sequences (incl. the
+    shortest and longest) against the oracle, and dS of two heads over all
+    64 sequences."""
     w = WORKLOADS[5]
     say("case workload 5", w.name)
     inp = make_inputs(w)
     gpu = run_gpu(inp, w.max_seqlen, w.softmax_scale, 0)
     lens = np.array(w.lengths)
     seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 2, 63})
+    group_errs = []
     for g in (1, 6):
         refs = _kv_group_reference(inp, w.softmax_scale, 0, g, seqs=seqs)
-        _check_group(gpu, refs, g, w.name)
-    e_ds = _ds_self_consistency(gpu, inp)
-    say(f"  ds(self)={e_ds:.2e}")
-    assert e_ds <= 1e-3
+        group_errs.append(_check_group(gpu, refs, g, w.name))
+    q, k, v, do, s, cu = (inp[n] for n in ("q", "k", "v", "dout", "sinks", "cu_seqlens"))
+    heads = [9, 50]
+    ds_ref = np.zeros(len(heads))
+    grp = w.num_q_heads // w.num_kv_heads
+    for n, h in enumerate(heads):
+        # head h alone (a one-head problem with its KV head), converted once
+        sub = [t[:, h:h + 1].double().numpy() for t in (q, do)]
+        kv = [t[:, h // grp:h // grp + 1].double().numpy() for t in (k, v)]
+        for seq in range(len(lens)):
+            _, _, part = oracle.backward_keys_blocked(sub[0], kv[0], kv[1], s[h:h + 1], sub[1], cu,
+                                                      w.softmax_scale, 0, seq, 0, [])
+            ds_ref[n] += part[0]
+    e_ds = rel_l2(gpu["ds"][heads], ds_ref)
+    e_ds_head = _ds_head_max(gpu["ds"][heads], ds_ref)
+    say(f"  dS heads {heads}: {e_ds:.2e} (worst head {e_ds_head:.2e}); self-consistency "
+        f"{_ds_self_consistency(gpu, inp):.2e}")
+    assert e_ds <= TOL_DS
+    a, b = group_errs
+    errs = {n: max(a[n], b[n]) for n in ("o", "lse")}
+    errs.update({n: math.sqrt((a[n] ** 2 * a["_den_" + n] + b[n] ** 2 * b["_den_" + n]) /
+                              (a["_den_" + n] + b["_den_" + n])) for n in ("dq", "dk", "dv")})
+    errs["ds"] = e_ds
+    errs["ds_head_max"] = e_ds_head
+    record_errors(w.name, f"O, LSE, dQ, dK, dV: KV groups 1 and 6 over sequences {seqs} (every row and key); "
+                  f"dS: query heads {heads} over all 64 sequences", errs)

@@ -333,6 +333,36 @@ def test_row_and_key_helpers_match_full_computation():
                 np.testing.assert_allclose(dv_k, dv[b + keys, g], atol=1e-13)
 
 
+@pytest.mark.parametrize("window,sink_value", [(0, None), (6, None), (0, -math.inf), (3, 30.0)])
+def test_blocked_key_helper_matches_backward_and_sdpa(window, sink_value):
+    """backward_keys_blocked: dK, dV at a key set and the per-sequence sink
+    gradients, against backward and directly against the SDPA reference."""
+    lengths, hq, hkv, d = (45, 0, 70), 6, 2, 8
+    q, k, v, do, s, cu = _inputs(lengths, hq, hkv, d, seed=37 + window, sink_value=sink_value)
+    scale = 0.4
+    dq, dk, dv, ds = oracle.backward(q, k, v, s, do, cu, scale, window)
+    _, _, _, dK, dV, dS = sdpa_with_sink_column(q, k, v, do, s, cu, scale, window)
+    ds_sum = np.zeros(hq)
+    for seq in range(len(lengths)):
+        b, L = int(cu[seq]), int(lengths[seq])
+        keys = np.array([j for j in (0, 1, 7, 31, 44, 69) if j < L], dtype=np.int64)
+        for g in range(hkv):
+            dk_k, dv_k, ds_g = oracle.backward_keys_blocked(q, k, v, s, do, cu, scale, window, seq, g,
+                                                             keys, row_block=16)
+            np.testing.assert_allclose(dk_k, dk[b + keys, g], atol=1e-13)
+            np.testing.assert_allclose(dv_k, dv[b + keys, g], atol=1e-13)
+            np.testing.assert_allclose(dk_k, dK[b + keys, g], atol=1e-11)
+            np.testing.assert_allclose(dv_k, dV[b + keys, g], atol=1e-11)
+            for h, val in ds_g.items():
+                ds_sum[h] += val
+    np.testing.assert_allclose(ds_sum, ds, atol=1e-13)
+    np.testing.assert_allclose(ds_sum, dS, atol=1e-11)
+    # a head subset and an empty key set give the same sink gradients
+    _, _, ds_one = oracle.backward_keys_blocked(q, k, v, s, do, cu, scale, window, 2, 1, [], heads=[4])
+    _, _, ds_all = oracle.backward_keys_blocked(q, k, v, s, do, cu, scale, window, 2, 1, [0, 5])
+    assert ds_one[4] == pytest.approx(ds_all[4], abs=1e-14)
+
+
 # ---------------------------------------------------------------------------
 # Planted mistakes: each mutated oracle must fail at least one pin above.
 
