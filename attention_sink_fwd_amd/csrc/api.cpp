@@ -301,6 +301,7 @@ int bwd_enqueue(const sink_attn_params* p, const BwdTensors& t, void* workspace,
   auto carve = [&](size_t bytes) { float* f = reinterpret_cast<float*>(wsb + off); off += bytes; return f; };
   a.ndelta = carve(ws.ndelta);
   a.nlse = carve(ws.nlse);
+  a.qscaled = reinterpret_cast<bf16_raw*>(carve(ws.qscaled));
   a.dk_part = carve(ws.dk_part);
   a.dv_part = carve(ws.dv_part);
   a.dsink_part = carve(ws.dsink_part);

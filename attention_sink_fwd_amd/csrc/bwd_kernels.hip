@@ -33,12 +33,14 @@
 // No float atomics anywhere: every gradient is a fixed-order sum, so the
 // backward pass is bitwise reproducible run to run.
 //
-// The score product's register-resident operand (Q in the dQ kernel, K in
-// the dK/dV kernel) is multiplied by scale * log2(e) once, when it is loaded,
-// and the score accumulators start from -LSE_i log2(e): they then hold
-// log2 P directly, so P = exp2(acc) needs no per-score multiply.  The scaled
-// operand is rounded to bf16 once (relative 2^-9 per element, about 2e-3 in
-// the exponent for d = 64: below the bf16 rounding P itself gets).
+// Every kernel scores with the same operands: q multiplied by
+// scale * log2(e) and rounded to bf16 once (as the forward kernel does), and
+// k as given.  The score accumulators start from -LSE_i log2(e): they then
+// hold log2 P directly, so P = exp2(acc) needs no per-score multiply, and P
+// in the backward is the forward's P up to float accumulation order.  The dQ
+// kernel forms the scaled query for its own rows and stores it to the
+// workspace for the dK/dV kernel, which scores S = (q scale log2 e) K^T and
+// forms dK = ln(2) dS^T (q scale log2 e) (= scale dS^T q).
 //
 // dQ is not accumulated with float atomics across key tiles: on this chip
 // float atomics retire at about 0.3 G element-operations per microsecond,
@@ -139,7 +141,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int qs = a.num_q_heads * hd, ks = a.num_kv_heads * hd;  // row strides (< 2^31 elements)
   // Base pointers of this sequence and the first head: row i of head hq0 + j
   // is base + i * stride + j * hd (Q, dO) or base + j * T + i (statistics).
-  const TIn* __restrict__ Qh = (const TIn*)a.q + (long)bos * qs + hq0 * hd;
+  // Q as the forward and dQ kernels score with it: bf16(q scale log2 e)
+  // (written by the dQ kernel), so P here equals theirs.
+  const bf16* __restrict__ Qh = (const bf16*)a.qscaled + (long)bos * qs + hq0 * hd;
   const TIn* __restrict__ dOh = (const TIn*)a.dout + (long)bos * qs + hq0 * hd;
   const TIn* __restrict__ Kg = (const TIn*)a.k + (long)bos * ks + g * hd;
   const TIn* __restrict__ Vg = (const TIn*)a.v + (long)bos * ks + g * hd;
@@ -171,7 +175,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     const int q0 = pt * kBM;
     if constexpr (kDirect) {
       const int rem = L - q0;  // rows from the tile's first on
-      const bf16* qb = (const bf16*)Qh + pj * hd + (long)q0 * qs;
+      const bf16* qb = Qh + pj * hd + (long)q0 * qs;
       const bf16* ob = (const bf16*)dOh + pj * hd + (long)q0 * qs;
       uint32_t off[2] = {voff[0], voff[1]};
       uint32_t soff = (uint32_t)lane * (uint32_t)sizeof(float);
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int d0 = 16 * c + 8 * h2;
-      kf[c] = d0 < hd ? __builtin_convertvector(load8f(Kg + krow * ks + d0) * a.scale_log2, bf16x8) : zero8();
+      kf[c] = d0 < hd ? load8(Kg + krow * ks + d0) : zero8();
       vf[c] = d0 < hd ? load8(Vg + krow * ks + d0) : zero8();
     }
   }
@@ -343,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
       for (int r = 0; r < 16; ++r) {
         const int key = wk_lo + 8 * (r >> 2) + 4 * h2 + (r & 3);
         if (key < L) {
-          dk_g[key * ks + d] = (TIn)(dk[db][r] * a.scale);
+          dk_g[key * ks + d] = (TIn)(dk[db][r] * kLn2);
           dv_g[key * ks + d] = (TIn)dv[db][r];
         }
       }
@@ -363,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     for (int r = 0; r < 16; ++r) {
       const int key = wk_lo + 8 * (r >> 2) + 4 * h2 + (r & 3);
       if (key < L) {
-        dk_g[key * ks + d] = dk[db][r] * a.scale;
+        dk_g[key * ks + d] = dk[db][r] * kLn2;
         dv_g[key * ks + d] = dv[db][r];
       }
     }
@@ -491,6 +495,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
   wait_vmem_all();  // fragments and the first two tiles resident (see wait_vmem_all)
   issue_fence();
+  if constexpr (kDirect) {
+    // The scaled query, the dK/dV kernel's score operand, goes out now so its
+    // stores drain during the loop: through this wavefront's 4 KB of the third
+    // stage (idle until the first step's prefetch, which follows that step's
+    // barrier), so that 8 lanes store the 128 contiguous bytes of one row of
+    // one head.  The loop's first wait (at most 4 operations in flight) then
+    // passes at once; tile t0 + 1 is resident already, and from tile t0 + 2
+    // on each wait also covers these older stores.
+    bf16* ep = (bf16*)&stage[2] + w * (32 * kD);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) *(bf16x8*)(ep + l32 * kD + (((2 * c + h2) ^ (l32 & 7)) << 3)) = qf[c];
+    issue_fence();  // the reads below take other lanes' writes (LDS keeps a wavefront's order)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 8 * i + (lane >> 3), j = lane & 7;
+      const bf16x8 x = *(const bf16x8*)(ep + c * kD + ((j ^ (c & 7)) << 3));
+      const int n = 32 * w + c;
+      const int row = q0 + n / hp;
+      if (row < L) *(bf16x8*)((bf16*)a.qscaled + (long)(bos + row) * qs + (hb * hp + n % hp) * kD + 8 * j) = x;
+    }
+    issue_fence();
+  }
   // Row statistics: the accumulator seeds of this kernel and of the dK/dV
   // kernel (stored after the loop, so the loop's load waits do not cover
   // them).
@@ -581,6 +607,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     a.nlse[(long)hq * T + bos + qrow] = nlse;
     a.ndelta[(long)hq * T + bos + qrow] = nD;
   }
+  if (!kDirect && qrow < L) {
+    bf16* qsc = (bf16*)a.qscaled + (long)(bos + qrow) * qs + hq * hd;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int d0 = 16 * c + 8 * h2;
+      if (d0 < hd) *(bf16x8*)(qsc + d0) = qf[c];
+    }
+  }
   {
     // Sum per head: lanes with equal lane % hp hold the same head.
     __shared__ float wsum[4][32];
@@ -654,10 +688,11 @@ BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d, int 
   BwdWorkspace w;
   w.ndelta = up((size_t)hq * total_tokens * sizeof(float));
   w.nlse = w.ndelta;
+  w.qscaled = up((size_t)total_tokens * hq * d * sizeof(bf16));
   w.dk_part = P > 1 ? up((size_t)P * total_tokens * hkv * d * sizeof(float)) : 0;
   w.dv_part = w.dk_part;
   w.dsink_part = up((size_t)bwd_dsink_parts(max_seqlen, num_seqs, heads_per_tile) * hq * sizeof(float));
-  w.total = w.ndelta + w.nlse + w.dk_part + w.dv_part + w.dsink_part;
+  w.total = w.ndelta + w.nlse + w.qscaled + w.dk_part + w.dv_part + w.dsink_part;
   return w;
 }
 

@@ -6,6 +6,8 @@
 
 namespace sinkattn {
 
+typedef unsigned short bf16_raw;  // bfloat16 storage as seen by host code
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -38,6 +40,7 @@ struct BwdArgs {
   void* dv;
   float* dsinks;
   float* ndelta;  // workspace: -D_i = -(dO_i . O_i), [Hq, T]
+  bf16_raw* qscaled;  // workspace: bf16(q * scale * log2 e), [T, Hq, d] (the score operand of every kernel)
   float* nlse;    // workspace: -LSE_i log2(e), [Hq, T]
   float* dk_part;  // workspace: float dK partial sums, [P, T, Hkv, d], P = (Hq/Hkv) / dkdv_heads
   float* dv_part;  // workspace: float dV partial sums, same shape (both unused when P == 1)
@@ -51,7 +54,7 @@ struct BwdArgs {
 
 // Workspace sections (bytes, each rounded up to 256).
 struct BwdWorkspace {
-  size_t ndelta, nlse, dk_part, dv_part, dsink_part, total;
+  size_t ndelta, nlse, qscaled, dk_part, dv_part, dsink_part, total;
 };
 BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d, int max_seqlen, int num_seqs,
                                   int dkdv_heads, int heads_per_tile);

@@ -9,11 +9,11 @@ Default workload: GPT-OSS-20B-shaped attention, B=1, Hq=64, Hkv=8, d=64,
 L=4096, causal, bf16.
 
 Prints ONE JSON line.  Throughput counts algorithmic flops (14*d per visible
-query/key pair per query head: 4d forward, 10d backward).  An untimed pass
-first brackets every kernel with HIP events (kernel_ms) and picks the
-dominant (longest) matrix-core kernel; in the timed region only that kernel
-is bracketed, with two events per step on the stream it runs on, and the
-roofline object reports it.
+query/key pair per query head: 4d forward, 10d backward).  Untimed passes
+first time each kernel alone, bracketed by two HIP events per step
+(kernel_ms), and pick the dominant (longest) matrix-core kernel; in the
+timed region only that kernel is bracketed, the same way, on the stream it
+runs on, and the roofline object reports it.
 """
 from __future__ import annotations
 
@@ -362,22 +362,35 @@ def main():
                              dq=dq, dk=dk, dv=dv, dsinks=ds, workspace=ws, stream=stream)
         _lib.check(lib.sink_attn_set_bwd_events(None))
 
-    # Untimed pass: every kernel bracketed by events, for the per-kernel
-    # breakdown and to find the dominant kernel.
+    # Untimed passes, one per kernel, each bracketing only that kernel with
+    # two events per step (as the timed region brackets the dominant one):
+    # the per-kernel breakdown and the dominant kernel.  (Bracketing every
+    # kernel in one pass would add an event packet between each pair of
+    # kernels and inflate each kernel's time.)
     nb = min(args.steps, 20)
-    evb = [[hip.event() for _ in range(6)] for _ in range(nb)]
-    run_steps(nb, lambda i: (evb[i][0], evb[i][1]),
-              lambda i: (evb[i][2].value, evb[i][3].value, evb[i][4].value, evb[i][5].value))
-    torch.cuda.synchronize()
 
     def avg(evs, a, b):
         return sum(hip.ms(e[a], e[b]) for e in evs) / len(evs)
 
-    kernel_ms = {"fwd": avg(evb, 0, 1), "bwd_dq": avg(evb, 2, 3), "bwd_dkdv": avg(evb, 3, 4),
-                 "bwd_post": avg(evb, 4, 5)}
-    for row in evb:
-        for e in row:
-            hip.destroy(e)
+    kernel_ms = {}
+    for kname in ("fwd", "bwd_dq", "bwd_dkdv", "bwd_post"):
+        evb = [[hip.event() for _ in range(2)] for _ in range(nb)]
+        if kname == "fwd":
+            fe, be = (lambda i: (evb[i][0], evb[i][1])), (lambda i: (None, None, None, None))
+        else:
+            j = {"bwd_dq": 0, "bwd_dkdv": 1, "bwd_post": 2}[kname]
+
+            def be(i, j=j):
+                h = [None, None, None, None]
+                h[j], h[j + 1] = evb[i][0].value, evb[i][1].value
+                return tuple(h)
+            fe = lambda i: None  # noqa: E731
+        run_steps(nb, fe, be)
+        torch.cuda.synchronize()
+        kernel_ms[kname] = avg(evb, 0, 1)
+        for row in evb:
+            for e in row:
+                hip.destroy(e)
     kms = {kname: kernel_ms[kname] for kname in ("fwd", "bwd_dkdv", "bwd_dq")}
     dom = max(kms, key=kms.get)
 
@@ -412,6 +425,9 @@ def main():
     pairs = w.visible_pairs()
     algo = {"fwd": 4.0 * w.head_dim * pairs, "bwd_dkdv": 8.0 * w.head_dim * pairs,
             "bwd_dq": 2.0 * w.head_dim * pairs}
+    # Matrix work each kernel executes: the dQ kernel recomputes S and dP
+    # (2 more products per pair than it is credited with).
+    executed = {"fwd": algo["fwd"], "bwd_dkdv": algo["bwd_dkdv"], "bwd_dq": 6.0 * w.head_dim * pairs}
     dom_tflops = algo[dom] / (dom_ms * 1e-3) / 1e12
     traffic = traffic_for_current_kernel(dom)
     result = {
@@ -441,7 +457,18 @@ def main():
         },
         "pct_bf16_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "kernel_ms": {kname: round(val, 4) for kname, val in kernel_ms.items()},
+        "kernel_ms_note": ("each kernel timed in its own untimed pass, bracketed alone by two events per "
+                           "step; sum minus ms_per_step: event overhead and launch gaps"),
+        "kernel_sum_minus_step_ms": round(sum(kernel_ms.values()) - ms, 4),
         "kernel_tflops": {kname: round(algo[kname] / (kms[kname] * 1e-3) / 1e12, 1) for kname in kms},
+        "kernel_frac": {
+            "fwd": round(algo["fwd"] / (kms["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "bwd_dq": {
+                "credited": round(algo["bwd_dq"] / (kms["bwd_dq"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "executed": round(executed["bwd_dq"] / (kms["bwd_dq"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            },
+            "bwd_dkdv": round(algo["bwd_dkdv"] / (kms["bwd_dkdv"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        },
         "roofline": {
             "kernel": dom,
             "kernel_ms": round(dom_ms, 4),

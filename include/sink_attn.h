@@ -165,9 +165,11 @@ int sink_attn_fwd_paged(const sink_attn_params *p, const sink_attn_paged_kv *kv,
 
 /*
  * Bytes of device workspace sink_attn_bwd needs for these parameters
- * (float row statistics, float dK/dV partial sums of the head groups and
- * per-query-tile dS partials, 256-byte aligned sections; the last depends on
- * max_seqlen and num_seqs).  Returns 0 when the parameters are invalid.
+ * (float row statistics [2, Hq, T], the bf16 scaled queries
+ * q * softmax_scale * log2(e) [T, Hq, d] that every kernel scores with,
+ * float dK/dV partial sums of the head groups and per-query-tile dS
+ * partials, 256-byte aligned sections; the last depends on max_seqlen and
+ * num_seqs).  Returns 0 when the parameters are invalid.
  */
 size_t sink_attn_bwd_workspace_size(const sink_attn_params *p);
 
@@ -217,9 +219,11 @@ int sink_attn_bwd(const sink_attn_params *p, const void *q, const void *k, const
  * results are then bitwise identical); otherwise the dK/dV kernel takes more
  * query heads per workgroup (fewer float partial sums, only the order of the
  * dK/dV additions changes), unless SINK_ATTN_DKDV_HEADS fixes the split.  A
- * shape whose workspace does not fit in any split (about num_q_heads *
- * total_tokens above 8 million) returns SINK_ATTN_ERR_UNSUPPORTED with the
- * size it needs, before anything is enqueued.
+ * shape whose workspace does not fit in any split returns
+ * SINK_ATTN_ERR_UNSUPPORTED with the size it needs, before anything is
+ * enqueued: the row statistics and the scaled queries alone take
+ * 8 + 2 * head_dim bytes per query head and token (num_q_heads *
+ * total_tokens up to about 490 thousand at head_dim 64).
  *   All calls on one device share its buffer: calls that overlap in time on
  * one device (two streams, or two threads) race and give wrong results; calls
  * ordered on one stream are safe.  The buffer's contents on entry are ignored

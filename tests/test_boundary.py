@@ -154,8 +154,9 @@ def test_workspace_size_and_too_small():
     # a KV group, so a tile holds 128 / 4 rows
     parts = (T + 31) // 32
     # dK/dV partial sums: one plane per head group; this small shape takes one
-    # head per group (P = hq / hkv planes)
-    want = 2 * up(4 * hq * T) + 2 * up(4 * (hq // hkv) * T * hkv * d) + up(4 * parts * hq)
+    # head per group (P = hq / hkv planes); the scaled queries are bf16 [T, Hq, d]
+    want = (2 * up(4 * hq * T) + up(2 * T * hq * d) + 2 * up(4 * (hq // hkv) * T * hkv * d)
+            + up(4 * parts * hq))
     assert lib.sink_attn_bwd_workspace_size(ctypes.byref(p)) == want
     assert _bwd(p, ws_bytes=want - 1) == _lib.SINK_ATTN_ERR_WORKSPACE_TOO_SMALL
     assert "workspace" in lib.sink_attn_last_error().decode()
@@ -169,7 +170,8 @@ def test_workspace_follows_dkdv_heads(monkeypatch, heads, planes):
     T, hq, hkv, d = 1000, 8, 2, 64
     p = _good_params(T, hq, hkv, d)
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    want = 2 * up(4 * hq * T) + 2 * up(4 * planes * T * hkv * d) + up(4 * ((T + 31) // 32) * hq)
+    want = (2 * up(4 * hq * T) + up(2 * T * hq * d) + 2 * up(4 * planes * T * hkv * d)
+            + up(4 * ((T + 31) // 32) * hq))
     assert lib.sink_attn_bwd_workspace_size(ctypes.byref(p)) == want
 
 
@@ -181,7 +183,7 @@ def test_workspace_follows_pack_heads(monkeypatch, pack, rows):
     T, hq, hkv, d = 1000, 8, 2, 64
     p = _good_params(T, hq, hkv, d)
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    want = 2 * up(4 * hq * T) + up(4 * ((T + rows - 1) // rows) * hq)
+    want = 2 * up(4 * hq * T) + up(2 * T * hq * d) + up(4 * ((T + rows - 1) // rows) * hq)
     assert lib.sink_attn_bwd_workspace_size(ctypes.byref(p)) == want
 
 
