@@ -115,7 +115,11 @@ constexpr int kStages = 3;
 // When it covers the whole group it writes dK, dV directly; otherwise it
 // stores its float partial sums to its own plane, which the post kernel adds
 // to the others in a fixed order.
-template <typename TIn, bool kDirect>
+//
+// kWindow: a window may cut some sequence; false fixes the window at 0, which
+// compiles every window test out (plain causal attention, or a window no
+// shorter than the longest sequence).
+template <typename TIn, bool kDirect, bool kWindow>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   // Three separate LDS objects (not an array): with every access naming its
   // stage at compile time, the compiler can tell that reading one stage does
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   if (k0 >= L) return;
 
   // The direct path is only built for head_dim == kD.
-  const int hd = kDirect ? kD : a.head_dim, T = a.total_tokens, window = a.window;
+  const int hd = kDirect ? kD : a.head_dim, T = a.total_tokens, window = kWindow ? a.window : 0;
   const int g = hq0 / grp;
   const int qs = a.num_q_heads * hd, ks = a.num_kv_heads * hd;  // row strides (< 2^31 elements)
   // Base pointers of this sequence and the first head: row i of head hq0 + j
@@ -258,8 +262,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
     const bool active = wk_lo < L && wk_lo <= qb + kBM - 1 && !(window > 0 && qb - wk_hi >= window);
     if (active) {
-      const bool need_mask = (wk_hi > qb) || (qb + kBM > L) ||
-                             (window > 0 && qb + kBM - 1 - wk_lo >= window);
+      // Bounds that cut this step for some (row, key) of the wavefront: rows
+      // before a key (causal), and rows past a key's window or past the
+      // sequence; masking tests only those.
+      const bool mask_lo = wk_hi > qb;
+      const bool mask_hi = (qb + kBM > L) || (window > 0 && qb + kBM - 1 - wk_lo >= window);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         // S and dP for query rows 32*mb .. 32*mb+31 of the tile; register r
@@ -292,8 +299,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         // rows past the end of the sequence), with lo and hi per lane.
         const int rbase = qb + 32 * mb + 8 * h2;
         const int lo = key_n - rbase;
-        const int hi = min(L - rbase, window > 0 ? lo + window : 0x7fffffff);
-        auto softmax_grad = [&](auto masked) {
+        const int hi = window > 0 ? min(L - rbase, lo + window) : L - rbase;
+        auto softmax_grad = [&](auto test_lo, auto test_hi) {
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb) {
             f32x8 pv, dv8;
@@ -301,10 +308,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
             for (int i = 0; i < 8; ++i) {
               const int r = 8 * hb + i;
               float p = fast_exp2(s[r]);
-              if constexpr (decltype(masked)::value) {
-                const int idx = 16 * hb + i;
-                p = (idx >= lo && idx < hi) ? p : 0.0f;
-              }
+              const int idx = 16 * hb + i;
+              bool vis = true;
+              if constexpr (decltype(test_lo)::value) vis = vis && idx >= lo;
+              if constexpr (decltype(test_hi)::value) vis = vis && idx < hi;
+              p = vis ? p : 0.0f;
               pv[i] = p;
               dv8[i] = p * dp[r];
             }
@@ -312,10 +320,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
             df[hb] = __builtin_convertvector(dv8, bf16x8);
           }
         };
-        if (need_mask)
-          softmax_grad(std::true_type{});
-        else
-          softmax_grad(std::false_type{});
+        if constexpr (kWindow) {
+          // Windowed steps are mostly cut on one side only: test just that one.
+          if (mask_lo && mask_hi)
+            softmax_grad(std::true_type{}, std::true_type{});
+          else if (mask_lo)
+            softmax_grad(std::true_type{}, std::false_type{});
+          else if (mask_hi)
+            softmax_grad(std::false_type{}, std::true_type{});
+          else
+            softmax_grad(std::false_type{}, std::false_type{});
+        } else {
+          // Plain causal: few masked steps, and fewer code paths schedule
+          // the unmasked one better.
+          if (mask_lo || mask_hi)
+            softmax_grad(std::true_type{}, std::true_type{});
+          else
+            softmax_grad(std::false_type{}, std::false_type{});
+        }
         // dV += P^T dO and dK += dS^T Q over these 32 rows (scale applied at the end).
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
@@ -388,7 +410,8 @@ struct __attribute__((aligned(16))) KStage {
 // scale log2 e; accumulators seeded with -LSE log2 e and -D of the lane's row), P^T = exp2(S^T),
 // dS^T = P^T dP^T, dQ^T += K^T dS^T with K^T from the row-major K tile
 // through transposing reads.  dQ is written once, in the output type.
-template <typename TIn, bool kDirect>
+// (kWindow as for the dK/dV kernel.)
+template <typename TIn, bool kDirect, bool kWindow>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ KStage stage[kStages];
 
@@ -396,7 +419,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
   // The direct path is only built for head_dim == kD.
-  const int hd = kDirect ? kD : a.head_dim, T = a.total_tokens, window = a.window;
+  const int hd = kDirect ? kD : a.head_dim, T = a.total_tokens, window = kWindow ? a.window : 0;
   // Column n = 32 w + l32 is query row q0 + n / hp of head hb * hp + n % hp
   // (hp query heads of one KV group share the workgroup's K/V tiles).
   const int hp = a.heads_per_tile, rows = kQT / hp;
@@ -560,12 +583,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         dp[blk] = mfma32(frag_row(st.v, kr, 16 * c + 8 * h2), of[c], dp[blk]);
       }
     }
-    const bool need_mask = (kb + kKT - 1 > wq_lo) || (window > 0 && wq_hi - kb >= window);
+    // Bounds that cut this tile for some row of the wavefront (keys after a
+    // row; keys left of a row's window); masking tests only those.
+    const bool mask_hi = kb + kKT - 1 > wq_lo;
+    const bool mask_lo = window > 0 && wq_hi - kb >= window;
     // key index 32*blk + 16*(r/8) + r%8 (+ 8*h2) is visible iff lo <= idx < hi
-    const int lo = window > 0 ? qrow - window + 1 - kb - 8 * h2 : -0x7fffffff;
+    const int lo = qrow - window + 1 - kb - 8 * h2;
     const int hi = qrow + 1 - kb - 8 * h2;
     bf16x8 df[4];
-    auto grad = [&](auto masked) {
+    auto grad = [&](auto test_lo, auto test_hi) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         f32x8 v;
@@ -573,19 +599,31 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         for (int i = 0; i < 8; ++i) {
           const int r = 8 * (c & 1) + i;
           float p = fast_exp2(s[c >> 1][r]);
-          if constexpr (decltype(masked)::value) {
-            const int idx = 16 * c + i;
-            p = (idx >= lo && idx < hi) ? p : 0.0f;
-          }
+          const int idx = 16 * c + i;
+          bool vis = true;
+          if constexpr (decltype(test_lo)::value) vis = vis && idx >= lo;
+          if constexpr (decltype(test_hi)::value) vis = vis && idx < hi;
+          p = vis ? p : 0.0f;
           v[i] = p * dp[c >> 1][r];
         }
         df[c] = __builtin_convertvector(v, bf16x8);
       }
     };
-    if (need_mask)
-      grad(std::true_type{});
-    else
-      grad(std::false_type{});
+    if constexpr (kWindow) {
+      if (mask_hi && mask_lo)
+        grad(std::true_type{}, std::true_type{});
+      else if (mask_hi)
+        grad(std::false_type{}, std::true_type{});
+      else if (mask_lo)
+        grad(std::true_type{}, std::false_type{});
+      else
+        grad(std::false_type{}, std::false_type{});
+    } else {
+      if (mask_hi)
+        grad(std::false_type{}, std::true_type{});
+      else
+        grad(std::false_type{}, std::false_type{});
+    }
     // dQ^T += K^T dS^T (chunk c = keys 16c .. 16c+15 of the tile).
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
@@ -730,26 +768,32 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs,
   const int qrows = kQT / a.heads_per_tile;
   const dim3 grid_q((max_seqlen + qrows - 1) / qrows * (Hq / a.heads_per_tile) * num_seqs);
   const bool direct = dtype == 0 && a.head_dim == kD;
+  // The window-free instances when no sequence is cut by the window.
+  const bool windowed = a.window > 0 && a.window < max_seqlen;
   auto mark = [&](int i) { return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess; };
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return e;
   if (T > 0) {
-    if (direct)
-      hipLaunchKernelGGL((bwd_dq_kernel<bf16, true>), grid_q, dim3(256), 0, stream, a);
+    if (direct && windowed)
+      hipLaunchKernelGGL((bwd_dq_kernel<bf16, true, true>), grid_q, dim3(256), 0, stream, a);
+    else if (direct)
+      hipLaunchKernelGGL((bwd_dq_kernel<bf16, true, false>), grid_q, dim3(256), 0, stream, a);
     else if (dtype == 0)
-      hipLaunchKernelGGL((bwd_dq_kernel<bf16, false>), grid_q, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<bf16, false, true>), grid_q, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<float, false>), grid_q, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dq_kernel<float, false, true>), grid_q, dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark(1)) != hipSuccess) return e;
   if (T > 0) {
-    if (direct)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, true>), grid_kv, dim3(256), 0, stream, a);
+    if (direct && windowed)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, true, true>), grid_kv, dim3(256), 0, stream, a);
+    else if (direct)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, true, false>), grid_kv, dim3(256), 0, stream, a);
     else if (dtype == 0)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, false>), grid_kv, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, false, true>), grid_kv, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<float, false>), grid_kv, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<float, false, true>), grid_kv, dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark(2)) != hipSuccess) return e;
