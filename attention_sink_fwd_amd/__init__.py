@@ -5,6 +5,7 @@ from .binding import (  # noqa: F401
     make_params,
     sink_attention,
     sink_attn_bwd,
+    sink_attn_bwd_fused,
     sink_attn_bwd_noalloc,
     sink_attn_bwd_workspace_size,
     sink_attn_fwd,

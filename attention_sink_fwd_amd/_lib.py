@@ -27,6 +27,7 @@ EXPORTED_SYMBOLS = (
     "sink_attn_fwd_paged",
     "sink_attn_bwd",
     "sink_attn_bwd_workspace_size",
+    "sink_attn_bwd_fused",
     "sink_attn_bwd_noalloc",
     "sink_attn_set_bwd_events",
     "sink_attn_status_string",
@@ -96,6 +97,8 @@ def load() -> ctypes.CDLL:
     lib.sink_attn_bwd_noalloc.restype = ctypes.c_int
     lib.sink_attn_bwd_workspace_size.argtypes = [P]
     lib.sink_attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.sink_attn_bwd_fused.argtypes = [P]
+    lib.sink_attn_bwd_fused.restype = ctypes.c_int
     lib.sink_attn_set_bwd_events.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
     lib.sink_attn_set_bwd_events.restype = ctypes.c_int
     i32, i64 = ctypes.c_int32, ctypes.c_int64

@@ -125,6 +125,16 @@ def sink_attn_bwd_workspace_size(q, k, cu_seqlens, max_seqlen, softmax_scale=Non
     return int(lib.sink_attn_bwd_workspace_size(ctypes.byref(p)))
 
 
+def sink_attn_bwd_fused(q, k, cu_seqlens, max_seqlen, softmax_scale=None, window=0) -> bool:
+    """True when sink_attn_bwd runs the fused short-window kernel for this shape."""
+    lib = _lib.load()
+    p = make_params(q, k, cu_seqlens, max_seqlen, softmax_scale, window)
+    r = int(lib.sink_attn_bwd_fused(ctypes.byref(p)))
+    if r < 0:
+        _lib.check(-r)
+    return r == 1
+
+
 def sink_attn_bwd(q, k, v, sinks, o, lse, dout, cu_seqlens, max_seqlen, softmax_scale=None,
                   window=0, dq=None, dk=None, dv=None, dsinks=None, workspace=None,
                   stream=None):

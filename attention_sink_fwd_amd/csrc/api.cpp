@@ -250,9 +250,18 @@ int resolve_dkdv_heads(const sink_attn_params* p, int* out) {
   return SINK_ATTN_OK;
 }
 
-sinkattn::BwdWorkspace workspace_layout(const sink_attn_params* p, int dkdv_heads, int pack_heads) {
+// The fused short-window backward kernel when the shape allows it, unless
+// SINK_ATTN_BWD_FUSED=0 asks for the dQ and dK/dV kernels.
+bool use_fused(const sink_attn_params* p) {
+  const char* env = std::getenv("SINK_ATTN_BWD_FUSED");
+  if (env && env[0] == '0') return false;
+  return sinkattn::bwd_window_fusable(p->dtype, p->head_dim, p->window, p->max_seqlen, p->num_q_heads,
+                                      p->num_kv_heads);
+}
+
+sinkattn::BwdWorkspace workspace_layout(const sink_attn_params* p, int dkdv_heads, int pack_heads, bool fused) {
   return sinkattn::bwd_workspace_layout(p->total_tokens, p->num_q_heads, p->num_kv_heads, p->head_dim, p->max_seqlen,
-                                        p->num_seqs, dkdv_heads, pack_heads);
+                                        p->num_seqs, dkdv_heads, pack_heads, fused);
 }
 
 }  // namespace
@@ -277,21 +286,22 @@ int bwd_check(const sink_attn_params* p, const BwdTensors& t) {
   return SINK_ATTN_OK;
 }
 
-int bwd_split(const sink_attn_params* p, int* dkdv_heads, int* pack_heads, bool* dkdv_overridden) {
-  *dkdv_overridden = std::getenv("SINK_ATTN_DKDV_HEADS") != nullptr;
-  SA_CHECK(resolve_dkdv_heads(p, dkdv_heads));
-  return resolve_pack_heads(p, 32, pack_heads);
+int bwd_split(const sink_attn_params* p, BwdSplit* split) {
+  split->dkdv_overridden = std::getenv("SINK_ATTN_DKDV_HEADS") != nullptr;
+  split->fused = use_fused(p);
+  SA_CHECK(resolve_dkdv_heads(p, &split->dkdv_heads));
+  return resolve_pack_heads(p, 32, &split->pack_heads);
 }
 
-BwdWorkspace bwd_layout(const sink_attn_params* p, int dkdv_heads, int pack_heads) {
-  return workspace_layout(p, dkdv_heads, pack_heads);
+BwdWorkspace bwd_layout(const sink_attn_params* p, const BwdSplit& split) {
+  return workspace_layout(p, split.dkdv_heads, split.pack_heads, split.fused);
 }
 
-int bwd_enqueue(const sink_attn_params* p, const BwdTensors& t, void* workspace, int dkdv_heads, int pack_heads,
+int bwd_enqueue(const sink_attn_params* p, const BwdTensors& t, void* workspace, const BwdSplit& split,
                 void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   SA_CHECK(maybe_validate_cu(p, s));
-  const BwdWorkspace ws = workspace_layout(p, dkdv_heads, pack_heads);
+  const BwdWorkspace ws = bwd_layout(p, split);
   char* wsb = static_cast<char*>(workspace);
   BwdArgs a{};
   a.q = t.q; a.k = t.k; a.v = t.v; a.o = t.o; a.dout = t.dout; a.lse = t.lse; a.sinks = t.sinks;
@@ -309,8 +319,10 @@ int bwd_enqueue(const sink_attn_params* p, const BwdTensors& t, void* workspace,
   a.total_tokens = p->total_tokens; a.window = p->window; a.num_seqs = p->num_seqs;
   a.scale = p->softmax_scale;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
-  a.dkdv_heads = dkdv_heads;
-  a.heads_per_tile = pack_heads;
+  a.dkdv_heads = split.dkdv_heads;
+  a.heads_per_tile = split.pack_heads;
+  a.fused = split.fused ? 1 : 0;
+  a.dkdv_planes = split.fused ? 2 : p->num_q_heads / p->num_kv_heads / split.dkdv_heads;
   hipError_t e = launch_bwd(a, p->dtype, p->max_seqlen, p->num_seqs, s, g_bwd_events_on ? g_bwd_events : nullptr);
   if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
   return SINK_ATTN_OK;
@@ -321,11 +333,16 @@ int bwd_enqueue(const sink_attn_params* p, const BwdTensors& t, void* workspace,
 extern "C" {
 
 size_t sink_attn_bwd_workspace_size(const sink_attn_params* p) {
-  int hg = 0, hp = 0;
-  if (check_params(p) != SINK_ATTN_OK || resolve_dkdv_heads(p, &hg) != SINK_ATTN_OK ||
-      resolve_pack_heads(p, 32, &hp) != SINK_ATTN_OK)
-    return 0;
-  return workspace_layout(p, hg, hp).total;
+  sinkattn::BwdSplit split;
+  if (check_params(p) != SINK_ATTN_OK || sinkattn::bwd_split(p, &split) != SINK_ATTN_OK) return 0;
+  return sinkattn::bwd_layout(p, split).total;
+}
+
+int sink_attn_bwd_fused(const sink_attn_params* p) {
+  g_last_error[0] = '\0';
+  const int st = check_params(p);
+  if (st != SINK_ATTN_OK) return -st;
+  return use_fused(p) ? 1 : 0;
 }
 
 int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const void* v, const float* sinks,
@@ -334,16 +351,15 @@ int sink_attn_bwd(const sink_attn_params* p, const void* q, const void* k, const
   g_last_error[0] = '\0';
   const sinkattn::BwdTensors t{q, k, v, sinks, o, lse, dout, dq, dk, dv, dsinks};
   SA_CHECK(sinkattn::bwd_check(p, t));
-  int dkdv_heads = 0, pack_heads = 0;
-  SA_CHECK(resolve_dkdv_heads(p, &dkdv_heads));
-  SA_CHECK(resolve_pack_heads(p, 32, &pack_heads));
-  const sinkattn::BwdWorkspace ws = workspace_layout(p, dkdv_heads, pack_heads);
+  sinkattn::BwdSplit split;
+  SA_CHECK(sinkattn::bwd_split(p, &split));
+  const sinkattn::BwdWorkspace ws = sinkattn::bwd_layout(p, split);
   if (workspace_bytes < ws.total)
     return fail(SINK_ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, ws.total);
   if (ws.total > 0 && !workspace) return fail(SINK_ATTN_ERR_INVALID_ARG, "workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(SINK_ATTN_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-  return sinkattn::bwd_enqueue(p, t, workspace, dkdv_heads, pack_heads, stream);
+  return sinkattn::bwd_enqueue(p, t, workspace, split, stream);
 }
 
 int sink_attn_set_bwd_events(void* const* events) {

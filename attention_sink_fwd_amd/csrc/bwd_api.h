@@ -27,15 +27,22 @@ struct BwdTensors {
 // Argument checks of the backward pass (status and sink_attn_last_error text,
 // nothing enqueued on failure).
 int bwd_check(const sink_attn_params* p, const BwdTensors& t);
-// The work split: query heads per dK/dV workgroup and per dQ workgroup (the
-// shape-based choice, or the SINK_ATTN_DKDV_HEADS / SINK_ATTN_PACK_HEADS
-// overrides; *dkdv_overridden tells whether the first was given).
-int bwd_split(const sink_attn_params* p, int* dkdv_heads, int* pack_heads, bool* dkdv_overridden);
+// The work split: the fused short-window kernel or the dQ and dK/dV kernels,
+// and for the latter the query heads per dK/dV workgroup and per dQ
+// workgroup (the shape-based choice, or the SINK_ATTN_BWD_FUSED,
+// SINK_ATTN_DKDV_HEADS and SINK_ATTN_PACK_HEADS overrides; dkdv_overridden
+// tells whether the second was given).
+struct BwdSplit {
+  bool fused = false;
+  int dkdv_heads = 1, pack_heads = 1;
+  bool dkdv_overridden = false;
+};
+int bwd_split(const sink_attn_params* p, BwdSplit* split);
 // Workspace sections for a split.
-BwdWorkspace bwd_layout(const sink_attn_params* p, int dkdv_heads, int pack_heads);
+BwdWorkspace bwd_layout(const sink_attn_params* p, const BwdSplit& split);
 // Carve `workspace` (256-byte aligned, at least bwd_layout(...).total bytes)
 // and enqueue the backward kernels on `stream`.
-int bwd_enqueue(const sink_attn_params* p, const BwdTensors& t, void* workspace, int dkdv_heads, int pack_heads,
+int bwd_enqueue(const sink_attn_params* p, const BwdTensors& t, void* workspace, const BwdSplit& split,
                 void* stream);
 
 }  // namespace sinkattn

@@ -48,6 +48,7 @@
 // whole backward pass.  Recomputing S and dP in the dQ kernel costs two
 // extra matrix products per visible block instead.
 #include <algorithm>
+#include <cstddef>
 #include <type_traits>
 
 #include "device_common.h"
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(BwdArgs a, int conv_block
   }
   // dK, dV = the head groups' partial sums, in group order.
   const long kchunks = (long)a.total_tokens * a.num_kv_heads * a.head_dim / 8;
-  const int P = a.num_q_heads / a.num_kv_heads / a.dkdv_heads;
+  const int P = a.dkdv_planes;
   for (long c = (long)blockIdx.x * kFlatThreads + tid; c < 2 * kchunks; c += (long)conv_blocks * kFlatThreads) {
     const bool is_k = c < kchunks;
     const long e = 8 * (is_k ? c : c - kchunks);
@@ -707,6 +708,430 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fused backward for short sliding windows (window <= 128, head_dim 64, bf16
+// inputs).  Query row i of a 128-row tile sees only keys i - window + 1 .. i,
+// which lie in the tile's own 128 keys and the 128 before them.  One workgroup
+// takes one such query tile and every query head of one KV group, with all
+// 256 keys resident: K in LDS and in registers, V in registers.  Per 64-row
+// step (one head) it forms S, dP, P and dS once, as the dK/dV kernel does
+// (eight wavefronts, 32 keys each), accumulates dK and dV in registers over
+// all the group's heads, and passes dS^T through LDS so that four wavefronts
+// form the step's dQ = scale dS K completely (every key that reaches these
+// rows is in the workgroup).  The other four compute the next step's row
+// statistics meanwhile: D = dO . O, -LSE log2(e), the sink term, and the
+// scaled queries bf16(q scale log2 e) (in place, the same rounding as the
+// forward kernel's).  So Q, dO and O are each read once, dQ written once, and
+// no scaled copy of Q goes through memory.  dK and dV of a key tile get
+// contributions from two workgroups (the tile's own query rows and the next
+// tile's); each writes its float sums to its own plane (0: own rows, 1: the
+// next tile's rows; the last tile of a sequence writes zeros to plane 1) and
+// the post kernel adds the two planes in that order.
+constexpr int kFQ = 128;         // query rows per fused workgroup
+constexpr int kFK = 2 * kFQ;     // keys it sees
+constexpr int kFMaxGroup = 64;   // query heads per KV head the fused kernel takes
+constexpr int kFPrefetchOps = 4; // VMEM instructions per wavefront and step prefetch (q, dO, O, LSE)
+
+struct __attribute__((aligned(16))) FStage {
+  bf16 q[kBM * kD];     // Q tile, swizzled [q][d]; scaled in place before use
+  bf16 dout[kBM * kD];  // dO tile, swizzled [q][d]
+  bf16 o[kBM * kD];     // O tile, swizzled [q][d] (for D only)
+  float lse[kBM];       // LSE of the tile rows (natural log)
+  float nlse[kBM];      // -LSE log2(e)
+  float ndelta[kBM];    // -D
+  float spare[kBM];     // landing area that keeps every wavefront's load count equal
+};
+// The workgroup's LDS in one object, so the layout (and every constant
+// offset between its parts) is fixed.
+struct __attribute__((aligned(16))) FLds {
+  FStage s0, s1, s2;    // ring of 64-row steps
+  bf16 ks[kFK * kD];    // K of the 256 keys, swizzled [key][d]
+  bf16 ds[kFK * kBM];   // dS^T of the current step, swizzled [key][row]
+  float wsum[kFMaxGroup][4];
+};
+constexpr uint32_t kOffDout = offsetof(FStage, dout), kOffO = offsetof(FStage, o);
+constexpr uint32_t kOffLse = offsetof(FStage, lse), kOffNlse = offsetof(FStage, nlse);
+constexpr uint32_t kOffNdelta = offsetof(FStage, ndelta);
+
+// LDS accesses by byte address.  The kernel keeps each per-lane address
+// pattern in one register and adds stage and block offsets as constants,
+// which the instructions take as immediate offsets.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(SA_LDS const void*)p; }
+template <typename V>
+__device__ __forceinline__ V lds_ld(uint32_t a) {
+  return *(SA_LDS const V*)a;
+}
+template <typename V>
+__device__ __forceinline__ void lds_st(uint32_t a, V v) {
+  *(SA_LDS V*)a = v;
+}
+__device__ __forceinline__ bf16x8 lds_tr8(uint32_t a0, uint32_t a1) {
+  i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS i16x4*)a0);
+  i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS i16x4*)a1);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// Byte offset of element (r, col) of a swizzled 64-column bf16 tile.
+__device__ __forceinline__ uint32_t swz_b(int r, int col) { return (uint32_t)swz(r, col) * (uint32_t)sizeof(bf16); }
+// Byte offsets of the two transposing reads of frag_tr_swz(X, 0, n0, lane);
+// frag_tr_swz(X, 16 c, n0, lane) reads 2048 c bytes further.
+__device__ __forceinline__ void tr_pattern(int n0, int lane, uint32_t& a0, uint32_t& a1) {
+  const int G = lane >> 4, j = lane & 15;
+  const int r = 8 * (G >> 1) + (j >> 2);
+  const int col = n0 + 16 * (G & 1) + 4 * (j & 3);
+  a0 = swz_b(r, col);
+  a1 = swz_b(r + 4, col);
+}
+// Keeps a value in its register and opaque to the optimizer from here on, so
+// that addresses formed from it are not precomputed per stage.
+#define SA_OPAQUE(x) asm volatile("" : "+v"(x))
+
+__global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
+  __shared__ FLds lds;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const TileUnit unit = xcd_unit(a.num_kv_heads, a.num_seqs);
+  const int seq = unit.seq, g = unit.head, qt = unit.rank;
+  const int ntiles = (int)gridDim.x / (a.num_kv_heads * a.num_seqs);
+  const int T = a.total_tokens, window = a.window;
+  // dS partial of query head g*G + j for this tile: dsink_slots[j * slot_stride]
+  const long slot_stride = (long)a.num_seqs * ntiles;
+  float* __restrict__ dsink_slots = a.dsink_part + ((long)g * G * a.num_seqs + seq) * ntiles + qt;
+  const int bos = a.cu_seqlens[seq];
+  const int L = a.cu_seqlens[seq + 1] - bos;
+  const int q0 = qt * kFQ;
+  if (q0 >= L) {
+    for (int j = tid; j < G; j += 512) dsink_slots[j * slot_stride] = 0.0f;
+    return;
+  }
+  const int qs = a.num_q_heads * kD, ks = a.num_kv_heads * kD;  // row strides (< 2^31 elements)
+  const bf16* __restrict__ Qg = (const bf16*)a.q + (long)bos * qs + g * G * kD;  // head g*G + j at + j*kD
+  const bf16* __restrict__ dOg = (const bf16*)a.dout + (long)bos * qs + g * G * kD;
+  const bf16* __restrict__ Og = (const bf16*)a.o + (long)bos * qs + g * G * kD;
+  const float* __restrict__ lse_g = a.lse + (long)g * G * T + bos;  // head g*G + j at + j*T
+  const bf16* __restrict__ Kg = (const bf16*)a.k + (long)bos * ks + g * kD;
+  const bf16* __restrict__ Vg = (const bf16*)a.v + (long)bos * ks + g * kD;
+  const int kbase = q0 - kFQ;                     // first key of the span (< 0 for the first tile)
+  const int nrb = L - q0 > kBM ? 2 : 1;           // 64-row steps per head
+  const int nsteps = G * nrb;
+
+  // Prefetch cursor (head pj, row block prb of step pf); it stops at the last
+  // step, so the ring's look-ahead past the end re-loads that step.
+  int pf = 0, pj = 0, prb = 0;
+  // This lane stages 16 bytes of row r_own of each 64-row tile into its
+  // swizzled slot (wavefront w: rows 8w .. 8w + 7).
+  const int r_own = 8 * w + (lane >> 3);
+  const uint32_t voff = (uint32_t)(r_own * qs + 8 * ((lane & 7) ^ swz_f(r_own))) * (uint32_t)sizeof(bf16);
+  auto prefetch = [&](FStage& st) {
+    const int qb = q0 + kBM * prb;
+    const int rem = L - qb;  // >= 1: rows from the tile's first on (rows past the end repeat the last)
+    uint32_t off = voff, soff = (uint32_t)lane * (uint32_t)sizeof(float);
+    if (rem < kBM) {
+      off = voff - (uint32_t)(max(r_own - (rem - 1), 0) * qs) * (uint32_t)sizeof(bf16);
+      soff = (uint32_t)min(lane, rem - 1) * (uint32_t)sizeof(float);
+    }
+    const long ro = (long)qb * qs + pj * kD;
+    lds_dma16_s(off, Qg + ro, st.q + 512 * w);
+    lds_dma16_s(off, dOg + ro, st.dout + 512 * w);
+    lds_dma16_s(off, Og + ro, st.o + 512 * w);
+    lds_dma4_s(soff, lse_g + (long)pj * T + qb, w == 0 ? st.lse : st.spare);
+    if (pf + 1 < nsteps) {
+      ++pf;
+      if (++prb == nrb) {
+        prb = 0;
+        ++pj;
+      }
+    }
+  };
+  prefetch(lds.s0);
+  issue_fence();
+  prefetch(lds.s1);
+  issue_fence();
+  // K of the 256 keys into LDS (keys outside the sequence repeat its first or
+  // last key; they are masked), and this wavefront's K and V fragments: B
+  // operands of S = Q K^T and dP = dO V^T (lane = key column).
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int blk = 4 * w + i;
+    const int r = 8 * blk + (lane >> 3);
+    const int key = min(max(kbase + r, 0), L - 1);
+    lds_dma16(Kg + (long)key * ks + 8 * ((lane & 7) ^ swz_f(r)), lds.ks + 512 * blk);
+  }
+  const int wk_lo = kbase + 32 * w, wk_hi = wk_lo + 31;
+  const int key_n = wk_lo + l32;
+  bf16x8 kf[4], vf[4];
+  {
+    const int krow = min(max(key_n, 0), L - 1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int d0 = 16 * c + 8 * h2;
+      kf[c] = load8(Kg + (long)krow * ks + d0);
+      vf[c] = load8(Vg + (long)krow * ks + d0);
+    }
+  }
+
+  // Per-lane LDS address patterns (bytes).  Stage-relative ones get the
+  // stage's offset added as a constant.
+  const int qrow_base = row_perm(l32);
+  uint32_t p_seed = 32u * h2;  // statistics of rows 8*h2 .. (+ 128*mb, + 64 for the second 8)
+  uint32_t p_row[4];           // row fragment of operand row qrow_base (+ 4096*mb), chunk 2c + h2
+#pragma unroll
+  for (int c = 0; c < 4; ++c) p_row[c] = swz_b(qrow_base, 16 * c + 8 * h2);
+  uint32_t p_tr[2][2];  // transposing reads for d block db (+ 2048 per 16 query rows)
+#pragma unroll
+  for (int db = 0; db < 2; ++db) tr_pattern(32 * db, lane, p_tr[db][0], p_tr[db][1]);
+  const int kl = 32 * w + l32;  // this lane's key row in ks and ds
+  uint32_t p_dsw[2][2];         // dS^T chunk of rows 32*mb + 16*hb + 8*h2 of key kl
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) p_dsw[mb][hb] = lds_addr(lds.ds) + swz_b(kl, 32 * mb + 16 * hb + 8 * h2);
+  // dQ wavefronts (w < 4): d block db, row block nb of the step.
+  const int db_q = w & 1, nb_q = (w >> 1) & 1;
+  uint32_t p_ks[2], p_dsr[2];
+  tr_pattern(32 * db_q, lane, p_ks[0], p_ks[1]);
+  tr_pattern(32 * nb_q, lane, p_dsr[0], p_dsr[1]);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    p_ks[e] += lds_addr(lds.ks);
+    p_dsr[e] += lds_addr(lds.ds);
+  }
+  // dQ epilogue: 32 rows of 64 bytes per wavefront in the consumed stage's Q
+  // tile, 16-byte chunks XOR-swizzled by row.
+  uint32_t p_epw = (uint32_t)(w & 3) * 2048u + (uint32_t)l32 * 64u + 8u * h2;  // + ((gi ^ sw) << 4)
+  const uint32_t ep_sw = (uint32_t)((l32 >> 2) & 3);
+  uint32_t p_epr[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = lane + 64 * i, row = c >> 2, jc = c & 3;
+    p_epr[i] = (uint32_t)(w & 3) * 2048u + (uint32_t)row * 64u + ((uint32_t)(jc ^ ((row >> 2) & 3)) << 4);
+  }
+  // Statistics threads (w >= 4): a quarter of row srow.
+  const int st_t = tid & 255, srow = st_t >> 2, sqd = st_t & 3;
+  uint32_t p_st[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) p_st[c] = swz_b(srow, 16 * sqd + 8 * c);
+  uint32_t p_srow = (uint32_t)srow * 4u;
+
+  wait_vmem_all();
+  issue_fence();
+  lds_barrier();
+
+  // Row statistics of step sidx from its stage (wavefronts 4..7), and the
+  // scaled queries in place.
+  float sterm = 0.0f;  // sink terms -p_sink D of this thread's rows, current head
+  auto stats = [&](FStage& st, int sidx) {
+    const uint32_t S = lds_addr(&st);
+    const int j = nrb == 2 ? sidx >> 1 : sidx, rb = sidx - j * nrb;
+    float dpart = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const f32x8 x = __builtin_convertvector(lds_ld<bf16x8>(S + kOffDout + p_st[c]), f32x8);
+      const f32x8 y = __builtin_convertvector(lds_ld<bf16x8>(S + kOffO + p_st[c]), f32x8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dpart += x[i] * y[i];
+      const f32x8 qv = __builtin_convertvector(lds_ld<bf16x8>(S + p_st[c]), f32x8);
+      lds_st<bf16x8>(S + p_st[c], __builtin_convertvector(qv * a.scale_log2, bf16x8));
+    }
+    dpart += __shfl_xor(dpart, 1);
+    dpart += __shfl_xor(dpart, 2);
+    if (sqd == 0) {
+      const float lse = lds_ld<float>(S + kOffLse + p_srow);
+      lds_st<float>(S + kOffNlse + p_srow, -lse * kLog2e);
+      lds_st<float>(S + kOffNdelta + p_srow, -dpart);
+      if (q0 + kBM * rb + srow < L) sterm += -__expf(a.sinks[g * G + j] - lse) * dpart;
+    }
+    if (rb == nrb - 1) {  // the head's last step: this wavefront's share of dS_h
+      const float sw = wave_sum(sterm);
+      if (lane == 0) lds.wsum[j][w - 4] = sw;
+      sterm = 0.0f;
+    }
+  };
+  if (w >= 4) stats(lds.s0, 0);
+
+  f32x16 dk[2], dv[2];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { dk[0][i] = dk[1][i] = dv[0][i] = dv[1][i] = 0.0f; }
+
+  // One step: consume `st` (step cs), compute the statistics of step cs + 1 in
+  // `nx`, prefetch step cs + 2 into `nn` (the stage of step cs - 1).
+  int cs = 0;
+  auto step = [&](FStage& st, FStage& nx, FStage& nn) {
+    SA_OPAQUE(p_seed);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) SA_OPAQUE(p_row[c]);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      SA_OPAQUE(p_tr[db][0]);
+      SA_OPAQUE(p_tr[db][1]);
+    }
+    const uint32_t S = lds_addr(&st);
+    lds_barrier();  // statistics and scaled queries of `st` ready; ds and `nn` free
+    prefetch(nn);
+    issue_fence();
+    const int j = nrb == 2 ? cs >> 1 : cs, rb = cs - j * nrb;
+    const int qb = q0 + kBM * rb;
+    const bool active = wk_lo >= 0 && wk_lo < L && wk_lo <= qb + kBM - 1 && qb - wk_hi < window;
+    if (active) {
+      const bool mask_lo = wk_hi > qb;
+      const bool mask_hi = (qb + kBM > L) || (qb + kBM - 1 - wk_lo >= window);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        // S and dP for rows 32*mb .. 32*mb+31 of the step, seeded with the row
+        // statistics (register r: row 32*mb + 16*(r/8) + 8*h2 + r%8).
+        f32x16 s, dp;
+        {
+          const uint32_t sa = S + kOffNlse + 128u * mb + p_seed, da = S + kOffNdelta + 128u * mb + p_seed;
+          const f32x8 s0 = lds_ld<f32x8>(sa), s1 = lds_ld<f32x8>(sa + 64);
+          const f32x8 d0 = lds_ld<f32x8>(da), d1 = lds_ld<f32x8>(da + 64);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            s[i] = s0[i];
+            s[8 + i] = s1[i];
+            dp[i] = d0[i];
+            dp[8 + i] = d1[i];
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          s = mfma32(lds_ld<bf16x8>(S + 4096u * mb + p_row[c]), kf[c], s);
+          dp = mfma32(lds_ld<bf16x8>(S + kOffDout + 4096u * mb + p_row[c]), vf[c], dp);
+        }
+        bf16x8 pf8[2], df[2];
+        const int rbase = qb + 32 * mb + 8 * h2;
+        const int lo = key_n - rbase;
+        const int hi = min(L - rbase, lo + window);
+        auto softmax_grad = [&](auto test_lo, auto test_hi) {
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            f32x8 pv, dv8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int r = 8 * hb + i;
+              float p = fast_exp2(s[r]);
+              const int idx = 16 * hb + i;
+              bool vis = true;
+              if constexpr (decltype(test_lo)::value) vis = vis && idx >= lo;
+              if constexpr (decltype(test_hi)::value) vis = vis && idx < hi;
+              p = vis ? p : 0.0f;
+              pv[i] = p;
+              dv8[i] = p * dp[r];
+            }
+            pf8[hb] = __builtin_convertvector(pv, bf16x8);
+            df[hb] = __builtin_convertvector(dv8, bf16x8);
+          }
+        };
+        if (mask_lo && mask_hi)
+          softmax_grad(std::true_type{}, std::true_type{});
+        else if (mask_lo)
+          softmax_grad(std::true_type{}, std::false_type{});
+        else if (mask_hi)
+          softmax_grad(std::false_type{}, std::true_type{});
+        else
+          softmax_grad(std::false_type{}, std::false_type{});
+        // dS^T row of this lane's key: 8 consecutive query rows per register half.
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) lds_st<bf16x8>(p_dsw[mb][hb], df[hb]);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const uint32_t o = 2048u * (2 * mb + cc);
+            dv[db] = mfma32(pf8[cc], lds_tr8(S + kOffDout + o + p_tr[db][0], S + kOffDout + o + p_tr[db][1]), dv[db]);
+            dk[db] = mfma32(df[cc], lds_tr8(S + o + p_tr[db][0], S + o + p_tr[db][1]), dk[db]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) lds_st<bf16x8>(p_dsw[mb][hb], zero8());
+    }
+    // This wavefront's share of step cs + 1 has landed once at most the
+    // prefetch just issued is in flight (the older dQ stores are covered too).
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    static_assert(kFPrefetchOps == 4, "wait count");
+    lds_barrier();  // ds complete; step cs + 1 visible
+    if (w < 4) {
+      // dQ^T block (d 32*db_q .. +31, rows 32*nb_q .. +31 of the step) = K^T dS^T
+      // over the 256 keys; register r: d = 32*db_q + 8*(r/4) + 4*h2 + r%4.
+      SA_OPAQUE(p_ks[0]);
+      SA_OPAQUE(p_ks[1]);
+      SA_OPAQUE(p_dsr[0]);
+      SA_OPAQUE(p_dsr[1]);
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < kFK / 16; ++c)
+        acc = mfma32(lds_tr8(p_ks[0] + 2048u * c, p_ks[1] + 2048u * c),
+                     lds_tr8(p_dsr[0] + 2048u * c, p_dsr[1] + 2048u * c), acc);
+      // Out through the consumed stage's Q tile (idle until the next step's
+      // prefetch, which follows that step's barrier).
+      SA_OPAQUE(p_epw);
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const f32x4 v = {acc[4 * gi] * a.scale, acc[4 * gi + 1] * a.scale, acc[4 * gi + 2] * a.scale,
+                         acc[4 * gi + 3] * a.scale};
+        lds_st<bf16x4>(S + p_epw + (((uint32_t)gi ^ ep_sw) << 4), __builtin_convertvector(v, bf16x4));
+      }
+      issue_fence();  // the reads below take other lanes' writes (LDS keeps a wavefront's order)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = lane + 64 * i, row = c >> 2, jc = c & 3;
+        const bf16x8 x = lds_ld<bf16x8>(S + p_epr[i]);
+        const int qrow = qb + 32 * nb_q + row;
+        if (qrow < L)
+          *(bf16x8*)((bf16*)a.dq + (long)(bos + qrow) * qs + (g * G + j) * kD + 32 * db_q + 8 * jc) = x;
+      }
+    } else if (cs + 1 < nsteps) {
+      SA_OPAQUE(p_st[0]);
+      SA_OPAQUE(p_st[1]);
+      stats(nx, cs + 1);
+    }
+    ++cs;
+  };
+  for (int f = 0; f < nsteps; f += kStages) {
+    step(lds.s0, lds.s1, lds.s2);
+    if (f + 1 < nsteps) step(lds.s1, lds.s2, lds.s0);
+    if (f + 2 < nsteps) step(lds.s2, lds.s0, lds.s1);
+  }
+
+  // The ring's last, redundant loads land before the end; wsum is complete
+  // after the barrier.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int j = tid; j < G; j += 512)
+    dsink_slots[j * slot_stride] = (lds.wsum[j][0] + lds.wsum[j][1]) + (lds.wsum[j][2] + lds.wsum[j][3]);
+  // dK, dV of this wavefront's keys (register r: key wk_lo + 8*(r/4) + 4*h2 + r%4)
+  // into plane 0 (keys of this tile) or 1 (keys of the tile before).
+  if (wk_lo < 0) return;
+  const long plane = (long)T * ks;
+  const bool own = w >= 4, last = q0 + kFQ >= L;
+  float* dk_g = a.dk_part + (own ? 0 : plane) + (long)bos * ks + g * kD;
+  float* dv_g = a.dv_part + (own ? 0 : plane) + (long)bos * ks + g * kD;
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    const int d = 32 * db + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = wk_lo + 8 * (r >> 2) + 4 * h2 + (r & 3);
+      if (key < L) {
+        dk_g[(long)key * ks + d] = dk[db][r] * kLn2;
+        dv_g[(long)key * ks + d] = dv[db][r];
+        if (own && last) {
+          dk_g[plane + (long)key * ks + d] = 0.0f;
+          dv_g[plane + (long)key * ks + d] = 0.0f;
+        }
+      }
+    }
+  }
+}
+#undef SA_OPAQUE
+
 int flat_blocks(long work_items) {
   const long b = (work_items + kFlatThreads - 1) / kFlatThreads;
   return (int)(b < 1 ? 1 : (b > 1024 ? 1024 : b));
@@ -720,18 +1145,32 @@ int bwd_dsink_parts(int max_seqlen, int num_seqs, int heads_per_tile) {
 }
 
 BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d, int max_seqlen, int num_seqs,
-                                  int dkdv_heads, int heads_per_tile) {
+                                  int dkdv_heads, int heads_per_tile, bool fused) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const int P = hq / hkv / dkdv_heads;  // head groups per KV head
   BwdWorkspace w;
-  w.ndelta = up((size_t)hq * total_tokens * sizeof(float));
-  w.nlse = w.ndelta;
-  w.qscaled = up((size_t)total_tokens * hq * d * sizeof(bf16));
-  w.dk_part = P > 1 ? up((size_t)P * total_tokens * hkv * d * sizeof(float)) : 0;
-  w.dv_part = w.dk_part;
-  w.dsink_part = up((size_t)bwd_dsink_parts(max_seqlen, num_seqs, heads_per_tile) * hq * sizeof(float));
+  if (fused) {
+    // Two dK/dV planes and a dS partial per (head, 128-row tile); the row
+    // statistics and scaled queries stay inside the workgroup.
+    w.ndelta = w.nlse = w.qscaled = 0;
+    w.dk_part = up((size_t)2 * total_tokens * hkv * d * sizeof(float));
+    w.dv_part = w.dk_part;
+    w.dsink_part = up((size_t)bwd_dsink_parts(max_seqlen, num_seqs, 1) * hq * sizeof(float));
+  } else {
+    const int P = hq / hkv / dkdv_heads;  // head groups per KV head
+    w.ndelta = up((size_t)hq * total_tokens * sizeof(float));
+    w.nlse = w.ndelta;
+    w.qscaled = up((size_t)total_tokens * hq * d * sizeof(bf16));
+    w.dk_part = P > 1 ? up((size_t)P * total_tokens * hkv * d * sizeof(float)) : 0;
+    w.dv_part = w.dk_part;
+    w.dsink_part = up((size_t)bwd_dsink_parts(max_seqlen, num_seqs, heads_per_tile) * hq * sizeof(float));
+  }
   w.total = w.ndelta + w.nlse + w.qscaled + w.dk_part + w.dv_part + w.dsink_part;
   return w;
+}
+
+bool bwd_window_fusable(int dtype, int head_dim, int window, int max_seqlen, int hq, int hkv) {
+  return dtype == 0 && head_dim == kD && window >= 1 && window <= kFQ && window < max_seqlen &&
+         hq / hkv <= kFMaxGroup;
 }
 
 int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, int window) {
@@ -759,42 +1198,51 @@ int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, 
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t stream,
                       const hipEvent_t* events) {
   const int T = a.total_tokens, Hq = a.num_q_heads;
-  const int parts = T > 0 ? bwd_dsink_parts(max_seqlen, num_seqs, a.heads_per_tile) : 0;
+  const int parts = T > 0 ? bwd_dsink_parts(max_seqlen, num_seqs, a.fused ? 1 : a.heads_per_tile) : 0;
   const long chunks = (long)T * 2 * a.num_kv_heads * a.head_dim / 8;
-  const bool dkdv_partials = a.dkdv_heads * a.num_kv_heads != Hq;
-  const int conv_blocks = (T > 0 && dkdv_partials) ? flat_blocks(chunks) : 0;
+  const int conv_blocks = (T > 0 && a.dkdv_planes > 1) ? flat_blocks(chunks) : 0;
   const int post_blocks = conv_blocks + Hq;
-  const dim3 grid_kv((max_seqlen + kBN - 1) / kBN * (Hq / a.dkdv_heads) * num_seqs);
-  const int qrows = kQT / a.heads_per_tile;
-  const dim3 grid_q((max_seqlen + qrows - 1) / qrows * (Hq / a.heads_per_tile) * num_seqs);
-  const bool direct = dtype == 0 && a.head_dim == kD;
-  // The window-free instances when no sequence is cut by the window.
-  const bool windowed = a.window > 0 && a.window < max_seqlen;
   auto mark = [&](int i) { return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess; };
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return e;
-  if (T > 0) {
-    if (direct && windowed)
-      hipLaunchKernelGGL((bwd_dq_kernel<bf16, true, true>), grid_q, dim3(256), 0, stream, a);
-    else if (direct)
-      hipLaunchKernelGGL((bwd_dq_kernel<bf16, true, false>), grid_q, dim3(256), 0, stream, a);
-    else if (dtype == 0)
-      hipLaunchKernelGGL((bwd_dq_kernel<bf16, false, true>), grid_q, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((bwd_dq_kernel<float, false, true>), grid_q, dim3(256), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if ((e = mark(1)) != hipSuccess) return e;
-  if (T > 0) {
-    if (direct && windowed)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, true, true>), grid_kv, dim3(256), 0, stream, a);
-    else if (direct)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, true, false>), grid_kv, dim3(256), 0, stream, a);
-    else if (dtype == 0)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, false, true>), grid_kv, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<float, false, true>), grid_kv, dim3(256), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.fused) {
+    // One kernel in place of the dQ and dK/dV kernels (both event slots mark its end).
+    if (T > 0) {
+      const dim3 grid((max_seqlen + kFQ - 1) / kFQ * a.num_kv_heads * num_seqs);
+      hipLaunchKernelGGL(bwd_window_kernel, grid, dim3(512), 0, stream, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if ((e = mark(1)) != hipSuccess) return e;
+  } else {
+    const dim3 grid_kv((max_seqlen + kBN - 1) / kBN * (Hq / a.dkdv_heads) * num_seqs);
+    const int qrows = kQT / a.heads_per_tile;
+    const dim3 grid_q((max_seqlen + qrows - 1) / qrows * (Hq / a.heads_per_tile) * num_seqs);
+    const bool direct = dtype == 0 && a.head_dim == kD;
+    // The window-free instances when no sequence is cut by the window.
+    const bool windowed = a.window > 0 && a.window < max_seqlen;
+    if (T > 0) {
+      if (direct && windowed)
+        hipLaunchKernelGGL((bwd_dq_kernel<bf16, true, true>), grid_q, dim3(256), 0, stream, a);
+      else if (direct)
+        hipLaunchKernelGGL((bwd_dq_kernel<bf16, true, false>), grid_q, dim3(256), 0, stream, a);
+      else if (dtype == 0)
+        hipLaunchKernelGGL((bwd_dq_kernel<bf16, false, true>), grid_q, dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL((bwd_dq_kernel<float, false, true>), grid_q, dim3(256), 0, stream, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if ((e = mark(1)) != hipSuccess) return e;
+    if (T > 0) {
+      if (direct && windowed)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, true, true>), grid_kv, dim3(256), 0, stream, a);
+      else if (direct)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, true, false>), grid_kv, dim3(256), 0, stream, a);
+      else if (dtype == 0)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, false, true>), grid_kv, dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<float, false, true>), grid_kv, dim3(256), 0, stream, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   if ((e = mark(2)) != hipSuccess) return e;
   if (dtype == 0)

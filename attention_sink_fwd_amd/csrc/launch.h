@@ -42,11 +42,13 @@ struct BwdArgs {
   float* ndelta;  // workspace: -D_i = -(dO_i . O_i), [Hq, T]
   bf16_raw* qscaled;  // workspace: bf16(q * scale * log2 e), [T, Hq, d] (the score operand of every kernel)
   float* nlse;    // workspace: -LSE_i log2(e), [Hq, T]
-  float* dk_part;  // workspace: float dK partial sums, [P, T, Hkv, d], P = (Hq/Hkv) / dkdv_heads
+  float* dk_part;  // workspace: float dK partial sums, [P, T, Hkv, d], P = dkdv_planes
   float* dv_part;  // workspace: float dV partial sums, same shape (both unused when P == 1)
   float* dsink_part;  // workspace: per-query-tile dS partials, [Hq, num_seqs, query tiles]
   int num_q_heads, num_kv_heads, head_dim, total_tokens, window, num_seqs;
   int dkdv_heads;      // query heads per dK/dV workgroup (divides Hq / Hkv)
+  int dkdv_planes;     // float dK/dV partial-sum planes the post kernel adds (1: dK, dV written directly)
+  int fused;           // 1: the fused short-window kernel replaces the dQ and dK/dV kernels
   int heads_per_tile;  // query heads of one KV head packed in a dQ workgroup (divides Hq/Hkv and 32)
   float scale;
   float scale_log2;
@@ -57,7 +59,11 @@ struct BwdWorkspace {
   size_t ndelta, nlse, qscaled, dk_part, dv_part, dsink_part, total;
 };
 BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d, int max_seqlen, int num_seqs,
-                                  int dkdv_heads, int heads_per_tile);
+                                  int dkdv_heads, int heads_per_tile, bool fused);
+// Whether the fused short-window backward kernel covers a shape: bf16,
+// head_dim 64, a window of 1..128 keys that cuts some sequence, and at most
+// 64 query heads per KV head.
+bool bwd_window_fusable(int dtype, int head_dim, int window, int max_seqlen, int hq, int hkv);
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s);
 // Query heads per dK/dV workgroup for a problem shape (a divisor of Hq/Hkv),

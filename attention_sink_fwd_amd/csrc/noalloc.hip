@@ -62,19 +62,23 @@ int sink_attn_bwd_noalloc(const sink_attn_params* p, const void* q, const void* 
   const sinkattn::BwdTensors t{q, k, v, sinks, o, lse, dout, dq, dk, dv, dsinks};
   int st = sinkattn::bwd_check(p, t);
   if (st != SINK_ATTN_OK) return st;
-  int dkdv_heads = 0, pack_heads = 0;
-  bool overridden = false;
-  st = sinkattn::bwd_split(p, &dkdv_heads, &pack_heads, &overridden);
+  sinkattn::BwdSplit split;
+  st = sinkattn::bwd_split(p, &split);
   if (st != SINK_ATTN_OK) return st;
-  // The split sink_attn_bwd would use, else (unless SINK_ATTN_DKDV_HEADS fixes
-  // it) the first one with more query heads per dK/dV workgroup -- fewer
-  // float partial-sum planes -- whose workspace fits the buffer.
+  // The split sink_attn_bwd would use; if its workspace does not fit the
+  // buffer, the dQ and dK/dV kernels instead of the fused short-window one,
+  // and (unless SINK_ATTN_DKDV_HEADS fixes it) the first split with more query
+  // heads per dK/dV workgroup -- fewer float partial-sum planes -- that fits.
   const int grp = p->num_q_heads / p->num_kv_heads;
-  size_t need = sinkattn::bwd_layout(p, dkdv_heads, pack_heads).total;
-  for (int hg = dkdv_heads + 1; need > kScratchBytes && !overridden && hg <= grp; ++hg) {
+  size_t need = sinkattn::bwd_layout(p, split).total;
+  if (need > kScratchBytes && split.fused) {
+    split.fused = false;
+    need = sinkattn::bwd_layout(p, split).total;
+  }
+  for (int hg = split.dkdv_heads + 1; need > kScratchBytes && !split.dkdv_overridden && hg <= grp; ++hg) {
     if (grp % hg != 0) continue;
-    dkdv_heads = hg;
-    need = sinkattn::bwd_layout(p, dkdv_heads, pack_heads).total;
+    split.dkdv_heads = hg;
+    need = sinkattn::bwd_layout(p, split).total;
   }
   if (need > kScratchBytes)
     return fail(SINK_ATTN_ERR_UNSUPPORTED,
@@ -92,7 +96,7 @@ int sink_attn_bwd_noalloc(const sink_attn_params* p, const void* q, const void* 
   void* ws = nullptr;
   st = scratch_on_current_device(&ws);
   if (st != SINK_ATTN_OK) return st;
-  return sinkattn::bwd_enqueue(p, t, ws, dkdv_heads, pack_heads, stream);
+  return sinkattn::bwd_enqueue(p, t, ws, split, stream);
 }
 
 }  // extern "C"

@@ -78,15 +78,18 @@ def sources_sha256(paths):
     return h.hexdigest()
 
 
-def traffic_for_current_kernel(kernel):
+def traffic_for_current_kernel(kernel, workload):
     """HBM bytes per launch of `kernel` from rocprofv3 FETCH_SIZE + WRITE_SIZE.
 
-    Taken from profiles/traffic.json, and only while the kernel's sources are
-    byte-identical to the ones the counters were measured on; else None.
+    Taken from profiles/traffic.json, and only for the workload the counters
+    were measured on, while the kernel's sources are byte-identical to the
+    ones they were measured on; else None.
     """
     try:
         with open(TRAFFIC_FILE) as f:
             entry = json.load(f)[kernel]
+        if entry.get("workload") != workload:
+            return None
         if entry.get("sources_sha256") != sources_sha256(entry["sources"]):
             return None
         return float(entry["bytes_per_launch"])
@@ -205,7 +208,8 @@ def paged_decode(args):
         "roofline": {"kernel": "fwd_paged", "kernel_ms": round(kern_ms, 5), "bound": "hbm",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": io_bytes,
-                     "traffic": traffic_for_current_kernel("fwd_paged")},
+                     "traffic": traffic_for_current_kernel(
+                         "fwd_paged", "paged_decode_b64_ctx4096_hq64_hkv8_d64_page64")},
     }), flush=True)
 
 
@@ -277,7 +281,7 @@ def token_logps(args):
         "roofline": {"kernel": dom, "kernel_ms": round(dom_ms, 5), "bound": "hbm",
                      "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(ach / PEAK_HBM_GBS, 4), "algorithmic_bytes": dom_bytes,
-                     "traffic": traffic_for_current_kernel(dom)},
+                     "traffic": traffic_for_current_kernel(dom, "token_logps_rows8192_vocab201088")},
     }), flush=True)
 
 
@@ -372,13 +376,18 @@ def main():
     def avg(evs, a, b):
         return sum(hip.ms(e[a], e[b]) for e in evs) / len(evs)
 
+    # Short windows run one fused backward kernel in place of the dQ and dK/dV
+    # kernels (its launch fills the first event slot pair).
+    fused = sa.sink_attn_bwd_fused(q, k, cu, w.max_seqlen, w.softmax_scale, w.window)
+    bwd_kernels = ("bwd_fused",) if fused else ("bwd_dq", "bwd_dkdv")
+    slot = {"bwd_dq": 0, "bwd_fused": 0, "bwd_dkdv": 1, "bwd_post": 2}
     kernel_ms = {}
-    for kname in ("fwd", "bwd_dq", "bwd_dkdv", "bwd_post"):
+    for kname in ("fwd", *bwd_kernels, "bwd_post"):
         evb = [[hip.event() for _ in range(2)] for _ in range(nb)]
         if kname == "fwd":
             fe, be = (lambda i: (evb[i][0], evb[i][1])), (lambda i: (None, None, None, None))
         else:
-            j = {"bwd_dq": 0, "bwd_dkdv": 1, "bwd_post": 2}[kname]
+            j = slot[kname]
 
             def be(i, j=j):
                 h = [None, None, None, None]
@@ -391,7 +400,7 @@ def main():
         for row in evb:
             for e in row:
                 hip.destroy(e)
-    kms = {kname: kernel_ms[kname] for kname in ("fwd", "bwd_dkdv", "bwd_dq")}
+    kms = {kname: kernel_ms[kname] for kname in ("fwd", *bwd_kernels)}
     dom = max(kms, key=kms.get)
 
     # Timed region: K steps; only the dominant kernel is bracketed (two
@@ -401,7 +410,7 @@ def main():
     none = None
     if dom == "fwd":
         fwd_ev, bwd_ev = (lambda i: (evt[i][0], evt[i][1])), (lambda i: (none, none, none, none))
-    elif dom == "bwd_dq":
+    elif slot[dom] == 0:
         fwd_ev, bwd_ev = (lambda i: None), (lambda i: (evt[i][0].value, evt[i][1].value, none, none))
     else:
         fwd_ev, bwd_ev = (lambda i: None), (lambda i: (none, evt[i][0].value, evt[i][1].value, none))
@@ -421,15 +430,26 @@ def main():
     # Algorithmic flops per launch of each matrix-core kernel (FA convention,
     # 2*d flops per visible pair per product): forward 2 products (S, PV);
     # dK/dV kernel 4 of the 5 backward products (S, dP, dV, dK); dQ kernel the
-    # remaining one (dQ) -- its recomputed S and dP are not counted.
+    # remaining one (dQ) -- its recomputed S and dP are not counted; the fused
+    # short-window kernel all 5.
     pairs = w.visible_pairs()
     algo = {"fwd": 4.0 * w.head_dim * pairs, "bwd_dkdv": 8.0 * w.head_dim * pairs,
-            "bwd_dq": 2.0 * w.head_dim * pairs}
-    # Matrix work each kernel executes: the dQ kernel recomputes S and dP
-    # (2 more products per pair than it is credited with).
-    executed = {"fwd": algo["fwd"], "bwd_dkdv": algo["bwd_dkdv"], "bwd_dq": 6.0 * w.head_dim * pairs}
+            "bwd_dq": 2.0 * w.head_dim * pairs, "bwd_fused": 10.0 * w.head_dim * pairs}
+    # Matrix work each kernel executes on visible pairs: the dQ kernel
+    # recomputes S and dP (2 more products per pair than it is credited with).
+    executed = dict(algo, bwd_dq=6.0 * w.head_dim * pairs)
+
+    def frac(kname, flops):
+        return round(flops / (kms[kname] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    kernel_frac = {"fwd": frac("fwd", algo["fwd"])}
+    if fused:
+        kernel_frac["bwd_fused"] = frac("bwd_fused", algo["bwd_fused"])
+    else:
+        kernel_frac["bwd_dq"] = {"credited": frac("bwd_dq", algo["bwd_dq"]),
+                                 "executed": frac("bwd_dq", executed["bwd_dq"])}
+        kernel_frac["bwd_dkdv"] = frac("bwd_dkdv", algo["bwd_dkdv"])
     dom_tflops = algo[dom] / (dom_ms * 1e-3) / 1e12
-    traffic = traffic_for_current_kernel(dom)
+    traffic = traffic_for_current_kernel(dom, w.name)
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -461,14 +481,7 @@ def main():
                            "step; sum minus ms_per_step: event overhead and launch gaps"),
         "kernel_sum_minus_step_ms": round(sum(kernel_ms.values()) - ms, 4),
         "kernel_tflops": {kname: round(algo[kname] / (kms[kname] * 1e-3) / 1e12, 1) for kname in kms},
-        "kernel_frac": {
-            "fwd": round(algo["fwd"] / (kms["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "bwd_dq": {
-                "credited": round(algo["bwd_dq"] / (kms["bwd_dq"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "executed": round(executed["bwd_dq"] / (kms["bwd_dq"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            },
-            "bwd_dkdv": round(algo["bwd_dkdv"] / (kms["bwd_dkdv"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        },
+        "kernel_frac": kernel_frac,
         "roofline": {
             "kernel": dom,
             "kernel_ms": round(dom_ms, 4),

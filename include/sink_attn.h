@@ -174,6 +174,24 @@ int sink_attn_fwd_paged(const sink_attn_params *p, const sink_attn_paged_kv *kv,
 size_t sink_attn_bwd_workspace_size(const sink_attn_params *p);
 
 /*
+ * Which backward kernels sink_attn_bwd runs for these parameters: 1 when one
+ * fused kernel computes dQ, dK, dV and the sink gradient (bf16, head_dim 64
+ * and a window of 1..128 keys shorter than max_seqlen, with at most 64 query
+ * heads per KV head: every key a query row sees then lies in its own
+ * 128-row tile or the one before), 0 for the separate dQ and dK/dV kernels,
+ * or minus the sink_attn_status of the error for invalid parameters (the
+ * text is in sink_attn_last_error()).
+ * SINK_ATTN_BWD_FUSED=0 selects the separate kernels for every shape (the
+ * workspace size follows the choice).  Both give dS, dQ, dK and dV to within
+ * float summation order; each is bitwise reproducible.  Nothing is enqueued.
+ * Reference: "GPT-OSS Agentic RL Training: A Practical Retrospective",
+ * section "Implementation in FlashAttention v3" (the backward pass with the
+ * sink gradient; GPT-OSS alternates full attention with a 128-token sliding
+ * window).
+ */
+int sink_attn_bwd_fused(const sink_attn_params *p);
+
+/*
  * Backward pass: dQ, dK, dV and dS.
  *   q, k, v, sinks            the forward inputs
  *   o, lse                    the forward outputs for exactly these inputs

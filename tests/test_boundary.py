@@ -175,6 +175,42 @@ def test_workspace_follows_dkdv_heads(monkeypatch, heads, planes):
     assert lib.sink_attn_bwd_workspace_size(ctypes.byref(p)) == want
 
 
+@pytest.mark.parametrize("window,dtype,fused_env,fused", [
+    (128, 0, None, True), (1, 0, None, True), (129, 0, None, False), (128, 1, None, False),
+    (128, 0, "0", False), (0, 0, None, False)])
+def test_workspace_of_the_fused_short_window_path(monkeypatch, window, dtype, fused_env, fused):
+    """bf16, head_dim 64 and a window of 1..128 keys take the fused kernel:
+    two float dK/dV planes and one dS partial per (query head, 128-row tile);
+    otherwise (or with SINK_ATTN_BWD_FUSED=0) the dQ and dK/dV kernels'
+    workspace."""
+    monkeypatch.delenv("SINK_ATTN_DKDV_HEADS", raising=False)
+    monkeypatch.delenv("SINK_ATTN_PACK_HEADS", raising=False)
+    if fused_env is None:
+        monkeypatch.delenv("SINK_ATTN_BWD_FUSED", raising=False)
+    else:
+        monkeypatch.setenv("SINK_ATTN_BWD_FUSED", fused_env)
+    lib = _lib.load()
+    T, hq, hkv, d = 1000, 8, 2, 64
+    p = _good_params(T, hq, hkv, d, window=window, dtype=dtype)
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    got = lib.sink_attn_bwd_workspace_size(ctypes.byref(p))
+    fused_size = 2 * up(4 * 2 * T * hkv * d) + up(4 * ((T + 127) // 128) * hq)
+    assert (got == fused_size) == fused, (got, fused_size)
+    if not fused:
+        assert got >= 2 * up(4 * hq * T) + up(2 * T * hq * d)
+
+
+def test_fused_path_needs_at_most_64_heads_per_kv_head(monkeypatch):
+    monkeypatch.delenv("SINK_ATTN_BWD_FUSED", raising=False)
+    lib = _lib.load()
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    T, d = 300, 64
+    for hq, fused in ((64, True), (128, False)):
+        p = _good_params(T, hq, 1, d, window=100)
+        got = lib.sink_attn_bwd_workspace_size(ctypes.byref(p))
+        assert (got == 2 * up(4 * 2 * T * d) + up(4 * ((T + 127) // 128) * hq)) == fused
+
+
 @pytest.mark.parametrize("pack,rows", [(1, 128), (2, 64), (4, 32)])
 def test_workspace_follows_pack_heads(monkeypatch, pack, rows):
     monkeypatch.setenv("SINK_ATTN_PACK_HEADS", str(pack))
