@@ -109,6 +109,8 @@ struct __attribute__((aligned(16))) QStage {
   float spare[kBM];     // landing area that keeps every wavefront's load count equal
 };
 constexpr int kStages = 3;
+constexpr uint32_t kQOffDout = offsetof(QStage, dout), kQOffNlse = offsetof(QStage, nlse);
+constexpr uint32_t kQOffNdelta = offsetof(QStage, ndelta);
 
 // dK and dV for one 128-key tile and `dkdv_heads` query heads of one KV
 // group.  The workgroup walks (head, query tile) steps through one LDS ring,
@@ -245,12 +247,32 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) { dk[0][i] = dk[1][i] = dv[0][i] = dv[1][i] = 0.0f; }
 
+  // Per-lane LDS address patterns (bytes; the stage's offset is added as a
+  // constant): statistics of rows 8*h2 (+ 128*mb, + 64 for rows 16..), row
+  // fragments of operand row row_perm(l32) (+ 4096*mb), chunk 2c + h2, and the
+  // transposing reads of d block db (+ 2048 per 16 query rows).
   const int qrow_base = row_perm(l32);
+  uint32_t p_seed = 32u * h2;
+  uint32_t p_row[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) p_row[c] = swz_b(qrow_base, 16 * c + 8 * h2);
+  uint32_t p_tr[2][2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db) tr_pattern(32 * db, lane, p_tr[db][0], p_tr[db][1]);
 
   // One step: consume query tile ct (of some head) from `st`, prefetch two
   // steps ahead into `nx` (the stage consumed in the previous step).
   int ct = qt0;
   auto step = [&](const QStage& st, QStage& nx) {
+    lds_opaque(p_seed);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) lds_opaque(p_row[c]);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      lds_opaque(p_tr[db][0]);
+      lds_opaque(p_tr[db][1]);
+    }
+    const uint32_t S = lds_addr(&st);
     // Wait for this wavefront's part of the tile (only the next prefetch may
     // still be in flight), then make all parts visible.
     if constexpr (kDirect) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
@@ -275,12 +297,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         // half of the registers covers 8 consecutive rows.  The accumulators
         // start from the row statistics -LSE log2(e) and -D, and K is
         // pre-scaled by scale * log2(e), so P = exp2(s) and dS = P * dP.
-        const int qr = qrow_base + 32 * mb;
-        const int ql0 = 32 * mb + 8 * h2;
         f32x16 s, dp;
         {
-          const f32x8 s0 = *(const f32x8*)(st.nlse + ql0), s1 = *(const f32x8*)(st.nlse + ql0 + 16);
-          const f32x8 d0 = *(const f32x8*)(st.ndelta + ql0), d1 = *(const f32x8*)(st.ndelta + ql0 + 16);
+          const uint32_t sa = S + kQOffNlse + 128u * mb + p_seed, da = S + kQOffNdelta + 128u * mb + p_seed;
+          const f32x8 s0 = lds_ld<f32x8>(sa), s1 = lds_ld<f32x8>(sa + 64);
+          const f32x8 d0 = lds_ld<f32x8>(da), d1 = lds_ld<f32x8>(da + 64);
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             s[i] = s0[i];
@@ -291,8 +312,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          s = mfma32(frag_row(st.q, qr, 16 * c + 8 * h2), kf[c], s);
-          dp = mfma32(frag_row(st.dout, qr, 16 * c + 8 * h2), vf[c], dp);
+          s = mfma32(lds_ld<bf16x8>(S + 4096u * mb + p_row[c]), kf[c], s);
+          dp = mfma32(lds_ld<bf16x8>(S + kQOffDout + 4096u * mb + p_row[c]), vf[c], dp);
         }
         bf16x8 pf[2], df[2];
         // Element (hb, i) of this lane is query row rbase + 16*hb + i against
@@ -344,9 +365,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
         for (int db = 0; db < 2; ++db) {
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc) {
-            const int c = 2 * mb + cc;
-            dv[db] = mfma32(pf[cc], frag_tr_swz(st.dout, 16 * c, 32 * db, lane), dv[db]);
-            dk[db] = mfma32(df[cc], frag_tr_swz(st.q, 16 * c, 32 * db, lane), dk[db]);
+            const uint32_t o = 2048u * (2 * mb + cc);
+            dv[db] = mfma32(pf[cc], lds_tr8(S + kQOffDout + o + p_tr[db][0], S + kQOffDout + o + p_tr[db][1]), dv[db]);
+            dk[db] = mfma32(df[cc], lds_tr8(S + o + p_tr[db][0], S + o + p_tr[db][1]), dk[db]);
           }
         }
       }
@@ -753,37 +774,6 @@ constexpr uint32_t kOffDout = offsetof(FStage, dout), kOffO = offsetof(FStage, o
 constexpr uint32_t kOffLse = offsetof(FStage, lse), kOffNlse = offsetof(FStage, nlse);
 constexpr uint32_t kOffNdelta = offsetof(FStage, ndelta);
 
-// LDS accesses by byte address.  The kernel keeps each per-lane address
-// pattern in one register and adds stage and block offsets as constants,
-// which the instructions take as immediate offsets.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(SA_LDS const void*)p; }
-template <typename V>
-__device__ __forceinline__ V lds_ld(uint32_t a) {
-  return *(SA_LDS const V*)a;
-}
-template <typename V>
-__device__ __forceinline__ void lds_st(uint32_t a, V v) {
-  *(SA_LDS V*)a = v;
-}
-__device__ __forceinline__ bf16x8 lds_tr8(uint32_t a0, uint32_t a1) {
-  i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS i16x4*)a0);
-  i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS i16x4*)a1);
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-// Byte offset of element (r, col) of a swizzled 64-column bf16 tile.
-__device__ __forceinline__ uint32_t swz_b(int r, int col) { return (uint32_t)swz(r, col) * (uint32_t)sizeof(bf16); }
-// Byte offsets of the two transposing reads of frag_tr_swz(X, 0, n0, lane);
-// frag_tr_swz(X, 16 c, n0, lane) reads 2048 c bytes further.
-__device__ __forceinline__ void tr_pattern(int n0, int lane, uint32_t& a0, uint32_t& a1) {
-  const int G = lane >> 4, j = lane & 15;
-  const int r = 8 * (G >> 1) + (j >> 2);
-  const int col = n0 + 16 * (G & 1) + 4 * (j & 3);
-  a0 = swz_b(r, col);
-  a1 = swz_b(r + 4, col);
-}
-// Keeps a value in its register and opaque to the optimizer from here on, so
-// that addresses formed from it are not precomputed per stage.
-#define SA_OPAQUE(x) asm volatile("" : "+v"(x))
 
 __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
   __shared__ FLds lds;
@@ -959,13 +949,13 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
   // `nx`, prefetch step cs + 2 into `nn` (the stage of step cs - 1).
   int cs = 0;
   auto step = [&](FStage& st, FStage& nx, FStage& nn) {
-    SA_OPAQUE(p_seed);
+    lds_opaque(p_seed);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) SA_OPAQUE(p_row[c]);
+    for (int c = 0; c < 4; ++c) lds_opaque(p_row[c]);
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-      SA_OPAQUE(p_tr[db][0]);
-      SA_OPAQUE(p_tr[db][1]);
+      lds_opaque(p_tr[db][0]);
+      lds_opaque(p_tr[db][1]);
     }
     const uint32_t S = lds_addr(&st);
     lds_barrier();  // statistics and scaled queries of `st` ready; ds and `nn` free
@@ -1058,10 +1048,10 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
     if (w < 4) {
       // dQ^T block (d 32*db_q .. +31, rows 32*nb_q .. +31 of the step) = K^T dS^T
       // over the 256 keys; register r: d = 32*db_q + 8*(r/4) + 4*h2 + r%4.
-      SA_OPAQUE(p_ks[0]);
-      SA_OPAQUE(p_ks[1]);
-      SA_OPAQUE(p_dsr[0]);
-      SA_OPAQUE(p_dsr[1]);
+      lds_opaque(p_ks[0]);
+      lds_opaque(p_ks[1]);
+      lds_opaque(p_dsr[0]);
+      lds_opaque(p_dsr[1]);
       f32x16 acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
@@ -1071,7 +1061,7 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
                      lds_tr8(p_dsr[0] + 2048u * c, p_dsr[1] + 2048u * c), acc);
       // Out through the consumed stage's Q tile (idle until the next step's
       // prefetch, which follows that step's barrier).
-      SA_OPAQUE(p_epw);
+      lds_opaque(p_epw);
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
         const f32x4 v = {acc[4 * gi] * a.scale, acc[4 * gi + 1] * a.scale, acc[4 * gi + 2] * a.scale,
@@ -1088,8 +1078,8 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
           *(bf16x8*)((bf16*)a.dq + (long)(bos + qrow) * qs + (g * G + j) * kD + 32 * db_q + 8 * jc) = x;
       }
     } else if (cs + 1 < nsteps) {
-      SA_OPAQUE(p_st[0]);
-      SA_OPAQUE(p_st[1]);
+      lds_opaque(p_st[0]);
+      lds_opaque(p_st[1]);
       stats(nx, cs + 1);
     }
     ++cs;
@@ -1130,7 +1120,6 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
     }
   }
 }
-#undef SA_OPAQUE
 
 int flat_blocks(long work_items) {
   const long b = (work_items + kFlatThreads - 1) / kFlatThreads;

@@ -255,6 +255,41 @@ __device__ __forceinline__ TileUnit xcd_unit(int num_heads, int num_seqs) {
   return t;
 }
 
+// ---------------------------------------------------------------------------
+// LDS accesses by byte address.  A kernel keeps each per-lane address pattern
+// in one register and adds stage and block offsets as constants, which the
+// instructions take as immediate offsets (below 64 KB).  Without this, an
+// unrolled ring of named stages gets every (pattern, stage) address hoisted
+// into a register of its own.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(SA_LDS const void*)p; }
+template <typename V>
+__device__ __forceinline__ V lds_ld(uint32_t a) {
+  return *(SA_LDS const V*)a;
+}
+template <typename V>
+__device__ __forceinline__ void lds_st(uint32_t a, V v) {
+  *(SA_LDS V*)a = v;
+}
+__device__ __forceinline__ bf16x8 lds_tr8(uint32_t a0, uint32_t a1) {
+  i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS i16x4*)a0);
+  i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS i16x4*)a1);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// Byte offset of element (r, col) of a swizzled 64-column bf16 tile.
+__device__ __forceinline__ uint32_t swz_b(int r, int col) { return (uint32_t)swz(r, col) * (uint32_t)sizeof(bf16); }
+// Byte offsets of the two transposing reads of frag_tr_swz(X, 0, n0, lane);
+// frag_tr_swz(X, 16 c, n0, lane) reads 2048 c bytes further.
+__device__ __forceinline__ void tr_pattern(int n0, int lane, uint32_t& a0, uint32_t& a1) {
+  const int G = lane >> 4, j = lane & 15;
+  const int r = 8 * (G >> 1) + (j >> 2);
+  const int col = n0 + 16 * (G & 1) + 4 * (j & 3);
+  a0 = swz_b(r, col);
+  a1 = swz_b(r + 4, col);
+}
+// Keeps a value in its register and opaque to the optimizer from here on, so
+// that addresses formed from it are not precomputed per stage.
+__device__ __forceinline__ void lds_opaque(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
 // acc + x.x + x.y in one instruction (v_dot2_f32_bf16 against (1, 1)).
 __device__ __forceinline__ float dot2_bf16(bf16x2 x, float acc) {
   const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
