@@ -246,7 +246,7 @@ int resolve_dkdv_heads(const sink_attn_params* p, int* out) {
     return SINK_ATTN_OK;
   }
   *out = sinkattn::dkdv_heads_per_workgroup(p->total_tokens, p->max_seqlen, p->num_q_heads, p->num_kv_heads,
-                                            p->window);
+                                            p->window, p->dtype, p->head_dim);
   return SINK_ATTN_OK;
 }
 

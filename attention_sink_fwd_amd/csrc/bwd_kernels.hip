@@ -1162,7 +1162,8 @@ bool bwd_window_fusable(int dtype, int head_dim, int window, int max_seqlen, int
          hq / hkv <= kFMaxGroup;
 }
 
-int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, int window) {
+int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, int window, int dtype,
+                             int head_dim) {
   constexpr long num_cus = 256;
   const int grp = hq / hkv;
   // Work in (64-row query step x 128-key tile) units.  Longest workgroup per
@@ -1179,9 +1180,19 @@ int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, 
   // group) such that the longest workgroup fits in a slot's average load and the
   // tail it leaves (its excess over an average workgroup) stays within an
   // eighth of that load.
-  for (int hg = grp; hg > 1; --hg)
-    if (grp % hg == 0 && hg * steps_max <= per_slot && 8 * hg * (steps_max - steps_avg) <= per_slot) return hg;
-  return 1;
+  int hg = 1;
+  for (int c = grp; c > 1; --c)
+    if (grp % c == 0 && c * steps_max <= per_slot && 8 * c * (steps_max - steps_avg) <= per_slot) {
+      hg = c;
+      break;
+    }
+  // The instance for bf16, head_dim 64 and no window cut fits three
+  // workgroups per CU; there two heads per workgroup (half the partial-sum
+  // planes) measured faster than one at 4096, 65536 and mixed lengths up to
+  // 8192 tokens, as long as the workgroups still fill every slot.
+  const bool three_per_cu = dtype == 0 && head_dim == kD && !(window > 0 && window < max_seqlen);
+  if (three_per_cu && hg == 1 && grp % 2 == 0 && tiles * (hq / 2) >= 3 * num_cus) hg = 2;
+  return hg;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t stream,

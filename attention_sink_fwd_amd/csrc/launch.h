@@ -68,7 +68,8 @@ bool bwd_window_fusable(int dtype, int head_dim, int window, int max_seqlen, int
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s);
 // Query heads per dK/dV workgroup for a problem shape (a divisor of Hq/Hkv),
 // sized for the 256 compute units of an MI355X.
-int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, int window);
+int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, int window, int dtype,
+                             int head_dim);
 // events: NULL, or four events (NULL entries skipped) recorded around the three kernels.
 hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s,
                       const hipEvent_t* events);
