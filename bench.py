@@ -87,7 +87,7 @@ def traffic_for_current_kernel(kernel, workload):
     """
     try:
         with open(TRAFFIC_FILE) as f:
-            entry = json.load(f)[kernel]
+            entry = json.load(f)[f"{kernel}@{workload}"]
         if entry.get("workload") != workload:
             return None
         if entry.get("sources_sha256") != sources_sha256(entry["sources"]):

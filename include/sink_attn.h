@@ -52,14 +52,18 @@
  * max_seqlen (set SINK_ATTN_VALIDATE=1 to have the host copy and check it,
  * which synchronises the stream).
  *
- * Tuning.  The backward's dK/dV kernel gives each workgroup one 128-key tile
+ * Tuning.  For bf16, head_dim 64 and a window of 1..128 keys (shorter than
+ * max_seqlen) the backward runs one fused kernel (see sink_attn_bwd_fused;
+ * SINK_ATTN_BWD_FUSED=0 selects the separate kernels instead).  Otherwise
+ * the backward's dK/dV kernel gives each workgroup one 128-key tile
  * and some of the query heads that share its KV head: all of them when the
  * problem has enough parallel work (dK, dV written once), else fewer, each
  * workgroup storing its float partial sums to the workspace for a fixed-order
  * sum.  The library picks the number from the shape (for an MI355X's 256
  * compute units); SINK_ATTN_DKDV_HEADS=n (a divisor of num_q_heads /
  * num_kv_heads) overrides it, for tests and tuning.  The workspace size
- * depends on it: query sink_attn_bwd_workspace_size under the same setting.
+ * depends on these choices: query sink_attn_bwd_workspace_size under the
+ * same settings.
  * The forward and dQ kernels pack the query heads of one KV head into a
  * workgroup (up to 32, a power of two dividing num_q_heads / num_kv_heads),
  * so each key/value tile is loaded once for all of them;
@@ -165,11 +169,14 @@ int sink_attn_fwd_paged(const sink_attn_params *p, const sink_attn_paged_kv *kv,
 
 /*
  * Bytes of device workspace sink_attn_bwd needs for these parameters
- * (float row statistics [2, Hq, T], the bf16 scaled queries
+ * (256-byte aligned sections).  With the separate dQ and dK/dV kernels: float
+ * row statistics [2, Hq, T], the bf16 scaled queries
  * q * softmax_scale * log2(e) [T, Hq, d] that every kernel scores with,
  * float dK/dV partial sums of the head groups and per-query-tile dS
- * partials, 256-byte aligned sections; the last depends on max_seqlen and
- * num_seqs).  Returns 0 when the parameters are invalid.
+ * partials (these depend on max_seqlen and num_seqs).  With the fused
+ * short-window kernel: two float dK/dV partial-sum planes [2, 2, T, Hkv, d]
+ * and the dS partials of its 128-row tiles.  Returns 0 when the parameters
+ * are invalid.
  */
 size_t sink_attn_bwd_workspace_size(const sink_attn_params *p);
 
@@ -239,9 +246,11 @@ int sink_attn_bwd(const sink_attn_params *p, const void *q, const void *k, const
  * dK/dV additions changes), unless SINK_ATTN_DKDV_HEADS fixes the split.  A
  * shape whose workspace does not fit in any split returns
  * SINK_ATTN_ERR_UNSUPPORTED with the size it needs, before anything is
- * enqueued: the row statistics and the scaled queries alone take
- * 8 + 2 * head_dim bytes per query head and token (num_q_heads *
- * total_tokens up to about 490 thousand at head_dim 64).
+ * enqueued: for the separate kernels the row statistics and the scaled
+ * queries alone take 8 + 2 * head_dim bytes per query head and token
+ * (num_q_heads * total_tokens up to about 490 thousand at head_dim 64).
+ * When the fused short-window kernel's workspace (16 * head_dim bytes per KV
+ * head and token) does not fit, the separate kernels run instead.
  *   All calls on one device share its buffer: calls that overlap in time on
  * one device (two streams, or two threads) race and give wrong results; calls
  * ordered on one stream are safe.  The buffer's contents on entry are ignored
