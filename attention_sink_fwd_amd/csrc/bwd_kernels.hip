@@ -163,8 +163,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int nsteps = HG * (qt1 - qt0);
 
   // Prefetch cursor: head pj, query tile pt of step pf; it stops at the last
-  // step, so the ring's look-ahead past the end re-loads that tile.
-  int pf = 0, pj = 0, pt = qt0;
+  // step, so the ring's look-ahead past the end re-loads that tile.  Each
+  // head's query tiles run from the last down to the diagonal one: every key
+  // tile of a head then starts at the same query tile, so the workgroups that
+  // run together read the same Q and dO tiles and share them in L2.
+  int pf = 0, pj = 0, pt = qt1 - 1;
   // Direct loads: this wavefront stages rows 16 w .. 16 w + 15 of the Q and
   // dO tiles (two 8-row blocks; lane l moves 16 bytes of row 8 blk + l / 8
   // into its swizzled slot) and one statistics row; the byte offsets within
@@ -212,8 +215,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     }
     if (pf + 1 < nsteps) {
       ++pf;
-      if (++pt == qt1) {
-        pt = qt0;
+      if (--pt < qt0) {
+        pt = qt1 - 1;
         ++pj;
       }
     }
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
   // One step: consume query tile ct (of some head) from `st`, prefetch two
   // steps ahead into `nx` (the stage consumed in the previous step).
-  int ct = qt0;
+  int ct = qt1 - 1;
   auto step = [&](const QStage& st, QStage& nx) {
     lds_opaque(p_seed);
 #pragma unroll
@@ -281,7 +284,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
     prefetch(nx);
     issue_fence();
     const int qb = ct * kBM;
-    if (++ct == qt1) ct = qt0;
+    if (--ct < qt0) ct = qt1 - 1;
 
     const bool active = wk_lo < L && wk_lo <= qb + kBM - 1 && !(window > 0 && qb - wk_hi >= window);
     if (active) {
