@@ -322,6 +322,7 @@ int bwd_enqueue(const sink_attn_params* p, const BwdTensors& t, void* workspace,
   a.dkdv_heads = split.dkdv_heads;
   a.heads_per_tile = split.pack_heads;
   a.fused = split.fused ? 1 : 0;
+  a.dsink_tiles = (p->max_seqlen + 127) / 128;
   a.dkdv_planes = split.fused ? 2 : p->num_q_heads / p->num_kv_heads / split.dkdv_heads;
   hipError_t e = launch_bwd(a, p->dtype, p->max_seqlen, p->num_seqs, s, g_bwd_events_on ? g_bwd_events : nullptr);
   if (e != hipSuccess) return fail(SINK_ATTN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));

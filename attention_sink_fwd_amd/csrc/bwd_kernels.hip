@@ -771,7 +771,7 @@ struct __attribute__((aligned(16))) FLds {
   FStage s0, s1, s2;    // ring of 64-row steps
   bf16 ks[kFK * kD];    // K of the 256 keys, swizzled [key][d]
   bf16 ds[kFK * kBM];   // dS^T of the current step, swizzled [key][row]
-  float wsum[kFMaxGroup][4];
+  float wsum[2][kFMaxGroup][4];  // per query tile of the pair, head, statistics wavefront
 };
 constexpr uint32_t kOffDout = offsetof(FStage, dout), kOffO = offsetof(FStage, o);
 constexpr uint32_t kOffLse = offsetof(FStage, lse), kOffNlse = offsetof(FStage, nlse);
@@ -786,17 +786,21 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
   const int h2 = lane >> 5, l32 = lane & 31;
   const int G = a.num_q_heads / a.num_kv_heads;
   const TileUnit unit = xcd_unit(a.num_kv_heads, a.num_seqs);
-  const int seq = unit.seq, g = unit.head, qt = unit.rank;
-  const int ntiles = (int)gridDim.x / (a.num_kv_heads * a.num_seqs);
+  const int seq = unit.seq, g = unit.head, pr = unit.rank;  // query tiles 2*pr and 2*pr + 1
   const int T = a.total_tokens, window = a.window;
-  // dS partial of query head g*G + j for this tile: dsink_slots[j * slot_stride]
+  // dS partial of query head g*G + j for query tile 2*pr + ph:
+  // dsink_slots[j * slot_stride + ph] (tiles past the layout are not written)
+  const int ntiles = a.dsink_tiles;
   const long slot_stride = (long)a.num_seqs * ntiles;
-  float* __restrict__ dsink_slots = a.dsink_part + ((long)g * G * a.num_seqs + seq) * ntiles + qt;
+  float* __restrict__ dsink_slots = a.dsink_part + ((long)g * G * a.num_seqs + seq) * ntiles + 2 * pr;
   const int bos = a.cu_seqlens[seq];
   const int L = a.cu_seqlens[seq + 1] - bos;
-  const int q0 = qt * kFQ;
+  const int q0 = pr * 2 * kFQ;
   if (q0 >= L) {
-    for (int j = tid; j < G; j += 512) dsink_slots[j * slot_stride] = 0.0f;
+    for (int j = tid; j < G; j += 512) {
+      if (2 * pr < ntiles) dsink_slots[j * slot_stride] = 0.0f;
+      if (2 * pr + 1 < ntiles) dsink_slots[j * slot_stride + 1] = 0.0f;
+    }
     return;
   }
   const int qs = a.num_q_heads * kD, ks = a.num_kv_heads * kD;  // row strides (< 2^31 elements)
@@ -807,18 +811,35 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
   const bf16* __restrict__ Kg = (const bf16*)a.k + (long)bos * ks + g * kD;
   const bf16* __restrict__ Vg = (const bf16*)a.v + (long)bos * ks + g * kD;
   const int kbase = q0 - kFQ;                     // first key of the span (< 0 for the first tile)
-  const int nrb = L - q0 > kBM ? 2 : 1;           // 64-row steps per head
-  const int nsteps = G * nrb;
+  // Phase ph takes query tile 2*pr + ph in 64-row steps, head after head.
+  const int nph = L - q0 > kFQ ? 2 : 1;
+  const int nrb0 = L - q0 > kBM ? 2 : 1;
+  const int nrb1 = nph == 2 ? (L - q0 - kFQ > kBM ? 2 : 1) : 0;
+  const int nsteps0 = G * nrb0, nsteps = nsteps0 + G * nrb1;
+  auto step_of = [&](int st_i, int& ph, int& j, int& rb) {
+    if (st_i < nsteps0) {
+      ph = 0;
+      j = nrb0 == 2 ? st_i >> 1 : st_i;
+      rb = st_i - j * nrb0;
+    } else {
+      const int t = st_i - nsteps0;
+      ph = 1;
+      j = nrb1 == 2 ? t >> 1 : t;
+      rb = t - j * nrb1;
+    }
+  };
 
-  // Prefetch cursor (head pj, row block prb of step pf); it stops at the last
-  // step, so the ring's look-ahead past the end re-loads that step.
-  int pf = 0, pj = 0, prb = 0;
+  // Prefetch cursor (step pf); it stops at the last step, so the ring's
+  // look-ahead past the end re-loads that step.
+  int pf = 0;
   // This lane stages 16 bytes of row r_own of each 64-row tile into its
   // swizzled slot (wavefront w: rows 8w .. 8w + 7).
   const int r_own = 8 * w + (lane >> 3);
   const uint32_t voff = (uint32_t)(r_own * qs + 8 * ((lane & 7) ^ swz_f(r_own))) * (uint32_t)sizeof(bf16);
   auto prefetch = [&](FStage& st) {
-    const int qb = q0 + kBM * prb;
+    int pph, pj, prb;
+    step_of(pf, pph, pj, prb);
+    const int qb = q0 + kFQ * pph + kBM * prb;
     const int rem = L - qb;  // >= 1: rows from the tile's first on (rows past the end repeat the last)
     uint32_t off = voff, soff = (uint32_t)lane * (uint32_t)sizeof(float);
     if (rem < kBM) {
@@ -830,32 +851,31 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
     lds_dma16_s(off, dOg + ro, st.dout + 512 * w);
     lds_dma16_s(off, Og + ro, st.o + 512 * w);
     lds_dma4_s(soff, lse_g + (long)pj * T + qb, w == 0 ? st.lse : st.spare);
-    if (pf + 1 < nsteps) {
-      ++pf;
-      if (++prb == nrb) {
-        prb = 0;
-        ++pj;
-      }
-    }
+    if (pf + 1 < nsteps) ++pf;
   };
   prefetch(lds.s0);
   issue_fence();
   prefetch(lds.s1);
   issue_fence();
   // K of the 256 keys into LDS (keys outside the sequence repeat its first or
-  // last key; they are masked), and this wavefront's K and V fragments: B
-  // operands of S = Q K^T and dP = dO V^T (lane = key column).
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int blk = 4 * w + i;
-    const int r = 8 * blk + (lane >> 3);
-    const int key = min(max(kbase + r, 0), L - 1);
-    lds_dma16(Kg + (long)key * ks + 8 * ((lane & 7) ^ swz_f(r)), lds.ks + 512 * blk);
-  }
-  const int wk_lo = kbase + 32 * w, wk_hi = wk_lo + 31;
-  const int key_n = wk_lo + l32;
+  // last key; they are masked): rows 0..127 hold wavefronts 0..3's keys (the
+  // tile before 2*pr in phase 0, the tile after it in phase 1), rows
+  // 128..255 the keys of tile 2*pr (wavefronts 4..7, both phases).  Each
+  // wavefront's own K and V fragments are the B operands of S = Q K^T and
+  // dP = dO V^T (lane = key column).
+  auto stage_keys = [&](int blk0, int nblk, int key0) {
+    for (int i = 0; i < nblk; ++i) {
+      const int blk = blk0 + i;
+      const int r = 8 * blk + (lane >> 3);
+      const int key = min(max(key0 + 8 * i + (lane >> 3), 0), L - 1);
+      lds_dma16(Kg + (long)key * ks + 8 * ((lane & 7) ^ swz_f(r)), lds.ks + 512 * blk);
+    }
+  };
+  stage_keys(4 * w, 4, kbase + 32 * w);
+  int wk_lo = kbase + 32 * w;
+  int key_n = wk_lo + l32;
   bf16x8 kf[4], vf[4];
-  {
+  auto load_kv = [&]() {
     const int krow = min(max(key_n, 0), L - 1);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -863,7 +883,8 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
       kf[c] = load8(Kg + (long)krow * ks + d0);
       vf[c] = load8(Vg + (long)krow * ks + d0);
     }
-  }
+  };
+  load_kv();
 
   // Per-lane LDS address patterns (bytes).  Stage-relative ones get the
   // stage's offset added as a constant.
@@ -917,7 +938,8 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
   float sterm = 0.0f;  // sink terms -p_sink D of this thread's rows, current head
   auto stats = [&](FStage& st, int sidx) {
     const uint32_t S = lds_addr(&st);
-    const int j = nrb == 2 ? sidx >> 1 : sidx, rb = sidx - j * nrb;
+    int ph, j, rb;
+    step_of(sidx, ph, j, rb);
     float dpart = 0.0f;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -934,11 +956,11 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
       const float lse = lds_ld<float>(S + kOffLse + p_srow);
       lds_st<float>(S + kOffNlse + p_srow, -lse * kLog2e);
       lds_st<float>(S + kOffNdelta + p_srow, -dpart);
-      if (q0 + kBM * rb + srow < L) sterm += -__expf(a.sinks[g * G + j] - lse) * dpart;
+      if (q0 + kFQ * ph + kBM * rb + srow < L) sterm += -__expf(a.sinks[g * G + j] - lse) * dpart;
     }
-    if (rb == nrb - 1) {  // the head's last step: this wavefront's share of dS_h
+    if (rb == (ph == 0 ? nrb0 : nrb1) - 1) {  // the head's last step in this tile: this wavefront's share of dS_h
       const float sw = wave_sum(sterm);
-      if (lane == 0) lds.wsum[j][w - 4] = sw;
+      if (lane == 0) lds.wsum[ph][j][w - 4] = sw;
       sterm = 0.0f;
     }
   };
@@ -947,6 +969,35 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
   f32x16 dk[2], dv[2];
 #pragma unroll
   for (int i = 0; i < 16; ++i) { dk[0][i] = dk[1][i] = dv[0][i] = dv[1][i] = 0.0f; }
+
+  // dK, dV of this wavefront's keys (register r: key wk_lo + 8*(r/4) +
+  // 4*h2 + r%4): mode 0 or 1 into that float plane, 2 directly in the output
+  // type (a key tile whose contributions are all in this workgroup).
+  const long plane = (long)T * ks;
+  auto store_dkdv = [&](int mode) {
+    if (wk_lo < 0) return;
+    float* dk_p = a.dk_part + (mode == 1 ? plane : 0) + (long)bos * ks + g * kD;
+    float* dv_p = a.dv_part + (mode == 1 ? plane : 0) + (long)bos * ks + g * kD;
+    bf16* dk_o = (bf16*)a.dk + (long)bos * ks + g * kD;
+    bf16* dv_o = (bf16*)a.dv + (long)bos * ks + g * kD;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int d = 32 * db + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = wk_lo + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        if (key < L) {
+          if (mode == 2) {
+            dk_o[(long)key * ks + d] = (bf16)(dk[db][r] * kLn2);
+            dv_o[(long)key * ks + d] = (bf16)dv[db][r];
+          } else {
+            dk_p[(long)key * ks + d] = dk[db][r] * kLn2;
+            dv_p[(long)key * ks + d] = dv[db][r];
+          }
+        }
+      }
+    }
+  };
 
   // One step: consume `st` (step cs), compute the statistics of step cs + 1 in
   // `nx`, prefetch step cs + 2 into `nn` (the stage of step cs - 1).
@@ -964,8 +1015,10 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
     lds_barrier();  // statistics and scaled queries of `st` ready; ds and `nn` free
     prefetch(nn);
     issue_fence();
-    const int j = nrb == 2 ? cs >> 1 : cs, rb = cs - j * nrb;
-    const int qb = q0 + kBM * rb;
+    int ph, j, rb;
+    step_of(cs, ph, j, rb);
+    const int qb = q0 + kFQ * ph + kBM * rb;
+    const int wk_hi = wk_lo + 31;
     const bool active = wk_lo >= 0 && wk_lo < L && wk_lo <= qb + kBM - 1 && qb - wk_hi < window;
     if (active) {
       const bool mask_lo = wk_hi > qb;
@@ -1085,6 +1138,22 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
       lds_opaque(p_st[1]);
       stats(nx, cs + 1);
     }
+    if (cs == nsteps0 - 1 && nph == 2) {
+      // End of tile 2*pr: wavefronts 0..3 hand in the tile before it and take
+      // the tile after it (ks rows 0..127 are free once every wavefront has
+      // finished this step's dQ).
+      lds_barrier();
+      if (w < 4) {
+        store_dkdv(1);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { dk[0][i] = dk[1][i] = dv[0][i] = dv[1][i] = 0.0f; }
+        wk_lo = q0 + kFQ + 32 * w;
+        key_n = wk_lo + l32;
+        stage_keys(4 * w, 4, wk_lo);
+        load_kv();
+      }
+      wait_vmem_all();
+    }
     ++cs;
   };
   for (int f = 0; f < nsteps; f += kStages) {
@@ -1097,30 +1166,63 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
   // after the barrier.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int j = tid; j < G; j += 512)
-    dsink_slots[j * slot_stride] = (lds.wsum[j][0] + lds.wsum[j][1]) + (lds.wsum[j][2] + lds.wsum[j][3]);
-  // dK, dV of this wavefront's keys (register r: key wk_lo + 8*(r/4) + 4*h2 + r%4)
-  // into plane 0 (keys of this tile) or 1 (keys of the tile before).
-  if (wk_lo < 0) return;
-  const long plane = (long)T * ks;
-  const bool own = w >= 4, last = q0 + kFQ >= L;
-  float* dk_g = a.dk_part + (own ? 0 : plane) + (long)bos * ks + g * kD;
-  float* dv_g = a.dv_part + (own ? 0 : plane) + (long)bos * ks + g * kD;
-#pragma unroll
-  for (int db = 0; db < 2; ++db) {
-    const int d = 32 * db + l32;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = wk_lo + 8 * (r >> 2) + 4 * h2 + (r & 3);
-      if (key < L) {
-        dk_g[(long)key * ks + d] = dk[db][r] * kLn2;
-        dv_g[(long)key * ks + d] = dv[db][r];
-        if (own && last) {
-          dk_g[plane + (long)key * ks + d] = 0.0f;
-          dv_g[plane + (long)key * ks + d] = 0.0f;
-        }
-      }
+  for (int j = tid; j < G; j += 512) {
+    const float* ws0 = lds.wsum[0][j];
+    dsink_slots[j * slot_stride] = (ws0[0] + ws0[1]) + (ws0[2] + ws0[3]);
+    if (2 * pr + 1 < ntiles) {
+      const float* ws1 = lds.wsum[1][j];
+      dsink_slots[j * slot_stride + 1] = nph == 2 ? (ws1[0] + ws1[1]) + (ws1[2] + ws1[3]) : 0.0f;
     }
+  }
+  // Tile 2*pr (wavefronts 4..7) has all its contributions: the rows of tiles
+  // 2*pr and 2*pr + 1.  Wavefronts 0..3 hold the tile before it (one phase:
+  // plane 1, the next tile's rows) or the tile after it: plane 0 if a later
+  // workgroup adds that tile's next rows, else complete.
+  if (w >= 4)
+    store_dkdv(2);
+  else if (nph == 1)
+    store_dkdv(1);
+  else
+    store_dkdv(q0 + 2 * kFQ >= L ? 2 : 0);
+}
+
+// dK, dV of the key tiles that two fused workgroups share: odd tile
+// t = 2*pr + 1 of each sequence, when tile t + 1 has rows, is plane 0 + plane 1
+// (in that order).  Blocks: (sequence, pair) x 8 blocks of 16 tokens, then
+// one per query head for dS_h (as in bwd_post_kernel).
+__global__ __launch_bounds__(256) void bwd_window_post_kernel(BwdArgs a, int plane_blocks, int npairs, int parts) {
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x >= plane_blocks) {
+    __shared__ float part[kFlatThreads];
+    const int h = blockIdx.x - plane_blocks;
+    if (h >= a.num_q_heads) return;
+    float s = 0.0f;
+    for (int j = tid; j < parts; j += kFlatThreads) s += a.dsink_part[(long)h * parts + j];
+    part[tid] = s;
+    __syncthreads();
+    for (int n = kFlatThreads / 2; n > 0; n >>= 1) {
+      if (tid < n) part[tid] += part[tid + n];
+      __syncthreads();
+    }
+    if (tid == 0) a.dsinks[h] = part[0];
+    return;
+  }
+  const int unit = blockIdx.x >> 3, sub = blockIdx.x & 7;
+  const int seq = unit / npairs, pr = unit - seq * npairs;
+  const int bos = a.cu_seqlens[seq];
+  const int L = a.cu_seqlens[seq + 1] - bos;
+  const int t = 2 * pr + 1;
+  if (kFQ * (t + 1) >= L) return;  // no tile after t: the fused workgroup wrote it whole
+  const int ks = a.num_kv_heads * kD;
+  const long base = (long)(bos + kFQ * t + 16 * sub) * ks;  // 16 tokens, contiguous
+  const long plane = (long)a.total_tokens * ks;
+  const int chunks = 16 * ks / 8;
+  for (int c = tid; c < 2 * chunks; c += kFlatThreads) {
+    const bool is_k = c < chunks;
+    const long e = base + 8L * (is_k ? c : c - chunks);
+    const float* src = (is_k ? a.dk_part : a.dv_part) + e;
+    const f32x8 acc = load8f(src) + load8f(src + plane);
+    store8((bf16*)(is_k ? a.dk : a.dv) + e, acc);
   }
 }
 
@@ -1209,13 +1311,20 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs,
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return e;
   if (a.fused) {
-    // One kernel in place of the dQ and dK/dV kernels (both event slots mark its end).
+    // One kernel in place of the dQ and dK/dV kernels (both event slots mark
+    // its end), then the shared key tiles' planes and dS.
+    const int npairs = (max_seqlen + 2 * kFQ - 1) / (2 * kFQ);
     if (T > 0) {
-      const dim3 grid((max_seqlen + kFQ - 1) / kFQ * a.num_kv_heads * num_seqs);
-      hipLaunchKernelGGL(bwd_window_kernel, grid, dim3(512), 0, stream, a);
+      hipLaunchKernelGGL(bwd_window_kernel, dim3(npairs * a.num_kv_heads * num_seqs), dim3(512), 0, stream, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if ((e = mark(1)) != hipSuccess) return e;
+    if ((e = mark(2)) != hipSuccess) return e;
+    const int plane_blocks = T > 0 ? npairs * num_seqs * 8 : 0;
+    hipLaunchKernelGGL(bwd_window_post_kernel, dim3(plane_blocks + Hq), dim3(kFlatThreads), 0, stream, a,
+                       plane_blocks, npairs, parts);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return mark(3);
   } else {
     const dim3 grid_kv((max_seqlen + kBN - 1) / kBN * (Hq / a.dkdv_heads) * num_seqs);
     const int qrows = kQT / a.heads_per_tile;

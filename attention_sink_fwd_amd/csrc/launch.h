@@ -49,6 +49,7 @@ struct BwdArgs {
   int dkdv_heads;      // query heads per dK/dV workgroup (divides Hq / Hkv)
   int dkdv_planes;     // float dK/dV partial-sum planes the post kernel adds (1: dK, dV written directly)
   int fused;           // 1: the fused short-window kernel replaces the dQ and dK/dV kernels
+  int dsink_tiles;     // fused kernel: 128-row tiles per (head, sequence) in the dS partial layout
   int heads_per_tile;  // query heads of one KV head packed in a dQ workgroup (divides Hq/Hkv and 32)
   float scale;
   float scale_log2;
