@@ -48,11 +48,13 @@
 // whole backward pass.  Recomputing S and dP in the dQ kernel costs two
 // extra matrix products per visible block instead.
 #include <algorithm>
+#include <cstdio>
 #include <cstddef>
 #include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
+#include "launch_debug.h"
 
 namespace sinkattn {
 
@@ -1308,6 +1310,9 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs,
   const int conv_blocks = (T > 0 && a.dkdv_planes > 1) ? flat_blocks(chunks) : 0;
   const int post_blocks = conv_blocks + Hq;
   auto mark = [&](int i) { return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess; };
+  char split[96];
+  std::snprintf(split, sizeof(split), "fused=%d dkdv_heads=%d pack_heads=%d planes=%d", a.fused, a.dkdv_heads,
+                a.heads_per_tile, a.dkdv_planes);
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return e;
   if (a.fused) {
@@ -1315,15 +1320,18 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs,
     // its end), then the shared key tiles' planes and dS.
     const int npairs = (max_seqlen + 2 * kFQ - 1) / (2 * kFQ);
     if (T > 0) {
-      hipLaunchKernelGGL(bwd_window_kernel, dim3(npairs * a.num_kv_heads * num_seqs), dim3(512), 0, stream, a);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      const dim3 grid(npairs * a.num_kv_heads * num_seqs);
+      hipLaunchKernelGGL(bwd_window_kernel, grid, dim3(512), 0, stream, a);
+      if ((e = after_launch("bwd_window_kernel", grid, dim3(512), split, stream)) != hipSuccess) return e;
     }
     if ((e = mark(1)) != hipSuccess) return e;
     if ((e = mark(2)) != hipSuccess) return e;
     const int plane_blocks = T > 0 ? npairs * num_seqs * 8 : 0;
     hipLaunchKernelGGL(bwd_window_post_kernel, dim3(plane_blocks + Hq), dim3(kFlatThreads), 0, stream, a,
                        plane_blocks, npairs, parts);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = after_launch("bwd_window_post_kernel", dim3(plane_blocks + Hq), dim3(kFlatThreads), split, stream)) !=
+        hipSuccess)
+      return e;
     return mark(3);
   } else {
     const dim3 grid_kv((max_seqlen + kBN - 1) / kBN * (Hq / a.dkdv_heads) * num_seqs);
@@ -1341,7 +1349,10 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs,
         hipLaunchKernelGGL((bwd_dq_kernel<bf16, false, true>), grid_q, dim3(256), 0, stream, a);
       else
         hipLaunchKernelGGL((bwd_dq_kernel<float, false, true>), grid_q, dim3(256), 0, stream, a);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = after_launch(direct ? (windowed ? "bwd_dq_kernel<direct,windowed>" : "bwd_dq_kernel<direct>")
+                                   : "bwd_dq_kernel<generic>",
+                            grid_q, dim3(256), split, stream)) != hipSuccess)
+        return e;
     }
     if ((e = mark(1)) != hipSuccess) return e;
     if (T > 0) {
@@ -1353,7 +1364,10 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs,
         hipLaunchKernelGGL((bwd_dkdv_kernel<bf16, false, true>), grid_kv, dim3(256), 0, stream, a);
       else
         hipLaunchKernelGGL((bwd_dkdv_kernel<float, false, true>), grid_kv, dim3(256), 0, stream, a);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = after_launch(direct ? (windowed ? "bwd_dkdv_kernel<direct,windowed>" : "bwd_dkdv_kernel<direct>")
+                                   : "bwd_dkdv_kernel<generic>",
+                            grid_kv, dim3(256), split, stream)) != hipSuccess)
+        return e;
     }
   }
   if ((e = mark(2)) != hipSuccess) return e;
@@ -1361,7 +1375,8 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs,
     hipLaunchKernelGGL(bwd_post_kernel<bf16>, dim3(post_blocks), dim3(kFlatThreads), 0, stream, a, conv_blocks, parts);
   else
     hipLaunchKernelGGL(bwd_post_kernel<float>, dim3(post_blocks), dim3(kFlatThreads), 0, stream, a, conv_blocks, parts);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = after_launch("bwd_post_kernel", dim3(post_blocks), dim3(kFlatThreads), split, stream)) != hipSuccess)
+    return e;
   return mark(3);
 }
 

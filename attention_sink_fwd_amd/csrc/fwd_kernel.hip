@@ -29,10 +29,12 @@
 // (the ceiling of log2 of the row's largest P), so rescaling P, l and O is
 // exact.  Every decision depends on the row alone, so a row's bits do not
 // depend on the other rows that share its wavefront.
+#include <cstdio>
 #include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
+#include "launch_debug.h"
 
 namespace sinkattn {
 
@@ -451,7 +453,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
 }
 
 template <int kWaves>
-void launch_fwd_waves(const FwdArgs& a, bool direct, int dtype, int max_seqlen, int num_seqs, hipStream_t stream) {
+hipError_t launch_fwd_waves(const FwdArgs& a, bool direct, int dtype, int max_seqlen, int num_seqs,
+                            hipStream_t stream) {
   const int hp = a.heads_per_tile, rows = 32 * kWaves / hp;
   const dim3 grid((max_seqlen + rows - 1) / rows * (a.num_q_heads / hp) * num_seqs), block(64 * kWaves);
   if (a.block_table) {
@@ -469,6 +472,9 @@ void launch_fwd_waves(const FwdArgs& a, bool direct, int dtype, int max_seqlen, 
     else
       hipLaunchKernelGGL((fwd_kernel<float, false, false, kWaves>), grid, block, 0, stream, a);
   }
+  char split[64];
+  std::snprintf(split, sizeof(split), "paged=%d pack_heads=%d waves=%d", a.block_table ? 1 : 0, hp, kWaves);
+  return after_launch(direct ? "fwd_kernel<direct>" : "fwd_kernel<generic>", grid, block, split, stream);
 }
 
 }  // namespace
@@ -480,11 +486,8 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int max_seqlen, int num_seqs,
   // longer fit in L2 (3 % faster at 65536 tokens); below that, four
   // wavefronts per workgroup balance better (4 % faster at 4096).  Each
   // lane's arithmetic is the same either way.
-  if (!a.block_table && max_seqlen >= 16384)
-    launch_fwd_waves<8>(a, direct, dtype, max_seqlen, num_seqs, stream);
-  else
-    launch_fwd_waves<4>(a, direct, dtype, max_seqlen, num_seqs, stream);
-  return hipGetLastError();
+  if (!a.block_table && max_seqlen >= 16384) return launch_fwd_waves<8>(a, direct, dtype, max_seqlen, num_seqs, stream);
+  return launch_fwd_waves<4>(a, direct, dtype, max_seqlen, num_seqs, stream);
 }
 
 }  // namespace sinkattn

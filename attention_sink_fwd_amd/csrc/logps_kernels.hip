@@ -22,6 +22,7 @@
 
 #include "device_common.h"
 #include "logps_launch.h"
+#include "launch_debug.h"
 
 namespace sinkattn {
 
@@ -175,7 +176,7 @@ hipError_t launch_logps_fwd(const LogpsArgs& a, int dtype, hipStream_t stream) {
     hipLaunchKernelGGL(logps_fwd_kernel<bf16>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(logps_fwd_kernel<float>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  return after_launch("logps_fwd_kernel", dim3(a.num_rows), dim3(kThreads), "", stream);
 }
 
 hipError_t launch_logps_bwd(const LogpsArgs& a, int dtype, hipStream_t stream) {
@@ -183,7 +184,7 @@ hipError_t launch_logps_bwd(const LogpsArgs& a, int dtype, hipStream_t stream) {
     hipLaunchKernelGGL(logps_bwd_kernel<bf16>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(logps_bwd_kernel<float>, dim3(a.num_rows), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  return after_launch("logps_bwd_kernel", dim3(a.num_rows), dim3(kThreads), "", stream);
 }
 
 }  // namespace sinkattn

@@ -50,7 +50,11 @@
  * cu_seqlens lives on the device and is NOT read by the host: it must be
  * non-decreasing, start at 0, end at total_tokens, and no length may exceed
  * max_seqlen (set SINK_ATTN_VALIDATE=1 to have the host copy and check it,
- * which synchronises the stream).
+ * which synchronises the stream).  Debugging: SINK_ATTN_SYNC_DEBUG=1
+ * synchronises the stream after every kernel launch, so a kernel fault is
+ * returned as SINK_ATTN_ERR_HIP by the call that launched it (not for use
+ * under graph capture); SINK_ATTN_TRACE=1 prints one line per launch to
+ * stderr (kernel, grid, workgroup size, work split).
  *
  * Tuning.  For bf16, head_dim 64 and a window of 1..128 keys (shorter than
  * max_seqlen) the backward runs one fused kernel (see sink_attn_bwd_fused;

@@ -34,6 +34,11 @@ CASES = [
     ((250,), 8, 8, 128, "minus_inf"),
     ((190,), 4, 2, 50, "plus30"),
     ((1000,), 8, 2, 1, "normal"),
+    # workgroups take two 128-row tiles: one whole pair, a pair and a single
+    # tile, two pairs, and a pair whose second tile has one row
+    ((256,), 8, 2, 128, "normal"),
+    ((384, 512), 4, 1, 100, "mixed"),
+    ((257, 385), 8, 2, 128, "normal"),
 ]
 
 

@@ -38,6 +38,7 @@ def test_host_code_is_clean_under_asan_and_ubsan():
         env.pop("SINK_ATTN_DKDV_HEADS", None)
         env.pop("SINK_ATTN_PACK_HEADS", None)
         env.pop("SINK_ATTN_VALIDATE", None)
+        env["SINK_ATTN_TRACE"] = "1"  # the trace path formats every launch's line
         r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=300)
         out = r.stdout + r.stderr
         assert r.returncode == 0, out[-4000:]
