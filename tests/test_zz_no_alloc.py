@@ -67,3 +67,52 @@ def test_noalloc_backward_matches_workspace_backward_twice():
         assert rel_l2(f64(got[3]), f64(ref[3])) <= TOL_DS
         for t in got:
             assert torch.isfinite(t).all()
+
+
+def _noalloc_into(d, w, window, outs, stream):
+    import attention_sink_fwd_amd as sa
+
+    lib = _lib.load()
+    q, k = d["q"], d["k"]
+    dq, dk, dv, ds = outs
+    p = sa.make_params(q, k, d["cu_seqlens"], w.max_seqlen, w.softmax_scale, window)
+    _lib.check(lib.sink_attn_bwd_noalloc(ctypes.byref(p), q.data_ptr(), k.data_ptr(), d["v"].data_ptr(),
+                                         d["sinks"].data_ptr(), d["o"].data_ptr(), d["lse"].data_ptr(),
+                                         d["dout"].data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                         ds.data_ptr(), stream.cuda_stream))
+
+
+@pytest.mark.parametrize("window", [0, 96])
+def test_noalloc_backward_replays_in_a_hip_graph(window):
+    """Captured in a HIP graph -- the use the entry point is for -- and
+    replayed three times, with eager work and a synchronisation between the
+    replays: every replay gives the eager call's bits (window 96 runs the
+    fused short-window kernel)."""
+    import attention_sink_fwd_amd as sa
+
+    w = custom_workload((300, 5, 190), 8, 2, 64, window, "bf16")
+    say("case no-alloc backward in a graph, window", window)
+    d = {n: t.to("cuda:0") for n, t in make_inputs(w, seed=23 + window).items()}
+    d["o"], d["lse"] = sa.sink_attn_fwd(d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens"], w.max_seqlen,
+                                        w.softmax_scale, window)
+    ref = [torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["k"]), torch.empty_like(d["sinks"])]
+    _noalloc_into(d, w, window, ref, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(t) for t in ref]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _noalloc_into(d, w, window, outs, side)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="thread_local"):
+        _noalloc_into(d, w, window, outs, torch.cuda.current_stream())
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv", "dsinks"), outs, ref):
+            assert torch.equal(a, b), (rep, name)
