@@ -135,8 +135,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int h2 = lane >> 5, l32 = lane & 31;
-  const int HG = a.dkdv_heads, grp = a.num_q_heads / a.num_kv_heads;
-  const TileUnit unit = xcd_unit(a.num_q_heads / HG, a.num_seqs);
+  const int HG = a.dkdv_heads, grp = udiv_uniform(a.num_q_heads, a.num_kv_heads);
+  const TileUnit unit = xcd_unit(udiv_uniform(a.num_q_heads, HG));
   const int seq = unit.seq, hq0 = unit.head * HG;
   const int kt = unit.rank;  // key tile 0 sees the most query tiles: runs first
   const int bos = a.cu_seqlens[seq];
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
   // The direct path is only built for head_dim == kD.
   const int hd = kDirect ? kD : a.head_dim, T = a.total_tokens, window = kWindow ? a.window : 0;
-  const int g = hq0 / grp;
+  const int g = udiv_uniform(hq0, grp);
   const int qs = a.num_q_heads * hd, ks = a.num_kv_heads * hd;  // row strides (< 2^31 elements)
   // Base pointers of this sequence and the first head: row i of head hq0 + j
   // is base + i * stride + j * hd (Q, dO) or base + j * T + i (statistics).
@@ -449,10 +449,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int hd = kDirect ? kD : a.head_dim, T = a.total_tokens, window = kWindow ? a.window : 0;
   // Column n = 32 w + l32 is query row q0 + n / hp of head hb * hp + n % hp
   // (hp query heads of one KV group share the workgroup's K/V tiles).
-  const int hp = a.heads_per_tile, rows = kQT / hp;
-  const TileUnit unit = xcd_unit(a.num_q_heads / hp, a.num_seqs);
+  // hp divides 32: a power of two, so rows and columns split by shifts.
+  const int hp = a.heads_per_tile, hps = __builtin_ctz((unsigned)hp), rows = kQT >> hps;
+  const TileUnit unit = xcd_unit(udiv_uniform(a.num_q_heads, hp));
   const int seq = unit.seq, hb = unit.head;
-  const int ntiles = (int)gridDim.x / (a.num_q_heads / hp * a.num_seqs);
+  const int ntiles = a.dq_tiles;
   const int qt = ntiles - 1 - unit.rank;  // heaviest (last) query tiles first
   // dS partial of head h for this tile: dsink_part[(h * num_seqs + seq) * ntiles + qt]
   float* __restrict__ dsink_slots = a.dsink_part + ((long)hb * hp * a.num_seqs + seq) * ntiles + qt;
@@ -465,10 +466,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     return;
   }
 
-  const int g = hb * hp / (a.num_q_heads / a.num_kv_heads);
+  const int g = udiv_uniform(hb * hp, udiv_uniform(a.num_q_heads, a.num_kv_heads));
   const int qs = a.num_q_heads * hd, ks = a.num_kv_heads * hd;
   const int col = 32 * w + l32;
-  const int hq = hb * hp + col % hp;  // this lane's query head
+  const int hq = hb * hp + (col & (hp - 1));  // this lane's query head
   const TIn* __restrict__ Qh = (const TIn*)a.q + (long)bos * qs + hq * hd;
   const TIn* __restrict__ dOh = (const TIn*)a.dout + (long)bos * qs + hq * hd;
   const TIn* __restrict__ Oh = (const TIn*)a.o + (long)bos * qs + hq * hd;
@@ -524,7 +525,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   // This lane's query row (column n of the transposed products) and its Q and
   // dO fragments (B operands); the lane holds half of the row's d values.
-  const int qrow = q0 + col / hp;
+  const int qrow = q0 + (col >> hps);
   const int qcl = min(qrow, L - 1);
   const float lse = a.lse[(long)hq * T + bos + qcl];
   const float sink = a.sinks[hq];
@@ -562,8 +563,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       const int c = 8 * i + (lane >> 3), j = lane & 7;
       const bf16x8 x = *(const bf16x8*)(ep + c * kD + ((j ^ (c & 7)) << 3));
       const int n = 32 * w + c;
-      const int row = q0 + n / hp;
-      if (row < L) *(bf16x8*)((bf16*)a.qscaled + (long)(bos + row) * qs + (hb * hp + n % hp) * kD + 8 * j) = x;
+      const int row = q0 + (n >> hps);
+      if (row < L) *(bf16x8*)((bf16*)a.qscaled + (long)(bos + row) * qs + (hb * hp + (n & (hp - 1))) * kD + 8 * j) = x;
     }
     issue_fence();
   }
@@ -580,7 +581,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int krow_base = row_perm(l32);
   // First and last rows of this wavefront; one whose rows all lie past the
   // sequence only takes part in the loads.
-  const int wq_lo = q0 + 32 * w / hp, wq_hi = q0 + (32 * w + 31) / hp;
+  const int wq_lo = q0 + ((32 * w) >> hps), wq_hi = q0 + ((32 * w + 31) >> hps);
   const bool live = wq_lo < L;
 
   // One key tile: consume `st`, prefetch tile t + 2 into `nx` (the stage
@@ -714,8 +715,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       const int c = 8 * i + (lane >> 3), j = lane & 7;  // column of this wavefront, 16-byte chunk
       const bf16x8 x = *(const bf16x8*)(ep + c * kD + ((j ^ (c & 7)) << 3));
       const int n = 32 * w + c;
-      const int row = q0 + n / hp;
-      if (row < L) *(bf16x8*)((bf16*)a.dq + (long)(bos + row) * qs + (hb * hp + n % hp) * kD + 8 * j) = x;
+      const int row = q0 + (n >> hps);
+      if (row < L) *(bf16x8*)((bf16*)a.dq + (long)(bos + row) * qs + (hb * hp + (n & (hp - 1))) * kD + 8 * j) = x;
     }
   } else if (qrow < L) {
     TIn* dq = (TIn*)a.dq + (long)(bos + qrow) * qs + hq * hd;
@@ -786,8 +787,8 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
-  const int G = a.num_q_heads / a.num_kv_heads;
-  const TileUnit unit = xcd_unit(a.num_kv_heads, a.num_seqs);
+  const int G = udiv_uniform(a.num_q_heads, a.num_kv_heads);
+  const TileUnit unit = xcd_unit(a.num_kv_heads);
   const int seq = unit.seq, g = unit.head, pr = unit.rank;  // query tiles 2*pr and 2*pr + 1
   const int T = a.total_tokens, window = a.window;
   // dS partial of query head g*G + j for query tile 2*pr + ph:
@@ -1302,8 +1303,11 @@ int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, 
   return hg;
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t stream,
+hipError_t launch_bwd(const BwdArgs& args, int dtype, int max_seqlen, int num_seqs, hipStream_t stream,
                       const hipEvent_t* events) {
+  BwdArgs a = args;
+  const int qrows = kQT / a.heads_per_tile;
+  a.dq_tiles = (max_seqlen + qrows - 1) / qrows;
   const int T = a.total_tokens, Hq = a.num_q_heads;
   const int parts = T > 0 ? bwd_dsink_parts(max_seqlen, num_seqs, a.fused ? 1 : a.heads_per_tile) : 0;
   const long chunks = (long)T * 2 * a.num_kv_heads * a.head_dim / 8;
@@ -1320,7 +1324,7 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs,
     // its end), then the shared key tiles' planes and dS.
     const int npairs = (max_seqlen + 2 * kFQ - 1) / (2 * kFQ);
     if (T > 0) {
-      const dim3 grid(npairs * a.num_kv_heads * num_seqs);
+      const dim3 grid(npairs * a.num_kv_heads, num_seqs);
       hipLaunchKernelGGL(bwd_window_kernel, grid, dim3(512), 0, stream, a);
       if ((e = after_launch("bwd_window_kernel", grid, dim3(512), split, stream)) != hipSuccess) return e;
     }
@@ -1334,9 +1338,8 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype, int max_seqlen, int num_seqs,
       return e;
     return mark(3);
   } else {
-    const dim3 grid_kv((max_seqlen + kBN - 1) / kBN * (Hq / a.dkdv_heads) * num_seqs);
-    const int qrows = kQT / a.heads_per_tile;
-    const dim3 grid_q((max_seqlen + qrows - 1) / qrows * (Hq / a.heads_per_tile) * num_seqs);
+    const dim3 grid_kv((max_seqlen + kBN - 1) / kBN * (Hq / a.dkdv_heads), num_seqs);
+    const dim3 grid_q(a.dq_tiles * (Hq / a.heads_per_tile), num_seqs);
     const bool direct = dtype == 0 && a.head_dim == kD;
     // The window-free instances when no sequence is cut by the window.
     const bool windowed = a.window > 0 && a.window < max_seqlen;

@@ -225,33 +225,42 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Work order of the tiled kernels (1-D launch of n = tiles * heads * seqs
-// workgroups).  The dispatcher places workgroup b on XCD b % 8, and each XCD
-// has its own L2.  When the heads split evenly over the 8 XCDs, XCD x owns
-// heads [x * H/8, (x+1) * H/8) (tiles that share K, V or Q, dO hit one L2)
-// and its workgroups b = x + 8 i take, in order of i: sequence after
-// sequence; within a sequence, tile rank after tile rank (rank 0 is each
-// kernel's heaviest tile); within a rank, head after head.  So every head's
-// heavy tiles start first and the light ones fill the end: ordering by head
-// first (all ranks of one head, then the next) left the last heads' heavy
-// tiles for the end of the launch, a tail that cost the dK/dV kernel 12 % at
-// one 4096-token sequence.  Otherwise (heads not a multiple of 8) the same
-// order runs over the whole grid, dealt round-robin over the XCDs.
+// n / d for wavefront-uniform 0 <= n, 1 <= d: a shift when d is a power of
+// two (the usual head and group counts), else an integer division.
+__device__ __forceinline__ int udiv_uniform(int n, int d) {
+  if ((d & (d - 1)) == 0) return n >> __builtin_ctz((unsigned)d);
+  return (int)((unsigned)n / (unsigned)d);
+}
+
+// Work order of the tiled kernels: a 2-D launch, x = tiles * heads workgroups
+// of one sequence, y = the sequence, dispatched x first.  The dispatcher
+// places consecutive workgroups on consecutive XCDs (workgroup x of a row on
+// XCD x % 8 when the row length is a multiple of 8), and each XCD has its own
+// L2.  When the heads split evenly over the 8 XCDs, XCD c owns heads
+// [c * H/8, (c+1) * H/8) (tiles that share K, V or Q, dO hit one L2) and its
+// workgroups x = c + 8 i take, in order of i: tile rank after tile rank (rank
+// 0 is each kernel's heaviest tile); within a rank, head after head.  So
+// every head's heavy tiles start first and the light ones fill the end:
+// ordering by head first (all ranks of one head, then the next) left the
+// last heads' heavy tiles for the end of the launch, a tail that cost the
+// dK/dV kernel 12 % at one 4096-token sequence.  Otherwise (heads not a
+// multiple of 8) the same order runs over the whole row, dealt round-robin
+// over the XCDs.  The sequence comes from the grid, not from a division.
 struct TileUnit {
   int head, seq, rank;
 };
-__device__ __forceinline__ TileUnit xcd_unit(int num_heads, int num_seqs) {
-  const int b = blockIdx.x, n = gridDim.x;
-  const int tiles = n / (num_heads * num_seqs);
-  const bool split = (num_heads & 7) == 0;
-  const int hx = split ? num_heads >> 3 : num_heads;  // heads of this XCD's share
-  const int i = split ? b >> 3 : b;                   // dispatch index within the share
-  const int per_seq = tiles * hx;
+__device__ __forceinline__ TileUnit xcd_unit(int num_heads) {
+  const int b = blockIdx.x;
   TileUnit t;
-  t.seq = i / per_seq;
-  const int r = i - t.seq * per_seq;
-  t.rank = r / hx;
-  t.head = (split ? (b & 7) * hx : 0) + r % hx;
+  t.seq = blockIdx.y;
+  if ((num_heads & 7) == 0) {
+    const int hx = num_heads >> 3, i = b >> 3;  // heads of this XCD's share, index within it
+    t.rank = udiv_uniform(i, hx);
+    t.head = (b & 7) * hx + (i - t.rank * hx);
+  } else {
+    t.rank = udiv_uniform(b, num_heads);
+    t.head = b - t.rank * num_heads;
+  }
   return t;
 }
 

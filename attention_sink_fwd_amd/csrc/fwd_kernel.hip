@@ -72,21 +72,21 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
   // Column n = 32 w + l32 of the workgroup's score tiles is query row
   // q0 + n / hp of head hb * hp + n % hp: hp query heads of one KV group
   // share the workgroup's K/V tiles (hp = 1: 128 rows of one head).
-  const int hp = a.heads_per_tile, rows = kBM / hp;
-  const TileUnit unit = xcd_unit(a.num_q_heads / hp, a.num_seqs);
+  // hp divides 32: a power of two, so columns split into (row, head) by shifts.
+  const int hp = a.heads_per_tile, hps = a.hp_shift, rows = kBM >> hps;
+  const TileUnit unit = xcd_unit(a.num_q_heads >> hps);
   const int seq = unit.seq, hb = unit.head;
-  const int ntiles = (int)gridDim.x / (a.num_q_heads / hp * a.num_seqs);
-  const int qt = ntiles - 1 - unit.rank;  // heaviest (last) query tiles first
+  const int qt = a.tiles - 1 - unit.rank;  // heaviest (last) query tiles first
   const int bos = a.cu_seqlens[seq];
   const int L = a.cu_seqlens[seq + 1] - bos;  // query rows of this sequence
   const int q0 = qt * rows;
   if (q0 >= L) return;
 
   const int hd = kDirect ? kD : a.head_dim;  // the direct path is only built for head_dim == kD
-  const int g = hb * hp / (a.num_q_heads / a.num_kv_heads);
+  const int g = udiv_uniform(hb, udiv_uniform(a.num_q_heads, a.num_kv_heads) >> hps);  // hp divides the group
   const int qs = a.num_q_heads * hd, ks = a.num_kv_heads * hd;  // row strides (< 2^31 elements)
   const int col = 32 * w + l32;
-  const int hq = hb * hp + col % hp;  // this lane's query head
+  const int hq = hb * hp + (col & (hp - 1));  // this lane's query head
 
   // Keys of this sequence and the position of query row 0.  A paged
   // sequence's length is clamped to what its block-table row can address.
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
   // This lane's query row (column n of S^T), its position, and its Q
   // fragments (B operand), pre-scaled by scale * log2(e) so that the score
   // products come out in the log2 domain (one bf16 rounding of scale * q).
-  const int qrow = q0 + col / hp;
+  const int qrow = q0 + (col >> hps);
   const int qpos = qoff + qrow;
   const TIn* __restrict__ Qh = (const TIn*)a.q + (long)bos * qs + hq * hd;
   bf16x8 qf[4];
@@ -213,8 +213,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
 
   // Positions of this wavefront's first and last rows; a wavefront whose
   // rows all lie past the sequence only takes part in the loads.
-  const int wq_lo = qoff + q0 + 32 * w / hp, wq_hi = qoff + q0 + (32 * w + 31) / hp;
-  const bool live = q0 + 32 * w / hp < L;
+  const int wq_lo = qoff + q0 + ((32 * w) >> hps), wq_hi = qoff + q0 + ((32 * w + 31) >> hps);
+  const bool live = q0 + ((32 * w) >> hps) < L;
   const int krow_base = row_perm(l32);
 
   // One key tile: consume `st`, prefetch the next tile into `nx` (the stage
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
   }
 
   const float lt = l + __shfl_xor(l, 32);
-  const float inv = 1.0f / lt;
+  const float inv = __builtin_amdgcn_rcpf(lt);  // (1 ulp; 1 / 0 = inf as before)
   if constexpr (kDirect) {
     // O goes out through LDS: a lane holds 4-value pieces of d for its own
     // column, so direct stores would write 8 bytes per lane scattered over 32
@@ -430,8 +430,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
       const int c = 8 * i + (lane >> 3), j = lane & 7;  // column of this wavefront, 16-byte chunk
       const bf16x8 x = *(const bf16x8*)(ep + c * kD + ((j ^ (c & 7)) << 3));
       const int n = 32 * w + c;
-      const int row = q0 + n / hp;
-      if (row < L) *(bf16x8*)((bf16*)a.o + (long)(bos + row) * qs + (hb * hp + n % hp) * kD + 8 * j) = x;
+      const int row = q0 + (n >> hps);
+      if (row < L) *(bf16x8*)((bf16*)a.o + (long)(bos + row) * qs + (hb * hp + (n & (hp - 1))) * kD + 8 * j) = x;
     }
     if (qrow < L && h2 == 0) a.lse[(long)hq * a.total_tokens + bos + qrow] = (m + __log2f(lt)) * kLn2;
   } else if (qrow < L) {
@@ -455,22 +455,25 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
 template <int kWaves>
 hipError_t launch_fwd_waves(const FwdArgs& a, bool direct, int dtype, int max_seqlen, int num_seqs,
                             hipStream_t stream) {
+  FwdArgs b = a;
   const int hp = a.heads_per_tile, rows = 32 * kWaves / hp;
-  const dim3 grid((max_seqlen + rows - 1) / rows * (a.num_q_heads / hp) * num_seqs), block(64 * kWaves);
+  b.hp_shift = __builtin_ctz((unsigned)hp);
+  b.tiles = (max_seqlen + rows - 1) / rows;
+  const dim3 grid(b.tiles * (a.num_q_heads / hp), num_seqs), block(64 * kWaves);
   if (a.block_table) {
     if (direct)
-      hipLaunchKernelGGL((fwd_kernel<bf16, true, true, kWaves>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<bf16, true, true, kWaves>), grid, block, 0, stream, b);
     else if (dtype == 0)
-      hipLaunchKernelGGL((fwd_kernel<bf16, false, true, kWaves>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<bf16, false, true, kWaves>), grid, block, 0, stream, b);
     else
-      hipLaunchKernelGGL((fwd_kernel<float, false, true, kWaves>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<float, false, true, kWaves>), grid, block, 0, stream, b);
   } else {
     if (direct)
-      hipLaunchKernelGGL((fwd_kernel<bf16, true, false, kWaves>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<bf16, true, false, kWaves>), grid, block, 0, stream, b);
     else if (dtype == 0)
-      hipLaunchKernelGGL((fwd_kernel<bf16, false, false, kWaves>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<bf16, false, false, kWaves>), grid, block, 0, stream, b);
     else
-      hipLaunchKernelGGL((fwd_kernel<float, false, false, kWaves>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<float, false, false, kWaves>), grid, block, 0, stream, b);
   }
   char split[64];
   std::snprintf(split, sizeof(split), "paged=%d pack_heads=%d waves=%d", a.block_table ? 1 : 0, hp, kWaves);

@@ -18,6 +18,8 @@ struct FwdArgs {
   const int32_t* cu_seqlens;
   int num_q_heads, num_kv_heads, head_dim, total_tokens, window, num_seqs;
   int heads_per_tile;  // query heads of one KV head packed in a workgroup (divides Hq/Hkv and 32)
+  int hp_shift;        // log2(heads_per_tile) (set by launch_fwd)
+  int tiles;           // query tiles per (sequence, head block) in the grid (set by launch_fwd)
   float scale_log2;    // softmax_scale * log2(e)
   // Paged key/value source (block_table == nullptr: k, v are packed like q).
   // k, v then point at the caches [num_pages, page_size, Hkv, d].
@@ -51,6 +53,7 @@ struct BwdArgs {
   int fused;           // 1: the fused short-window kernel replaces the dQ and dK/dV kernels
   int dsink_tiles;     // fused kernel: 128-row tiles per (head, sequence) in the dS partial layout
   int heads_per_tile;  // query heads of one KV head packed in a dQ workgroup (divides Hq/Hkv and 32)
+  int dq_tiles;        // query tiles per (sequence, head block) of the dQ grid (set by launch_bwd)
   float scale;
   float scale_log2;
 };
