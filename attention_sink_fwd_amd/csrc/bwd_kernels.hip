@@ -741,47 +741,59 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 // which lie in the tile's own 128 keys and the 128 before them.  One workgroup
 // takes one such query tile and every query head of one KV group, with all
 // 256 keys resident: K in LDS and in registers, V in registers.  Per 64-row
-// step (one head) it forms S, dP, P and dS once, as the dK/dV kernel does
-// (eight wavefronts, 32 keys each), accumulates dK and dV in registers over
-// all the group's heads, and passes dS^T through LDS so that four wavefronts
-// form the step's dQ = scale dS K completely (every key that reaches these
-// rows is in the workgroup).  The other four compute the next step's row
-// statistics meanwhile: D = dO . O, -LSE log2(e), the sink term, and the
-// scaled queries bf16(q scale log2 e) (in place, the same rounding as the
-// forward kernel's).  So Q, dO and O are each read once, dQ written once, and
-// no scaled copy of Q goes through memory.  dK and dV of a key tile get
-// contributions from two workgroups (the tile's own query rows and the next
-// tile's); each writes its float sums to its own plane (0: own rows, 1: the
-// next tile's rows; the last tile of a sequence writes zeros to plane 1) and
-// the post kernel adds the two planes in that order.
-constexpr int kFQ = 128;         // query rows per fused workgroup
-constexpr int kFK = 2 * kFQ;     // keys it sees
-constexpr int kFMaxGroup = 64;   // query heads per KV head the fused kernel takes
-constexpr int kFPrefetchOps = 4; // VMEM instructions per wavefront and step prefetch (q, dO, O, LSE)
+// step (one head) it forms S, dP, P and dS once, as the dK/dV kernel does,
+// accumulates dK and dV in registers over all the group's heads, and passes
+// dS^T through LDS so that the step's dQ = scale dS K is formed completely
+// inside the workgroup (every key that reaches these rows is in it).  So Q,
+// dO and O are each read once, dQ written once, and no scaled copy of Q goes
+// through memory.
+//
+// The twelve wavefronts have two roles, three per SIMD:
+// * eight key wavefronts (32 keys each) do only the step's products: S, dP,
+//   P, dS (dS^T to LDS), dV and dK;
+// * four producer wavefronts issue every load of the query side (Q and dO
+//   into the LDS ring, LSE, and O into their own registers), form the next
+//   step's row statistics (D = dO . O, -LSE log2(e), the sink term, and the
+//   scaled queries bf16(q scale log2 e) in place, the same rounding as the
+//   forward kernel's), and form dQ of the previous step from its dS^T
+//   (double-buffered) and K in LDS.
+// One barrier per step hands everything over: at barrier cs the step's
+// statistics are ready and the previous step's dS^T is complete; the dQ of
+// step cs - 1 and the statistics of step cs + 1 then run beside the products
+// of step cs.  dK and dV of a key tile get contributions from two workgroups
+// (the tile's own query rows and the next tile's); each writes its float sums
+// to its own plane (0: own rows, 1: the next tile's rows; the last tile of a
+// sequence writes zeros to plane 1) and the post kernel adds the two planes
+// in that order.
+constexpr int kFQ = 128;          // query rows per fused workgroup
+constexpr int kFK = 2 * kFQ;      // keys it sees
+constexpr int kFMaxGroup = 64;    // query heads per KV head the fused kernel takes
+constexpr int kFKeyWaves = 8;     // key wavefronts (32 keys each)
+constexpr int kFThreads = 64 * (kFKeyWaves + 4);
 
 struct __attribute__((aligned(16))) FStage {
   bf16 q[kBM * kD];     // Q tile, swizzled [q][d]; scaled in place before use
   bf16 dout[kBM * kD];  // dO tile, swizzled [q][d]
-  bf16 o[kBM * kD];     // O tile, swizzled [q][d] (for D only)
   float lse[kBM];       // LSE of the tile rows (natural log)
   float nlse[kBM];      // -LSE log2(e)
   float ndelta[kBM];    // -D
-  float spare[kBM];     // landing area that keeps every wavefront's load count equal
 };
 // The workgroup's LDS in one object, so the layout (and every constant
 // offset between its parts) is fixed.
 struct __attribute__((aligned(16))) FLds {
-  FStage s0, s1, s2;    // ring of 64-row steps
-  bf16 ks[kFK * kD];    // K of the 256 keys, swizzled [key][d]
-  bf16 ds[kFK * kBM];   // dS^T of the current step, swizzled [key][row]
-  float wsum[2][kFMaxGroup][4];  // per query tile of the pair, head, statistics wavefront
+  FStage s0, s1, s2;        // ring of 64-row steps
+  bf16 ks[kFK * kD];        // K of the 256 keys, swizzled [key][d]
+  bf16 ds[2][kFK * kBM];    // dS^T of steps of even / odd index, swizzled [key][row]
+  bf16 epi[4][32 * 32];     // each producer's dQ block on its way out
+  float wsum[2][kFMaxGroup][4];  // per query tile of the pair, head, producer
 };
-constexpr uint32_t kOffDout = offsetof(FStage, dout), kOffO = offsetof(FStage, o);
+static_assert(sizeof(FLds) <= 160 * 1024, "LDS of one compute unit");
+constexpr uint32_t kOffDout = offsetof(FStage, dout);
 constexpr uint32_t kOffLse = offsetof(FStage, lse), kOffNlse = offsetof(FStage, nlse);
 constexpr uint32_t kOffNdelta = offsetof(FStage, ndelta);
+constexpr uint32_t kDsBytes = kFK * kBM * sizeof(bf16);
 
-
-__global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kFThreads) void bwd_window_kernel(BwdArgs a) {
   __shared__ FLds lds;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -800,20 +812,15 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
   const int L = a.cu_seqlens[seq + 1] - bos;
   const int q0 = pr * 2 * kFQ;
   if (q0 >= L) {
-    for (int j = tid; j < G; j += 512) {
+    for (int j = tid; j < G; j += kFThreads) {
       if (2 * pr < ntiles) dsink_slots[j * slot_stride] = 0.0f;
       if (2 * pr + 1 < ntiles) dsink_slots[j * slot_stride + 1] = 0.0f;
     }
     return;
   }
   const int qs = a.num_q_heads * kD, ks = a.num_kv_heads * kD;  // row strides (< 2^31 elements)
-  const bf16* __restrict__ Qg = (const bf16*)a.q + (long)bos * qs + g * G * kD;  // head g*G + j at + j*kD
-  const bf16* __restrict__ dOg = (const bf16*)a.dout + (long)bos * qs + g * G * kD;
-  const bf16* __restrict__ Og = (const bf16*)a.o + (long)bos * qs + g * G * kD;
-  const float* __restrict__ lse_g = a.lse + (long)g * G * T + bos;  // head g*G + j at + j*T
   const bf16* __restrict__ Kg = (const bf16*)a.k + (long)bos * ks + g * kD;
-  const bf16* __restrict__ Vg = (const bf16*)a.v + (long)bos * ks + g * kD;
-  const int kbase = q0 - kFQ;                     // first key of the span (< 0 for the first tile)
+  const int kbase = q0 - kFQ;  // first key of the span (< 0 for the first tile)
   // Phase ph takes query tile 2*pr + ph in 64-row steps, head after head.
   const int nph = L - q0 > kFQ ? 2 : 1;
   const int nrb0 = L - q0 > kBM ? 2 : 1;
@@ -831,41 +838,8 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
       rb = t - j * nrb1;
     }
   };
-
-  // Prefetch cursor (step pf); it stops at the last step, so the ring's
-  // look-ahead past the end re-loads that step.
-  int pf = 0;
-  // This lane stages 16 bytes of row r_own of each 64-row tile into its
-  // swizzled slot (wavefront w: rows 8w .. 8w + 7).
-  const int r_own = 8 * w + (lane >> 3);
-  const uint32_t voff = (uint32_t)(r_own * qs + 8 * ((lane & 7) ^ swz_f(r_own))) * (uint32_t)sizeof(bf16);
-  auto prefetch = [&](FStage& st) {
-    int pph, pj, prb;
-    step_of(pf, pph, pj, prb);
-    const int qb = q0 + kFQ * pph + kBM * prb;
-    const int rem = L - qb;  // >= 1: rows from the tile's first on (rows past the end repeat the last)
-    uint32_t off = voff, soff = (uint32_t)lane * (uint32_t)sizeof(float);
-    if (rem < kBM) {
-      off = voff - (uint32_t)(max(r_own - (rem - 1), 0) * qs) * (uint32_t)sizeof(bf16);
-      soff = (uint32_t)min(lane, rem - 1) * (uint32_t)sizeof(float);
-    }
-    const long ro = (long)qb * qs + pj * kD;
-    lds_dma16_s(off, Qg + ro, st.q + 512 * w);
-    lds_dma16_s(off, dOg + ro, st.dout + 512 * w);
-    lds_dma16_s(off, Og + ro, st.o + 512 * w);
-    lds_dma4_s(soff, lse_g + (long)pj * T + qb, w == 0 ? st.lse : st.spare);
-    if (pf + 1 < nsteps) ++pf;
-  };
-  prefetch(lds.s0);
-  issue_fence();
-  prefetch(lds.s1);
-  issue_fence();
-  // K of the 256 keys into LDS (keys outside the sequence repeat its first or
-  // last key; they are masked): rows 0..127 hold wavefronts 0..3's keys (the
-  // tile before 2*pr in phase 0, the tile after it in phase 1), rows
-  // 128..255 the keys of tile 2*pr (wavefronts 4..7, both phases).  Each
-  // wavefront's own K and V fragments are the B operands of S = Q K^T and
-  // dP = dO V^T (lane = key column).
+  // 8 * nblk keys (rows 8 * blk0 .. of ks) from key0 on into LDS (keys outside the
+  // sequence repeat its first or last key; they are masked).
   auto stage_keys = [&](int blk0, int nblk, int key0) {
     for (int i = 0; i < nblk; ++i) {
       const int blk = blk0 + i;
@@ -874,72 +848,301 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
       lds_dma16(Kg + (long)key * ks + 8 * ((lane & 7) ^ swz_f(r)), lds.ks + 512 * blk);
     }
   };
-  stage_keys(4 * w, 4, kbase + 32 * w);
-  int wk_lo = kbase + 32 * w;
-  int key_n = wk_lo + l32;
-  bf16x8 kf[4], vf[4];
-  auto load_kv = [&]() {
-    const int krow = min(max(key_n, 0), L - 1);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int d0 = 16 * c + 8 * h2;
-      kf[c] = load8(Kg + (long)krow * ks + d0);
-      vf[c] = load8(Vg + (long)krow * ks + d0);
-    }
-  };
-  load_kv();
 
-  // Per-lane LDS address patterns (bytes).  Stage-relative ones get the
-  // stage's offset added as a constant.
-  const int qrow_base = row_perm(l32);
-  uint32_t p_seed = 32u * h2;  // statistics of rows 8*h2 .. (+ 128*mb, + 64 for the second 8)
-  uint32_t p_row[4];           // row fragment of operand row qrow_base (+ 4096*mb), chunk 2c + h2
+  if (w < kFKeyWaves) {
+    // ---- key wavefronts: keys wk_lo .. wk_lo + 31 (rows 32 w .. of ks).
+    // Rows 0..127 of ks hold wavefronts 0..3's keys (the tile before 2*pr in
+    // phase 0, the tile after it in phase 1), rows 128..255 the keys of tile
+    // 2*pr (wavefronts 4..7, both phases); each wavefront stages its own 32
+    // rows.  A wavefront's K (read from its rows of ks) and V (registers)
+    // fragments are the B operands of S = Q K^T and dP = dO V^T (lane = key).
+    const bf16* __restrict__ Vg = (const bf16*)a.v + (long)bos * ks + g * kD;
+    int wk_lo = kbase + 32 * w;
+    int key_n = wk_lo + l32;
+    bf16x8 vf[4];
+    auto load_kv = [&]() {
+      stage_keys(4 * w, 4, wk_lo);
+      const int krow = min(max(key_n, 0), L - 1);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) p_row[c] = swz_b(qrow_base, 16 * c + 8 * h2);
-  uint32_t p_tr[2][2];  // transposing reads for d block db (+ 2048 per 16 query rows)
+      for (int c = 0; c < 4; ++c) vf[c] = load8(Vg + (long)krow * ks + 16 * c + 8 * h2);
+    };
+    load_kv();
+    // Per-lane LDS byte addresses into the current step's stage (advanced by
+    // one stage per step; block offsets are added as constants): statistics
+    // of rows 8*h2 .. (+ 128*mb, + 64 for the second 8), the row fragment of
+    // operand row qrow_base (+ 4096*mb), chunk 2c + h2, and the transposing
+    // reads of d block db (+ 2048 per 16 query rows).  The two loops below run
+    // one step per iteration (no unrolling over the ring), so that the key
+    // swap between them sits outside both.
+    const uint32_t s0 = lds_addr(&lds.s0);
+    const int qrow_base = row_perm(l32);
+    uint32_t p_seed = s0 + 32u * h2;
+    uint32_t p_row[4];
 #pragma unroll
-  for (int db = 0; db < 2; ++db) tr_pattern(32 * db, lane, p_tr[db][0], p_tr[db][1]);
-  const int kl = 32 * w + l32;  // this lane's key row in ks and ds
-  uint32_t p_dsw[2][2];         // dS^T chunk of rows 32*mb + 16*hb + 8*h2 of key kl
+    for (int c = 0; c < 4; ++c) p_row[c] = s0 + swz_b(qrow_base, 16 * c + 8 * h2);
+    uint32_t p_tr[2][2];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+    for (int db = 0; db < 2; ++db) {
+      tr_pattern(32 * db, lane, p_tr[db][0], p_tr[db][1]);
+      p_tr[db][0] += s0;
+      p_tr[db][1] += s0;
+    }
+    // dS^T row of this lane's key kl = 32 w + l32: rows 32*mb + 16*hb + 8*h2
+    // .. + 7 are 16-byte chunk 4*mb + 2*hb + h2, stored in slot chunk ^ f(kl)
+    // (+ kDsBytes for odd steps).  Its K row in ks has the same swizzle: d
+    // 16*c + 8*h2 .. + 7 is chunk 2*c + h2.  Both are formed per use from two
+    // registers.
+    const int kl = 32 * w + l32;
+    uint32_t p_dsrow = lds_addr(lds.ds[0]) + (uint32_t)kl * 128u;
+    uint32_t p_dsx = (uint32_t)(swz_f(kl) ^ h2);
+    const uint32_t ks_from_ds = lds_addr(lds.ks) - lds_addr(lds.ds[0]);
+    auto dsw_addr = [&](int mb, int hb) { return p_dsrow + ((p_dsx ^ (uint32_t)(4 * mb + 2 * hb)) << 4); };
+    auto kf_of = [&](int c) { return lds_ld<bf16x8>(p_dsrow + ks_from_ds + ((p_dsx ^ (uint32_t)(2 * c)) << 4)); };
+
+    f32x16 dk[2], dv[2];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) p_dsw[mb][hb] = lds_addr(lds.ds) + swz_b(kl, 32 * mb + 16 * hb + 8 * h2);
-  // dQ wavefronts (w < 4): d block db, row block nb of the step.
-  const int db_q = w & 1, nb_q = (w >> 1) & 1;
-  uint32_t p_ks[2], p_dsr[2];
-  tr_pattern(32 * db_q, lane, p_ks[0], p_ks[1]);
-  tr_pattern(32 * nb_q, lane, p_dsr[0], p_dsr[1]);
+    for (int i = 0; i < 16; ++i) { dk[0][i] = dk[1][i] = dv[0][i] = dv[1][i] = 0.0f; }
+    wait_vmem_all();  // K rows and V fragments resident (the K rows are read only by this wavefront until
+                      // the first barrier)
+
+    // dK, dV of this wavefront's keys (register r: key wk_lo + 8*(r/4) +
+    // 4*h2 + r%4): mode 0 or 1 into that float plane, 2 directly in the output
+    // type (a key tile whose contributions are all in this workgroup).
+    const long plane = (long)T * ks;
+    auto store_dkdv = [&](int mode) {
+      if (wk_lo < 0) return;
+      float* dk_p = a.dk_part + (mode == 1 ? plane : 0) + (long)bos * ks + g * kD;
+      float* dv_p = a.dv_part + (mode == 1 ? plane : 0) + (long)bos * ks + g * kD;
+      bf16* dk_o = (bf16*)a.dk + (long)bos * ks + g * kD;
+      bf16* dv_o = (bf16*)a.dv + (long)bos * ks + g * kD;
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    p_ks[e] += lds_addr(lds.ks);
-    p_dsr[e] += lds_addr(lds.ds);
+      for (int db = 0; db < 2; ++db) {
+        const int d = 32 * db + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = wk_lo + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          if (key < L) {
+            if (mode == 2) {
+              dk_o[(long)key * ks + d] = (bf16)(dk[db][r] * kLn2);
+              dv_o[(long)key * ks + d] = (bf16)dv[db][r];
+            } else {
+              dk_p[(long)key * ks + d] = dk[db][r] * kLn2;
+              dv_p[(long)key * ks + d] = dv[db][r];
+            }
+          }
+        }
+      }
+    };
+
+    // One step: the products of step cs from its stage (statistics and
+    // scaled queries in place), dS^T into ds[cs % 2].
+    int cs = 0, stg = 0;  // step, its stage
+    auto step = [&]() {
+      lds_opaque(p_seed);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) lds_opaque(p_row[c]);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        lds_opaque(p_tr[db][0]);
+        lds_opaque(p_tr[db][1]);
+      }
+      lds_opaque(p_dsrow);
+      lds_opaque(p_dsx);
+      lds_barrier();  // statistics of this stage ready; ds[cs % 2] free (its dQ is done)
+      const uint32_t dsb = (cs & 1) ? kDsBytes : 0u;
+      int ph, j, rb;
+      step_of(cs, ph, j, rb);
+      const int qb = q0 + kFQ * ph + kBM * rb;
+      const int wk_hi = wk_lo + 31;
+      const bool active = wk_lo >= 0 && wk_lo < L && wk_lo <= qb + kBM - 1 && qb - wk_hi < window;
+      if (active) {
+        // Rows of this step that some key of the wavefront does not see
+        // (causal side, window side or past the sequence): one masked form.
+        const bool masked = (wk_hi > qb) || (qb + kBM > L) || (qb + kBM - 1 - wk_lo >= window);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          // S and dP for rows 32*mb .. 32*mb+31 of the step, seeded with the row
+          // statistics (register r: row 32*mb + 16*(r/8) + 8*h2 + r%8).
+          f32x16 s, dp;
+          {
+            const uint32_t sa = p_seed + kOffNlse + 128u * mb, da = p_seed + kOffNdelta + 128u * mb;
+            const f32x8 s0v = lds_ld<f32x8>(sa), s1v = lds_ld<f32x8>(sa + 64);
+            const f32x8 d0v = lds_ld<f32x8>(da), d1v = lds_ld<f32x8>(da + 64);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              s[i] = s0v[i];
+              s[8 + i] = s1v[i];
+              dp[i] = d0v[i];
+              dp[8 + i] = d1v[i];
+            }
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            s = mfma32(lds_ld<bf16x8>(p_row[c] + 4096u * mb), kf_of(c), s);
+            dp = mfma32(lds_ld<bf16x8>(p_row[c] + kOffDout + 4096u * mb), vf[c], dp);
+          }
+          bf16x8 pf8[2], df[2];
+          auto softmax_grad = [&](auto test) {
+            // Visible iff lo <= 16*hb + i < hi, from this lane's key and first
+            // row.  (The lane id is read again here rather than kept live
+            // through the loop: the key wavefronts have no register to spare.)
+            int lo = 0, hi = 0;
+            if constexpr (decltype(test)::value) {
+              const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+              const int rbase = qb + 32 * mb + ((ln >> 2) & 8);
+              lo = wk_lo + (ln & 31) - rbase;
+              hi = min(L - rbase, lo + window);
+            }
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+              f32x8 pv, dv8;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                const int r = 8 * hb + i;
+                float p = fast_exp2(s[r]);
+                const int idx = 16 * hb + i;
+                if constexpr (decltype(test)::value) p = (idx >= lo && idx < hi) ? p : 0.0f;
+                pv[i] = p;
+                dv8[i] = p * dp[r];
+              }
+              pf8[hb] = __builtin_convertvector(pv, bf16x8);
+              df[hb] = __builtin_convertvector(dv8, bf16x8);
+            }
+          };
+          if (masked)
+            softmax_grad(std::true_type{});
+          else
+            softmax_grad(std::false_type{});
+          // dS^T row of this lane's key: 8 consecutive query rows per register half.
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) lds_st<bf16x8>(dsw_addr(mb, hb) + dsb, df[hb]);
+#pragma unroll
+          for (int db = 0; db < 2; ++db) {
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+              const uint32_t o = 2048u * (2 * mb + cc);
+              dv[db] = mfma32(pf8[cc], lds_tr8(p_tr[db][0] + kOffDout + o, p_tr[db][1] + kOffDout + o), dv[db]);
+              dk[db] = mfma32(df[cc], lds_tr8(p_tr[db][0] + o, p_tr[db][1] + o), dk[db]);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) lds_st<bf16x8>(dsw_addr(mb, hb) + dsb, zero8());
+      }
+      // Next step's stage.
+      const uint32_t adv = stg == kStages - 1 ? (uint32_t)(-(kStages - 1) * (int)sizeof(FStage)) : (uint32_t)sizeof(FStage);
+      stg = stg == kStages - 1 ? 0 : stg + 1;
+      p_seed += adv;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) p_row[c] += adv;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        p_tr[db][0] += adv;
+        p_tr[db][1] += adv;
+      }
+      ++cs;
+    };
+    while (cs < nsteps0) step();
+    if (nph == 2) {
+      // Wavefronts 0..3 hand in the tile before 2*pr and take the tile after
+      // it.  ks rows 0..127 are rewritten once the producers have formed the
+      // last phase-0 step's dQ from them.
+      if (w < 4) {
+        store_dkdv(1);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { dk[0][i] = dk[1][i] = dv[0][i] = dv[1][i] = 0.0f; }
+        wk_lo = q0 + kFQ + 32 * w;
+        key_n = wk_lo + l32;
+      }
+      lds_barrier();  // phase 0's last dS^T is complete
+      lds_barrier();  // the producers are done with the old rows
+      if (w < 4) load_kv();
+      wait_vmem_all();  // (the next step's barrier makes the new rows visible to the producers)
+      while (cs < nsteps) step();
+    }
+    lds_barrier();  // the last dS^T is complete (the producers' final dQ)
+    // Tile 2*pr (wavefronts 4..7) has all its contributions: the rows of tiles
+    // 2*pr and 2*pr + 1.  Wavefronts 0..3 hold the tile before it (one phase:
+    // plane 1, the next tile's rows) or the tile after it: plane 0 if a later
+    // workgroup adds that tile's next rows, else complete.
+    if (w >= 4)
+      store_dkdv(2);
+    else if (nph == 1)
+      store_dkdv(1);
+    else
+      store_dkdv(q0 + 2 * kFQ >= L ? 2 : 0);
+    return;
   }
-  // dQ epilogue: 32 rows of 64 bytes per wavefront in the consumed stage's Q
-  // tile, 16-byte chunks XOR-swizzled by row.
-  uint32_t p_epw = (uint32_t)(w & 3) * 2048u + (uint32_t)l32 * 64u + 8u * h2;  // + ((gi ^ sw) << 4)
-  const uint32_t ep_sw = (uint32_t)((l32 >> 2) & 3);
-  uint32_t p_epr[2];
+
+  // ---- producer wavefronts pw = 0..3 (one per SIMD).
+  const int pw = w - kFKeyWaves, pt = tid - 64 * kFKeyWaves;  // producer wavefront, thread 0..255
+  const bf16* __restrict__ Qg = (const bf16*)a.q + (long)bos * qs + g * G * kD;  // head g*G + j at + j*kD
+  const bf16* __restrict__ dOg = (const bf16*)a.dout + (long)bos * qs + g * G * kD;
+  const bf16* __restrict__ Og = (const bf16*)a.o + (long)bos * qs + g * G * kD;
+  const float* __restrict__ lse_g = a.lse + (long)g * G * T + bos;  // head g*G + j at + j*T
+  // Statistics: thread pt takes a quarter (16 values of d) of row srow, one
+  // of the 16 rows whose Q, dO and LSE its own wavefront loads (the
+  // producers do not wait for each other's loads).
+  const int srow = pt >> 2, sqd = pt & 3;
+  // Loads: this lane stages 16 bytes of rows r_own[i] of the Q and dO tiles
+  // into their swizzled slots (wavefront pw: rows 16 pw .. 16 pw + 15), and
+  // the 32 bytes of O that its statistics need into registers.  The O loads
+  // come last, after the LDS-direct loads (which the compiler does not
+  // count): then the wait the compiler puts before the statistics' use of O
+  // counts exactly the dQ stores issued since, the same as the explicit wait.
+  uint32_t voff[2];
+  int r_own[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int c = lane + 64 * i, row = c >> 2, jc = c & 3;
-    p_epr[i] = (uint32_t)(w & 3) * 2048u + (uint32_t)row * 64u + ((uint32_t)(jc ^ ((row >> 2) & 3)) << 4);
+    r_own[i] = 16 * pw + 8 * i + (lane >> 3);
+    voff[i] = (uint32_t)(r_own[i] * qs + 8 * ((lane & 7) ^ swz_f(r_own[i]))) * (uint32_t)sizeof(bf16);
   }
-  // Statistics threads (w >= 4): a quarter of row srow.
-  const int st_t = tid & 255, srow = st_t >> 2, sqd = st_t & 3;
+  bf16x8 o_reg[2];  // O of the next step's statistics: row srow, columns 16*sqd + 8*c
+  // Prefetch cursor (step pf); it stops at the last step, so the ring's
+  // look-ahead past the end re-loads that step.
+  int pf = 0;
+  auto prefetch = [&](FStage& st) {
+    int pph, pj, prb;
+    step_of(pf, pph, pj, prb);
+    const int qb = q0 + kFQ * pph + kBM * prb;
+    const int rem = L - qb;  // >= 1: rows from the tile's first on (rows past the end repeat the last)
+    uint32_t off[2] = {voff[0], voff[1]};
+    uint32_t soff = (uint32_t)(16 * pw + lane) * (uint32_t)sizeof(float);  // lanes 0..15: LSE of rows 16 pw ..
+    if (rem < kBM) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) off[i] = voff[i] - (uint32_t)(max(r_own[i] - (rem - 1), 0) * qs) * (uint32_t)sizeof(bf16);
+      soff = (uint32_t)min(16 * pw + lane, rem - 1) * (uint32_t)sizeof(float);
+    }
+    const long ro = (long)qb * qs + pj * kD;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lds_dma16_s(off[i], Qg + ro, st.q + 512 * (2 * pw + i));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lds_dma16_s(off[i], dOg + ro, st.dout + 512 * (2 * pw + i));
+    // Each producer loads the LSE of its own rows (the only rows whose
+    // statistics it forms, so its own wait covers them): 16 lanes.
+    if (lane < 16) lds_dma4_s(soff, lse_g + (long)pj * T + qb, st.lse + 16 * pw);
+    issue_fence();
+    const bf16* orow = Og + (long)(qb + min(srow, rem - 1)) * qs + pj * kD + 16 * sqd;
+    o_reg[0] = load8(orow);
+    o_reg[1] = load8(orow + 8);
+    if (pf + 1 < nsteps) ++pf;
+  };
+
+  // Row statistics of step sidx from its stage, and the scaled queries in place.
   uint32_t p_st[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) p_st[c] = swz_b(srow, 16 * sqd + 8 * c);
-  uint32_t p_srow = (uint32_t)srow * 4u;
-
-  wait_vmem_all();
-  issue_fence();
-  lds_barrier();
-
-  // Row statistics of step sidx from its stage (wavefronts 4..7), and the
-  // scaled queries in place.
+  const uint32_t p_srow = (uint32_t)srow * 4u;
   float sterm = 0.0f;  // sink terms -p_sink D of this thread's rows, current head
   auto stats = [&](FStage& st, int sidx) {
+    // This step's loads (and everything before them) have landed once at
+    // most the last dQ's two stores are in flight.
+    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    lds_opaque(p_st[0]);
+    lds_opaque(p_st[1]);
     const uint32_t S = lds_addr(&st);
     int ph, j, rb;
     step_of(sidx, ph, j, rb);
@@ -947,7 +1150,7 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const f32x8 x = __builtin_convertvector(lds_ld<bf16x8>(S + kOffDout + p_st[c]), f32x8);
-      const f32x8 y = __builtin_convertvector(lds_ld<bf16x8>(S + kOffO + p_st[c]), f32x8);
+      const f32x8 y = __builtin_convertvector(o_reg[c], f32x8);
 #pragma unroll
       for (int i = 0; i < 8; ++i) dpart += x[i] * y[i];
       const f32x8 qv = __builtin_convertvector(lds_ld<bf16x8>(S + p_st[c]), f32x8);
@@ -963,213 +1166,106 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
     }
     if (rb == (ph == 0 ? nrb0 : nrb1) - 1) {  // the head's last step in this tile: this wavefront's share of dS_h
       const float sw = wave_sum(sterm);
-      if (lane == 0) lds.wsum[ph][j][w - 4] = sw;
+      if (lane == 0) lds.wsum[ph][j][pw] = sw;
       sterm = 0.0f;
     }
   };
-  if (w >= 4) stats(lds.s0, 0);
 
-  f32x16 dk[2], dv[2];
+  // dQ of step sidx: block (d 32*db_q .. +31, rows 32*nb_q .. +31) = K^T dS^T
+  // over the 256 keys (register r: d = 32*db_q + 8*(r/4) + 4*h2 + r%4, lane
+  // l32: the row), in two accumulators (even and odd 16-key chunks), out
+  // through this wavefront's block of epi.
+  const int db_q = pw & 1, nb_q = pw >> 1;
+  uint32_t p_ks[2], p_dsr[2];
+  tr_pattern(32 * db_q, lane, p_ks[0], p_ks[1]);
+  tr_pattern(32 * nb_q, lane, p_dsr[0], p_dsr[1]);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) { dk[0][i] = dk[1][i] = dv[0][i] = dv[1][i] = 0.0f; }
-
-  // dK, dV of this wavefront's keys (register r: key wk_lo + 8*(r/4) +
-  // 4*h2 + r%4): mode 0 or 1 into that float plane, 2 directly in the output
-  // type (a key tile whose contributions are all in this workgroup).
-  const long plane = (long)T * ks;
-  auto store_dkdv = [&](int mode) {
-    if (wk_lo < 0) return;
-    float* dk_p = a.dk_part + (mode == 1 ? plane : 0) + (long)bos * ks + g * kD;
-    float* dv_p = a.dv_part + (mode == 1 ? plane : 0) + (long)bos * ks + g * kD;
-    bf16* dk_o = (bf16*)a.dk + (long)bos * ks + g * kD;
-    bf16* dv_o = (bf16*)a.dv + (long)bos * ks + g * kD;
+  for (int e = 0; e < 2; ++e) {
+    p_ks[e] += lds_addr(lds.ks);
+    p_dsr[e] += lds_addr(lds.ds[0]);
+  }
+  const uint32_t ep_base = lds_addr(lds.epi[pw]);
+  uint32_t p_epw = (uint32_t)l32 * 64u + 8u * h2;  // + ((gi ^ sw) << 4)
+  const uint32_t ep_sw = (uint32_t)((l32 >> 2) & 3);
+  uint32_t p_epr[2];
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      const int d = 32 * db + l32;
+  for (int i = 0; i < 2; ++i) {
+    const int c = lane + 64 * i, row = c >> 2, jc = c & 3;
+    p_epr[i] = (uint32_t)row * 64u + ((uint32_t)(jc ^ ((row >> 2) & 3)) << 4);
+  }
+  auto dq_of = [&](int sidx) {
+    lds_opaque(p_ks[0]);
+    lds_opaque(p_ks[1]);
+    lds_opaque(p_dsr[0]);
+    lds_opaque(p_dsr[1]);
+    const uint32_t dsb = (sidx & 1) ? kDsBytes : 0u;
+    int ph, j, rb;
+    step_of(sidx, ph, j, rb);
+    const int qb = q0 + kFQ * ph + kBM * rb;
+    f32x16 acc0, acc1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = wk_lo + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        if (key < L) {
-          if (mode == 2) {
-            dk_o[(long)key * ks + d] = (bf16)(dk[db][r] * kLn2);
-            dv_o[(long)key * ks + d] = (bf16)dv[db][r];
-          } else {
-            dk_p[(long)key * ks + d] = dk[db][r] * kLn2;
-            dv_p[(long)key * ks + d] = dv[db][r];
-          }
-        }
-      }
+    for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kFK / 16; c += 2) {
+      acc0 = mfma32(lds_tr8(p_ks[0] + 2048u * c, p_ks[1] + 2048u * c),
+                    lds_tr8(p_dsr[0] + dsb + 2048u * c, p_dsr[1] + dsb + 2048u * c), acc0);
+      acc1 = mfma32(lds_tr8(p_ks[0] + 2048u * (c + 1), p_ks[1] + 2048u * (c + 1)),
+                    lds_tr8(p_dsr[0] + dsb + 2048u * (c + 1), p_dsr[1] + dsb + 2048u * (c + 1)), acc1);
+    }
+    lds_opaque(p_epw);
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const f32x4 v = {(acc0[4 * gi] + acc1[4 * gi]) * a.scale, (acc0[4 * gi + 1] + acc1[4 * gi + 1]) * a.scale,
+                       (acc0[4 * gi + 2] + acc1[4 * gi + 2]) * a.scale, (acc0[4 * gi + 3] + acc1[4 * gi + 3]) * a.scale};
+      lds_st<bf16x4>(ep_base + p_epw + (((uint32_t)gi ^ ep_sw) << 4), __builtin_convertvector(v, bf16x4));
+    }
+    issue_fence();  // the reads below take other lanes' writes (LDS keeps a wavefront's order)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = lane + 64 * i, row = c >> 2, jc = c & 3;
+      const bf16x8 x = lds_ld<bf16x8>(ep_base + p_epr[i]);
+      const int qrow = qb + 32 * nb_q + row;
+      if (qrow < L)
+        *(bf16x8*)((bf16*)a.dq + (long)(bos + qrow) * qs + (g * G + j) * kD + 32 * db_q + 8 * jc) = x;
     }
   };
 
-  // One step: consume `st` (step cs), compute the statistics of step cs + 1 in
-  // `nx`, prefetch step cs + 2 into `nn` (the stage of step cs - 1).
-  int cs = 0;
-  auto step = [&](FStage& st, FStage& nx, FStage& nn) {
-    lds_opaque(p_seed);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) lds_opaque(p_row[c]);
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      lds_opaque(p_tr[db][0]);
-      lds_opaque(p_tr[db][1]);
-    }
-    const uint32_t S = lds_addr(&st);
-    lds_barrier();  // statistics and scaled queries of `st` ready; ds and `nn` free
-    prefetch(nn);
+  // Prologue: step 0 and its statistics, then step 1 (its wait is the first
+  // step's statistics').  (The key wavefronts stage K.)
+  prefetch(lds.s0);
+  issue_fence();
+  stats(lds.s0, 0);
+  prefetch(lds.s1);
+  issue_fence();
+
+  // One step: barrier cs, the statistics of step cs + 1 (loaded during step
+  // cs - 1), the prefetch of step cs + 2 into the stage of step cs - 1, then
+  // dQ of step cs - 1.  Stages by index: step i uses stage i % 3.
+  auto ring = [&](int i) -> FStage& { return *(FStage*)((char*)&lds.s0 + i * sizeof(FStage)); };
+  int cs = 0, stg = 0;  // step, its stage
+  auto pstep = [&]() {
+    const int nx = stg == kStages - 1 ? 0 : stg + 1, nn = nx == kStages - 1 ? 0 : nx + 1;
+    lds_barrier();  // step cs - 1's dS^T complete; its stage free
+    if (cs + 1 < nsteps) stats(ring(nx), cs + 1);
+    prefetch(ring(nn));
     issue_fence();
-    int ph, j, rb;
-    step_of(cs, ph, j, rb);
-    const int qb = q0 + kFQ * ph + kBM * rb;
-    const int wk_hi = wk_lo + 31;
-    const bool active = wk_lo >= 0 && wk_lo < L && wk_lo <= qb + kBM - 1 && qb - wk_hi < window;
-    if (active) {
-      const bool mask_lo = wk_hi > qb;
-      const bool mask_hi = (qb + kBM > L) || (qb + kBM - 1 - wk_lo >= window);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        // S and dP for rows 32*mb .. 32*mb+31 of the step, seeded with the row
-        // statistics (register r: row 32*mb + 16*(r/8) + 8*h2 + r%8).
-        f32x16 s, dp;
-        {
-          const uint32_t sa = S + kOffNlse + 128u * mb + p_seed, da = S + kOffNdelta + 128u * mb + p_seed;
-          const f32x8 s0 = lds_ld<f32x8>(sa), s1 = lds_ld<f32x8>(sa + 64);
-          const f32x8 d0 = lds_ld<f32x8>(da), d1 = lds_ld<f32x8>(da + 64);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            s[i] = s0[i];
-            s[8 + i] = s1[i];
-            dp[i] = d0[i];
-            dp[8 + i] = d1[i];
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          s = mfma32(lds_ld<bf16x8>(S + 4096u * mb + p_row[c]), kf[c], s);
-          dp = mfma32(lds_ld<bf16x8>(S + kOffDout + 4096u * mb + p_row[c]), vf[c], dp);
-        }
-        bf16x8 pf8[2], df[2];
-        const int rbase = qb + 32 * mb + 8 * h2;
-        const int lo = key_n - rbase;
-        const int hi = min(L - rbase, lo + window);
-        auto softmax_grad = [&](auto test_lo, auto test_hi) {
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            f32x8 pv, dv8;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const int r = 8 * hb + i;
-              float p = fast_exp2(s[r]);
-              const int idx = 16 * hb + i;
-              bool vis = true;
-              if constexpr (decltype(test_lo)::value) vis = vis && idx >= lo;
-              if constexpr (decltype(test_hi)::value) vis = vis && idx < hi;
-              p = vis ? p : 0.0f;
-              pv[i] = p;
-              dv8[i] = p * dp[r];
-            }
-            pf8[hb] = __builtin_convertvector(pv, bf16x8);
-            df[hb] = __builtin_convertvector(dv8, bf16x8);
-          }
-        };
-        if (mask_lo && mask_hi)
-          softmax_grad(std::true_type{}, std::true_type{});
-        else if (mask_lo)
-          softmax_grad(std::true_type{}, std::false_type{});
-        else if (mask_hi)
-          softmax_grad(std::false_type{}, std::true_type{});
-        else
-          softmax_grad(std::false_type{}, std::false_type{});
-        // dS^T row of this lane's key: 8 consecutive query rows per register half.
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) lds_st<bf16x8>(p_dsw[mb][hb], df[hb]);
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc) {
-            const uint32_t o = 2048u * (2 * mb + cc);
-            dv[db] = mfma32(pf8[cc], lds_tr8(S + kOffDout + o + p_tr[db][0], S + kOffDout + o + p_tr[db][1]), dv[db]);
-            dk[db] = mfma32(df[cc], lds_tr8(S + o + p_tr[db][0], S + o + p_tr[db][1]), dk[db]);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) lds_st<bf16x8>(p_dsw[mb][hb], zero8());
-    }
-    // This wavefront's share of step cs + 1 has landed once at most the
-    // prefetch just issued is in flight (the older dQ stores are covered too).
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    static_assert(kFPrefetchOps == 4, "wait count");
-    lds_barrier();  // ds complete; step cs + 1 visible
-    if (w < 4) {
-      // dQ^T block (d 32*db_q .. +31, rows 32*nb_q .. +31 of the step) = K^T dS^T
-      // over the 256 keys; register r: d = 32*db_q + 8*(r/4) + 4*h2 + r%4.
-      lds_opaque(p_ks[0]);
-      lds_opaque(p_ks[1]);
-      lds_opaque(p_dsr[0]);
-      lds_opaque(p_dsr[1]);
-      f32x16 acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-#pragma unroll
-      for (int c = 0; c < kFK / 16; ++c)
-        acc = mfma32(lds_tr8(p_ks[0] + 2048u * c, p_ks[1] + 2048u * c),
-                     lds_tr8(p_dsr[0] + 2048u * c, p_dsr[1] + 2048u * c), acc);
-      // Out through the consumed stage's Q tile (idle until the next step's
-      // prefetch, which follows that step's barrier).
-      lds_opaque(p_epw);
-#pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        const f32x4 v = {acc[4 * gi] * a.scale, acc[4 * gi + 1] * a.scale, acc[4 * gi + 2] * a.scale,
-                         acc[4 * gi + 3] * a.scale};
-        lds_st<bf16x4>(S + p_epw + (((uint32_t)gi ^ ep_sw) << 4), __builtin_convertvector(v, bf16x4));
-      }
-      issue_fence();  // the reads below take other lanes' writes (LDS keeps a wavefront's order)
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c = lane + 64 * i, row = c >> 2, jc = c & 3;
-        const bf16x8 x = lds_ld<bf16x8>(S + p_epr[i]);
-        const int qrow = qb + 32 * nb_q + row;
-        if (qrow < L)
-          *(bf16x8*)((bf16*)a.dq + (long)(bos + qrow) * qs + (g * G + j) * kD + 32 * db_q + 8 * jc) = x;
-      }
-    } else if (cs + 1 < nsteps) {
-      lds_opaque(p_st[0]);
-      lds_opaque(p_st[1]);
-      stats(nx, cs + 1);
-    }
-    if (cs == nsteps0 - 1 && nph == 2) {
-      // End of tile 2*pr: wavefronts 0..3 hand in the tile before it and take
-      // the tile after it (ks rows 0..127 are free once every wavefront has
-      // finished this step's dQ).
-      lds_barrier();
-      if (w < 4) {
-        store_dkdv(1);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { dk[0][i] = dk[1][i] = dv[0][i] = dv[1][i] = 0.0f; }
-        wk_lo = q0 + kFQ + 32 * w;
-        key_n = wk_lo + l32;
-        stage_keys(4 * w, 4, wk_lo);
-        load_kv();
-      }
-      wait_vmem_all();
-    }
+    if (cs >= 1 && cs != nsteps0) dq_of(cs - 1);  // (the last phase-0 step's is formed at the swap)
+    stg = nx;
     ++cs;
   };
-  for (int f = 0; f < nsteps; f += kStages) {
-    step(lds.s0, lds.s1, lds.s2);
-    if (f + 1 < nsteps) step(lds.s1, lds.s2, lds.s0);
-    if (f + 2 < nsteps) step(lds.s2, lds.s0, lds.s1);
+  while (cs < nsteps0) pstep();
+  if (nph == 2) {
+    lds_barrier();  // phase 0's last dS^T is complete
+    dq_of(nsteps0 - 1);
+    lds_barrier();  // done with the old ks rows
+    while (cs < nsteps) pstep();
   }
-
+  lds_barrier();  // the last step's dS^T is complete
+  dq_of(nsteps - 1);
   // The ring's last, redundant loads land before the end; wsum is complete
-  // after the barrier.
+  // (the statistics of every step were formed before the last barrier).
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int j = tid; j < G; j += 512) {
+  for (int j = pt; j < G; j += 256) {
     const float* ws0 = lds.wsum[0][j];
     dsink_slots[j * slot_stride] = (ws0[0] + ws0[1]) + (ws0[2] + ws0[3]);
     if (2 * pr + 1 < ntiles) {
@@ -1177,16 +1273,6 @@ __global__ __launch_bounds__(512) void bwd_window_kernel(BwdArgs a) {
       dsink_slots[j * slot_stride + 1] = nph == 2 ? (ws1[0] + ws1[1]) + (ws1[2] + ws1[3]) : 0.0f;
     }
   }
-  // Tile 2*pr (wavefronts 4..7) has all its contributions: the rows of tiles
-  // 2*pr and 2*pr + 1.  Wavefronts 0..3 hold the tile before it (one phase:
-  // plane 1, the next tile's rows) or the tile after it: plane 0 if a later
-  // workgroup adds that tile's next rows, else complete.
-  if (w >= 4)
-    store_dkdv(2);
-  else if (nph == 1)
-    store_dkdv(1);
-  else
-    store_dkdv(q0 + 2 * kFQ >= L ? 2 : 0);
 }
 
 // dK, dV of the key tiles that two fused workgroups share: odd tile
@@ -1325,8 +1411,8 @@ hipError_t launch_bwd(const BwdArgs& args, int dtype, int max_seqlen, int num_se
     const int npairs = (max_seqlen + 2 * kFQ - 1) / (2 * kFQ);
     if (T > 0) {
       const dim3 grid(npairs * a.num_kv_heads, num_seqs);
-      hipLaunchKernelGGL(bwd_window_kernel, grid, dim3(512), 0, stream, a);
-      if ((e = after_launch("bwd_window_kernel", grid, dim3(512), split, stream)) != hipSuccess) return e;
+      hipLaunchKernelGGL(bwd_window_kernel, grid, dim3(kFThreads), 0, stream, a);
+      if ((e = after_launch("bwd_window_kernel", grid, dim3(kFThreads), split, stream)) != hipSuccess) return e;
     }
     if ((e = mark(1)) != hipSuccess) return e;
     if ((e = mark(2)) != hipSuccess) return e;
