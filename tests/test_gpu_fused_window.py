@@ -73,3 +73,36 @@ def test_fused_and_two_kernel_paths_agree(monkeypatch):
         e = rel_l2(res["1"][n], res["0"][n])
         say(f"  {n} fused vs two-kernel rel-L2 {e:.2e}")
         assert e < 5e-3, (n, e)
+
+
+def test_fused_backward_is_bitwise_reproducible_at_scale(monkeypatch):
+    """Two 4096-token sequences, 64 query heads on 8 KV heads, window 128:
+    256 fused workgroups at once, three runs over different workspace
+    contents give identical bits.  Each of the kernel's producer wavefronts
+    forms the statistics of the rows it loaded itself; a hand-over between
+    wavefronts without a barrier would show here as run-to-run differences."""
+    import attention_sink_fwd_amd as sa
+
+    monkeypatch.setenv("SINK_ATTN_BWD_FUSED", "1")
+    w = custom_workload((4096, 4096), 64, 8, 64, 128, "bf16")
+    say("case fused bitwise at scale", w.lengths)
+    d = {k: v.to("cuda:0") for k, v in make_inputs(w, seed=77).items()}
+    assert sa.sink_attn_bwd_fused(d["q"], d["k"], d["cu_seqlens"], w.max_seqlen, w.softmax_scale, 128)
+    o, lse = sa.sink_attn_fwd(d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens"], w.max_seqlen,
+                              w.softmax_scale, 128)
+    nb = sa.sink_attn_bwd_workspace_size(d["q"], d["k"], d["cu_seqlens"], w.max_seqlen, w.softmax_scale, 128)
+    outs = []
+    for fill in (0x00, 0x7F, 0xFF):
+        ws = torch.full((nb,), fill, dtype=torch.uint8, device="cuda:0")
+        r = sa.sink_attn_bwd(d["q"], d["k"], d["v"], d["sinks"], o, lse, d["dout"], d["cu_seqlens"],
+                             w.max_seqlen, w.softmax_scale, 128, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in r])
+    for run in outs[1:]:
+        for a, b in zip(outs[0], run):
+            assert torch.equal(a, b)
+    # and the first run is right: dS_h against its definition on the GPU's own O and LSE
+    s = d["sinks"].double().cpu()
+    dvec = torch.einsum("thd,thd->ht", d["dout"].double().cpu(), o.double().cpu())
+    want = -(torch.exp(s[:, None] - lse.double().cpu()) * dvec).sum(dim=1)
+    assert rel_l2(outs[0][3].double().cpu().numpy(), want.numpy()) < 1e-5
