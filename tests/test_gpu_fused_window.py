@@ -1,5 +1,5 @@
 """Short sliding windows (1..128 keys, bf16, head_dim 64): the fused backward
-kernel (one workgroup per 128-row query tile and KV group, dQ, dK, dV and the
+kernel (one workgroup per pair of 128-row query tiles and KV group; dQ, dK, dV and the
 sink gradient from one pass) and, with SINK_ATTN_BWD_FUSED=0, the dQ and
 dK/dV kernels, each against the float64 oracle on every element.
 
