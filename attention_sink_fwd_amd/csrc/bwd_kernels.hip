@@ -739,14 +739,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 // Fused backward for short sliding windows (window <= 128, head_dim 64, bf16
 // inputs).  Query row i of a 128-row tile sees only keys i - window + 1 .. i,
 // which lie in the tile's own 128 keys and the 128 before them.  One workgroup
-// takes one such query tile and every query head of one KV group, with all
-// 256 keys resident: K in LDS and in registers, V in registers.  Per 64-row
-// step (one head) it forms S, dP, P and dS once, as the dK/dV kernel does,
-// accumulates dK and dV in registers over all the group's heads, and passes
-// dS^T through LDS so that the step's dQ = scale dS K is formed completely
-// inside the workgroup (every key that reaches these rows is in it).  So Q,
-// dO and O are each read once, dQ written once, and no scaled copy of Q goes
-// through memory.
+// takes two consecutive such query tiles in turn, for every query head of one
+// KV group, with the 256 keys the current tile sees resident: K in LDS, V in
+// registers.  Per 64-row step (one head) it forms S, dP, P and dS once, as
+// the dK/dV kernel does, accumulates dK and dV in registers over all the
+// group's heads, and passes dS^T through LDS so that the step's dQ = scale dS
+// K is formed completely inside the workgroup (every key that reaches these
+// rows is in it).  So Q, dO and O are each read once, dQ written once, and no
+// scaled copy of Q goes through memory.
 //
 // The twelve wavefronts have two roles, three per SIMD:
 // * eight key wavefronts (32 keys each) do only the step's products: S, dP,
@@ -760,11 +760,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 // One barrier per step hands everything over: at barrier cs the step's
 // statistics are ready and the previous step's dS^T is complete; the dQ of
 // step cs - 1 and the statistics of step cs + 1 then run beside the products
-// of step cs.  dK and dV of a key tile get contributions from two workgroups
-// (the tile's own query rows and the next tile's); each writes its float sums
-// to its own plane (0: own rows, 1: the next tile's rows; the last tile of a
-// sequence writes zeros to plane 1) and the post kernel adds the two planes
-// in that order.
+// of step cs.  dK and dV of key tile t get contributions from query tiles t
+// and t + 1.  For query tiles 2p and 2p + 1, key tile 2p has both in this
+// workgroup and is written once in the output type; key tiles 2p - 1 and
+// 2p + 1 share theirs with the neighbouring workgroups, so each part goes to
+// a float plane of its own (0: the tile's own rows, 1: the next tile's rows;
+// a tile with no next rows is written whole), and the post kernel adds the
+// two planes in that order.
 constexpr int kFQ = 128;          // query rows per fused workgroup
 constexpr int kFK = 2 * kFQ;      // keys it sees
 constexpr int kFMaxGroup = 64;    // query heads per KV head the fused kernel takes
