@@ -876,19 +876,21 @@ __global__ __launch_bounds__(kFThreads) void bwd_window_kernel(BwdArgs a) {
     // reads of d block db (+ 2048 per 16 query rows).  The two loops below run
     // one step per iteration (no unrolling over the ring), so that the key
     // swap between them sits outside both.
+    // The chunk swizzle is an XOR on address bits 4..6 (stage bases and row
+    // offsets leave them clear): chunk 2c + h2 of a row is the c = 0 one with
+    // bits 5..6 XOR 2c, and d block 1 of a transposing read is block 0 with
+    // bit 6 flipped.  So one register per pattern.
     const uint32_t s0 = lds_addr(&lds.s0);
+    static_assert(sizeof(FStage) % 128 == 0, "stage bases keep address bits 4..6 clear");
     const int qrow_base = row_perm(l32);
     uint32_t p_seed = s0 + 32u * h2;
-    uint32_t p_row[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) p_row[c] = s0 + swz_b(qrow_base, 16 * c + 8 * h2);
-    uint32_t p_tr[2][2];
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      tr_pattern(32 * db, lane, p_tr[db][0], p_tr[db][1]);
-      p_tr[db][0] += s0;
-      p_tr[db][1] += s0;
-    }
+    uint32_t p_row0 = s0 + swz_b(qrow_base, 8 * h2);
+    auto p_row = [&](int c) { return p_row0 ^ (32u * (uint32_t)c); };
+    uint32_t p_tr0[2];
+    tr_pattern(0, lane, p_tr0[0], p_tr0[1]);
+    p_tr0[0] += s0;
+    p_tr0[1] += s0;
+    auto p_tr = [&](int db, int e) { return p_tr0[e] ^ (64u * (uint32_t)db); };
     // dS^T row of this lane's key kl = 32 w + l32: rows 32*mb + 16*hb + 8*h2
     // .. + 7 are 16-byte chunk 4*mb + 2*hb + h2, stored in slot chunk ^ f(kl)
     // (+ kDsBytes for odd steps).  Its K row in ks has the same swizzle: d
@@ -941,13 +943,9 @@ __global__ __launch_bounds__(kFThreads) void bwd_window_kernel(BwdArgs a) {
     int cs = 0, stg = 0;  // step, its stage
     auto step = [&]() {
       lds_opaque(p_seed);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) lds_opaque(p_row[c]);
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        lds_opaque(p_tr[db][0]);
-        lds_opaque(p_tr[db][1]);
-      }
+      lds_opaque(p_row0);
+      lds_opaque(p_tr0[0]);
+      lds_opaque(p_tr0[1]);
       lds_opaque(p_dsrow);
       lds_opaque(p_dsx);
       lds_barrier();  // statistics of this stage ready; ds[cs % 2] free (its dQ is done)
@@ -956,95 +954,109 @@ __global__ __launch_bounds__(kFThreads) void bwd_window_kernel(BwdArgs a) {
       step_of(cs, ph, j, rb);
       const int qb = q0 + kFQ * ph + kBM * rb;
       const int wk_hi = wk_lo + 31;
-      const bool active = wk_lo >= 0 && wk_lo < L && wk_lo <= qb + kBM - 1 && qb - wk_hi < window;
-      if (active) {
-        // Rows of this step that some key of the wavefront does not see
+      // One 32-row half of the step (rows h0 .. h0 + 31, h0 = qb + 32*mb):
+      // S and dP seeded with the row statistics (register r: row h0 +
+      // 16*(r/8) + 8*h2 + r%8), P and dS, dS^T to LDS, dV and dK.  A half
+      // that none of the wavefront's keys reach (past the window, before the
+      // diagonal or past the sequence) only writes its dS^T rows as zeros.
+      auto half_live = [&](int mb) {
+        const int h0 = qb + 32 * mb, h1 = min(h0 + 31, L - 1);
+        return wk_lo >= 0 && h0 < L && wk_lo <= h1 && h0 - wk_hi < window;
+      };
+      auto zero_half = [&](int mb) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) lds_st<bf16x8>(dsw_addr(mb, hb) + dsb, zero8());
+      };
+      // mb: a constant (both halves) or a wavefront-uniform value (one half).
+      auto half = [&](auto mbv) {
+        const int mb = mbv;
+        const int h0 = qb + 32 * mb;
+        // Rows of this half that some key of the wavefront does not see
         // (causal side, window side or past the sequence): one masked form.
-        const bool masked = (wk_hi > qb) || (qb + kBM > L) || (qb + kBM - 1 - wk_lo >= window);
+        const bool masked = (wk_hi > h0) || (h0 + 32 > L) || (h0 + 31 - wk_lo >= window);
+        f32x16 s, dp;
+        {
+          const uint32_t sa = p_seed + kOffNlse + 128u * mb, da = p_seed + kOffNdelta + 128u * mb;
+          const f32x8 s0v = lds_ld<f32x8>(sa), s1v = lds_ld<f32x8>(sa + 64);
+          const f32x8 d0v = lds_ld<f32x8>(da), d1v = lds_ld<f32x8>(da + 64);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          // S and dP for rows 32*mb .. 32*mb+31 of the step, seeded with the row
-          // statistics (register r: row 32*mb + 16*(r/8) + 8*h2 + r%8).
-          f32x16 s, dp;
-          {
-            const uint32_t sa = p_seed + kOffNlse + 128u * mb, da = p_seed + kOffNdelta + 128u * mb;
-            const f32x8 s0v = lds_ld<f32x8>(sa), s1v = lds_ld<f32x8>(sa + 64);
-            const f32x8 d0v = lds_ld<f32x8>(da), d1v = lds_ld<f32x8>(da + 64);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              s[i] = s0v[i];
-              s[8 + i] = s1v[i];
-              dp[i] = d0v[i];
-              dp[8 + i] = d1v[i];
-            }
-          }
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            s = mfma32(lds_ld<bf16x8>(p_row[c] + 4096u * mb), kf_of(c), s);
-            dp = mfma32(lds_ld<bf16x8>(p_row[c] + kOffDout + 4096u * mb), vf[c], dp);
-          }
-          bf16x8 pf8[2], df[2];
-          auto softmax_grad = [&](auto test) {
-            // Visible iff lo <= 16*hb + i < hi, from this lane's key and first
-            // row.  (The lane id is read again here rather than kept live
-            // through the loop: the key wavefronts have no register to spare.)
-            int lo = 0, hi = 0;
-            if constexpr (decltype(test)::value) {
-              const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-              const int rbase = qb + 32 * mb + ((ln >> 2) & 8);
-              lo = wk_lo + (ln & 31) - rbase;
-              hi = min(L - rbase, lo + window);
-            }
-#pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-              f32x8 pv, dv8;
-#pragma unroll
-              for (int i = 0; i < 8; ++i) {
-                const int r = 8 * hb + i;
-                float p = fast_exp2(s[r]);
-                const int idx = 16 * hb + i;
-                if constexpr (decltype(test)::value) p = (idx >= lo && idx < hi) ? p : 0.0f;
-                pv[i] = p;
-                dv8[i] = p * dp[r];
-              }
-              pf8[hb] = __builtin_convertvector(pv, bf16x8);
-              df[hb] = __builtin_convertvector(dv8, bf16x8);
-            }
-          };
-          if (masked)
-            softmax_grad(std::true_type{});
-          else
-            softmax_grad(std::false_type{});
-          // dS^T row of this lane's key: 8 consecutive query rows per register half.
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb) lds_st<bf16x8>(dsw_addr(mb, hb) + dsb, df[hb]);
-#pragma unroll
-          for (int db = 0; db < 2; ++db) {
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-              const uint32_t o = 2048u * (2 * mb + cc);
-              dv[db] = mfma32(pf8[cc], lds_tr8(p_tr[db][0] + kOffDout + o, p_tr[db][1] + kOffDout + o), dv[db]);
-              dk[db] = mfma32(df[cc], lds_tr8(p_tr[db][0] + o, p_tr[db][1] + o), dk[db]);
-            }
+          for (int i = 0; i < 8; ++i) {
+            s[i] = s0v[i];
+            s[8 + i] = s1v[i];
+            dp[i] = d0v[i];
+            dp[8 + i] = d1v[i];
           }
         }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          s = mfma32(lds_ld<bf16x8>(p_row(c) + 4096u * mb), kf_of(c), s);
+          dp = mfma32(lds_ld<bf16x8>(p_row(c) + kOffDout + 4096u * mb), vf[c], dp);
+        }
+        bf16x8 pf8[2], df[2];
+        auto softmax_grad = [&](auto test) {
+          // Visible iff lo <= 16*hb + i < hi, from this lane's key and first
+          // row.  (The lane id is read again here rather than kept live
+          // through the loop: the key wavefronts have no register to spare.)
+          int lo = 0, hi = 0;
+          if constexpr (decltype(test)::value) {
+            const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+            const int rbase = h0 + ((ln >> 2) & 8);
+            lo = wk_lo + (ln & 31) - rbase;
+            hi = min(L - rbase, lo + window);
+          }
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            f32x8 pv, dv8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int r = 8 * hb + i;
+              float p = fast_exp2(s[r]);
+              const int idx = 16 * hb + i;
+              if constexpr (decltype(test)::value) p = (idx >= lo && idx < hi) ? p : 0.0f;
+              pv[i] = p;
+              dv8[i] = p * dp[r];
+            }
+            pf8[hb] = __builtin_convertvector(pv, bf16x8);
+            df[hb] = __builtin_convertvector(dv8, bf16x8);
+          }
+        };
+        if (masked)
+          softmax_grad(std::true_type{});
+        else
+          softmax_grad(std::false_type{});
+        // dS^T row of this lane's key: 8 consecutive query rows per register half.
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) lds_st<bf16x8>(dsw_addr(mb, hb) + dsb, df[hb]);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const uint32_t o = 2048u * (2 * mb + cc);
+            dv[db] = mfma32(pf8[cc], lds_tr8(p_tr(db, 0) + kOffDout + o, p_tr(db, 1) + kOffDout + o), dv[db]);
+            dk[db] = mfma32(df[cc], lds_tr8(p_tr(db, 0) + o, p_tr(db, 1) + o), dk[db]);
+          }
+        }
+      };
+      const bool live0 = half_live(0), live1 = half_live(1);
+      if (live0 || live1) {
+        // The first live half, then the second one if it is live too.
+        const int mb = __builtin_amdgcn_readfirstlane(live0 ? 0 : 1);
+        half(mb);
+        if (live0 && live1)
+          half(std::integral_constant<int, 1>{});
+        else
+          zero_half(1 - mb);
       } else {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb) lds_st<bf16x8>(dsw_addr(mb, hb) + dsb, zero8());
+        zero_half(0);
+        zero_half(1);
       }
       // Next step's stage.
       const uint32_t adv = stg == kStages - 1 ? (uint32_t)(-(kStages - 1) * (int)sizeof(FStage)) : (uint32_t)sizeof(FStage);
       stg = stg == kStages - 1 ? 0 : stg + 1;
       p_seed += adv;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) p_row[c] += adv;
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        p_tr[db][0] += adv;
-        p_tr[db][1] += adv;
-      }
+      p_row0 += adv;
+      p_tr0[0] += adv;
+      p_tr0[1] += adv;
       ++cs;
     };
     while (cs < nsteps0) step();
