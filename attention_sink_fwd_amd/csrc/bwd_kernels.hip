@@ -781,8 +781,10 @@ struct __attribute__((aligned(16))) FStage {
   float ndelta[kBM];    // -D
 };
 // The workgroup's LDS in one object, so the layout (and every constant
-// offset between its parts) is fixed.
-struct __attribute__((aligned(16))) FLds {
+// offset between its parts) is fixed; 128-byte aligned, so stage and row
+// addresses keep address bits 0..6 clear (the key wavefronts derive swizzled
+// addresses by XOR on bits 4..6).
+struct __attribute__((aligned(128))) FLds {
   FStage s0, s1, s2;        // ring of 64-row steps
   bf16 ks[kFK * kD];        // K of the 256 keys, swizzled [key][d]
   bf16 ds[2][kFK * kBM];    // dS^T of steps of even / odd index, swizzled [key][row]
