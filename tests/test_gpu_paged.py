@@ -195,3 +195,44 @@ def test_paged_rows_bit_identical_with_minus_inf_sink_and_very_negative_scores(w
     rows = pg["rows"].to("cuda:0")
     assert torch.isfinite(o_t).all() and torch.isfinite(lse_t).all()
     assert torch.equal(o, o_t[rows]) and torch.equal(lse, lse_t[:, rows])
+
+
+def _draw_paged_shape(seed):
+    rng = np.random.default_rng(seed)
+    nseq = int(rng.integers(1, 9))
+    lens = [int(x) for x in rng.integers(1, 3000, size=nseq)]
+    decode = rng.random() < 0.5
+    q_lens = [1 if decode else int(rng.integers(1, L + 1)) for L in lens]
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8, 16]))
+    d = int(rng.choice([64, 64, 64, 32, 40]))
+    dtype = "bf16" if rng.random() < 0.85 else "f32"
+    window = 0 if rng.random() < 0.5 else int(rng.integers(1, 400))
+    ps = int(rng.choice([64, 128, 256, 512]))
+    sinks = str(rng.choice(["normal", "mixed", "minus_inf"]))
+    return lens, q_lens, hq, hkv, d, dtype, window, ps, sinks
+
+
+@pytest.mark.parametrize("seed", range(7000, 7040))
+def test_random_paged_shapes_bit_identical_to_training_rows(seed):
+    """Seeded random batches: one to eight sequences of 1..2999 cached keys,
+    decode (one new token each) or prefill (1..L new tokens), pages of 64 to
+    512 keys in shuffled order (unused slots hold NaN), windows, float32 and
+    head dimensions 32 to 64.  The new rows equal the training forward's rows
+    at the same positions bit for bit, and are finite."""
+    import attention_sink_fwd_amd as sa
+    from tests.test_gpu_parity import _set_sinks
+
+    lens, q_lens, hq, hkv, d, dtype, window, ps, sinks = _draw_paged_shape(seed)
+    say("case paged random", seed, lens, "decode" if max(q_lens) == 1 else "prefill", hq, hkv, d, dtype,
+        window, ps, sinks)
+    w = custom_workload(lens, hq, hkv, d, window, dtype)
+    inp = _set_sinks(make_inputs(w, seed=seed), sinks, hq)
+    dev = {k: v.to("cuda:0") for k, v in inp.items()}
+    o_t, lse_t = sa.sink_attn_fwd(dev["q"], dev["k"], dev["v"], dev["sinks"], dev["cu_seqlens"],
+                                  w.max_seqlen, w.softmax_scale, window)
+    pg = make_paged(inp, q_lens, ps, seed=seed)
+    o, lse = _run(pg, w)
+    rows = pg["rows"].to("cuda:0")
+    assert torch.isfinite(o).all()
+    assert torch.equal(o, o_t[rows]) and torch.equal(lse, lse_t[:, rows])
