@@ -259,6 +259,19 @@ bool use_fused(const sink_attn_params* p) {
                                       p->num_kv_heads);
 }
 
+// Query tiles per fused workgroup: SINK_ATTN_FUSED_TILES if set (1..4), else
+// the shape-based choice.
+int resolve_fused_tiles(const sink_attn_params* p, int* out) {
+  if (const char* env = std::getenv("SINK_ATTN_FUSED_TILES")) {
+    const int n = std::atoi(env);
+    if (n < 1 || n > 4) return fail(SINK_ATTN_ERR_INVALID_ARG, "SINK_ATTN_FUSED_TILES=%s must be 1, 2, 3 or 4", env);
+    *out = n;
+    return SINK_ATTN_OK;
+  }
+  *out = sinkattn::fused_tiles_per_workgroup(p->max_seqlen, p->num_seqs, p->num_kv_heads);
+  return SINK_ATTN_OK;
+}
+
 sinkattn::BwdWorkspace workspace_layout(const sink_attn_params* p, int dkdv_heads, int pack_heads, bool fused) {
   return sinkattn::bwd_workspace_layout(p->total_tokens, p->num_q_heads, p->num_kv_heads, p->head_dim, p->max_seqlen,
                                         p->num_seqs, dkdv_heads, pack_heads, fused);
@@ -289,6 +302,7 @@ int bwd_check(const sink_attn_params* p, const BwdTensors& t) {
 int bwd_split(const sink_attn_params* p, BwdSplit* split) {
   split->dkdv_overridden = std::getenv("SINK_ATTN_DKDV_HEADS") != nullptr;
   split->fused = use_fused(p);
+  if (split->fused) SA_CHECK(resolve_fused_tiles(p, &split->fused_tiles));
   SA_CHECK(resolve_dkdv_heads(p, &split->dkdv_heads));
   return resolve_pack_heads(p, 32, &split->pack_heads);
 }
@@ -322,6 +336,7 @@ int bwd_enqueue(const sink_attn_params* p, const BwdTensors& t, void* workspace,
   a.dkdv_heads = split.dkdv_heads;
   a.heads_per_tile = split.pack_heads;
   a.fused = split.fused ? 1 : 0;
+  a.fused_tiles = split.fused_tiles;
   a.dsink_tiles = (p->max_seqlen + 127) / 128;
   a.dkdv_planes = split.fused ? 2 : p->num_q_heads / p->num_kv_heads / split.dkdv_heads;
   hipError_t e = launch_bwd(a, p->dtype, p->max_seqlen, p->num_seqs, s, g_bwd_events_on ? g_bwd_events : nullptr);

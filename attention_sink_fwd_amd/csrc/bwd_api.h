@@ -29,11 +29,13 @@ struct BwdTensors {
 int bwd_check(const sink_attn_params* p, const BwdTensors& t);
 // The work split: the fused short-window kernel or the dQ and dK/dV kernels,
 // and for the latter the query heads per dK/dV workgroup and per dQ
-// workgroup (the shape-based choice, or the SINK_ATTN_BWD_FUSED,
-// SINK_ATTN_DKDV_HEADS and SINK_ATTN_PACK_HEADS overrides; dkdv_overridden
+// workgroup; for the former the query tiles per workgroup (the shape-based
+// choice, or the SINK_ATTN_BWD_FUSED, SINK_ATTN_DKDV_HEADS,
+// SINK_ATTN_PACK_HEADS and SINK_ATTN_FUSED_TILES overrides; dkdv_overridden
 // tells whether the second was given).
 struct BwdSplit {
   bool fused = false;
+  int fused_tiles = 1;
   int dkdv_heads = 1, pack_heads = 1;
   bool dkdv_overridden = false;
 };

@@ -761,14 +761,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 // statistics are ready and the previous step's dS^T is complete; the dQ of
 // step cs - 1 and the statistics of step cs + 1 then run beside the products
 // of step cs.  dK and dV of key tile t get contributions from query tiles t
-// and t + 1.  For query tiles 2p and 2p + 1, key tile 2p has both in this
-// workgroup and is written once in the output type; key tiles 2p - 1 and
-// 2p + 1 share theirs with the neighbouring workgroups, so each part goes to
-// a float plane of its own (0: the tile's own rows, 1: the next tile's rows;
-// a tile with no next rows is written whole), and the post kernel adds the
-// two planes in that order.
-constexpr int kFQ = 128;          // query rows per fused workgroup
-constexpr int kFK = 2 * kFQ;      // keys it sees
+// and t + 1.  A workgroup takes n consecutive query tiles a .. a + n - 1
+// (n = 1..4, chosen on the host): key tiles a .. a + n - 2 have both in this
+// workgroup and are written once in the output type; key tiles a - 1 and
+// a + n - 1 share theirs with the neighbouring workgroups, so each part goes
+// to a float plane of its own (0: the tile's own rows, 1: the next tile's
+// rows; a tile with no next rows is written whole), and the post kernel adds
+// the two planes in that order.
+constexpr int kFQ = 128;          // query rows per fused query tile
+constexpr int kFK = 2 * kFQ;      // keys a query tile sees
+constexpr int kFMaxTiles = 4;     // query tiles per fused workgroup at most
 constexpr int kFMaxGroup = 64;    // query heads per KV head the fused kernel takes
 constexpr int kFKeyWaves = 8;     // key wavefronts (32 keys each)
 constexpr int kFThreads = 64 * (kFKeyWaves + 4);
@@ -789,7 +791,7 @@ struct __attribute__((aligned(128))) FLds {
   bf16 ks[kFK * kD];        // K of the 256 keys, swizzled [key][d]
   bf16 ds[2][kFK * kBM];    // dS^T of steps of even / odd index, swizzled [key][row]
   bf16 epi[4][32 * 32];     // each producer's dQ block on its way out
-  float wsum[2][kFMaxGroup][4];  // per query tile of the pair, head, producer
+  float wsum[kFMaxTiles][kFMaxGroup][4];  // per query tile of the workgroup, head, producer
 };
 static_assert(sizeof(FLds) <= 160 * 1024, "LDS of one compute unit");
 constexpr uint32_t kOffDout = offsetof(FStage, dout);
@@ -804,43 +806,39 @@ __global__ __launch_bounds__(kFThreads) void bwd_window_kernel(BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
   const int G = udiv_uniform(a.num_q_heads, a.num_kv_heads);
+  const int NT = a.fused_tiles;  // query tiles per workgroup
   const TileUnit unit = xcd_unit(a.num_kv_heads);
-  const int seq = unit.seq, g = unit.head, pr = unit.rank;  // query tiles 2*pr and 2*pr + 1
+  const int seq = unit.seq, g = unit.head;
+  const int t0 = NT * unit.rank;  // query tiles t0 .. t0 + NT - 1
   const int T = a.total_tokens, window = a.window;
-  // dS partial of query head g*G + j for query tile 2*pr + ph:
+  // dS partial of query head g*G + j for query tile t0 + ph:
   // dsink_slots[j * slot_stride + ph] (tiles past the layout are not written)
   const int ntiles = a.dsink_tiles;
   const long slot_stride = (long)a.num_seqs * ntiles;
-  float* __restrict__ dsink_slots = a.dsink_part + ((long)g * G * a.num_seqs + seq) * ntiles + 2 * pr;
+  float* __restrict__ dsink_slots = a.dsink_part + ((long)g * G * a.num_seqs + seq) * ntiles + t0;
   const int bos = a.cu_seqlens[seq];
   const int L = a.cu_seqlens[seq + 1] - bos;
-  const int q0 = pr * 2 * kFQ;
+  const int q0 = t0 * kFQ;
   if (q0 >= L) {
-    for (int j = tid; j < G; j += kFThreads) {
-      if (2 * pr < ntiles) dsink_slots[j * slot_stride] = 0.0f;
-      if (2 * pr + 1 < ntiles) dsink_slots[j * slot_stride + 1] = 0.0f;
-    }
+    for (int j = tid; j < G; j += kFThreads)
+      for (int ph = 0; ph < NT && t0 + ph < ntiles; ++ph) dsink_slots[j * slot_stride + ph] = 0.0f;
     return;
   }
   const int qs = a.num_q_heads * kD, ks = a.num_kv_heads * kD;  // row strides (< 2^31 elements)
   const bf16* __restrict__ Kg = (const bf16*)a.k + (long)bos * ks + g * kD;
   const int kbase = q0 - kFQ;  // first key of the span (< 0 for the first tile)
-  // Phase ph takes query tile 2*pr + ph in 64-row steps, head after head.
-  const int nph = L - q0 > kFQ ? 2 : 1;
-  const int nrb0 = L - q0 > kBM ? 2 : 1;
-  const int nrb1 = nph == 2 ? (L - q0 - kFQ > kBM ? 2 : 1) : 0;
-  const int nsteps0 = G * nrb0, nsteps = nsteps0 + G * nrb1;
+  // Phase ph takes query tile t0 + ph in 64-row steps, head after head; all
+  // phases but the last have 128 rows (two steps per head).
+  const int nph = min(NT, (L - q0 + kFQ - 1) / kFQ);
+  const int nrbl = L - q0 - kFQ * (nph - 1) > kBM ? 2 : 1;  // steps per head of the last phase
+  const int nsteps = 2 * G * (nph - 1) + G * nrbl;
+  const int nsteps0 = nph == 1 ? nsteps : 2 * G;  // steps of phase 0
   auto step_of = [&](int st_i, int& ph, int& j, int& rb) {
-    if (st_i < nsteps0) {
-      ph = 0;
-      j = nrb0 == 2 ? st_i >> 1 : st_i;
-      rb = st_i - j * nrb0;
-    } else {
-      const int t = st_i - nsteps0;
-      ph = 1;
-      j = nrb1 == 2 ? t >> 1 : t;
-      rb = t - j * nrb1;
-    }
+    ph = (st_i >= 2 * G) + (st_i >= 4 * G) + (st_i >= 6 * G);  // (at most four phases: no division)
+    const int t = st_i - 2 * G * ph;
+    const int nrb = ph == nph - 1 ? nrbl : 2;
+    j = nrb == 2 ? t >> 1 : t;
+    rb = t - j * nrb;
   };
   // 8 * nblk keys (rows 8 * blk0 .. of ks) from key0 on into LDS (keys outside the
   // sequence repeat its first or last key; they are masked).
@@ -917,6 +915,12 @@ __global__ __launch_bounds__(kFThreads) void bwd_window_kernel(BwdArgs a) {
     const long plane = (long)T * ks;
     auto store_dkdv = [&](int mode) {
       if (wk_lo < 0) return;
+      // The lane's key and column from an opaque copy of the lane id: the
+      // per-lane addresses are then formed here, not hoisted out of the
+      // phase loop and kept live through every step.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int l32 = ln & 31, h2 = ln >> 5;
       float* dk_p = a.dk_part + (mode == 1 ? plane : 0) + (long)bos * ks + g * kD;
       float* dv_p = a.dv_part + (mode == 1 ? plane : 0) + (long)bos * ks + g * kD;
       bf16* dk_o = (bf16*)a.dk + (long)bos * ks + g * kD;
@@ -1061,35 +1065,41 @@ __global__ __launch_bounds__(kFThreads) void bwd_window_kernel(BwdArgs a) {
       p_tr0[1] += adv;
       ++cs;
     };
-    while (cs < nsteps0) step();
-    if (nph == 2) {
-      // Wavefronts 0..3 hand in the tile before 2*pr and take the tile after
-      // it.  ks rows 0..127 are rewritten once the producers have formed the
-      // last phase-0 step's dQ from them.
-      if (w < 4) {
-        store_dkdv(1);
+    // Phase ph sees key tiles t0 + ph - 1 and t0 + ph: wavefronts 0..3 hold
+    // the one of even offset from t0 - 1, wavefronts 4..7 the other.
+    int pend = nsteps0;
+    while (cs < pend) step();
+    for (int ph = 1; ph < nph; ++ph) {
+      // The group holding key tile t0 + ph - 2 (only phase ph - 1 reaches it
+      // from here) hands it in and takes tile t0 + ph: tile t0 - 1 goes to
+      // plane 1 (the previous workgroup adds its own rows), a later one is
+      // complete.  Its ks rows are rewritten once the producers have formed
+      // the last dQ of phase ph - 1 from them.
+      const bool swaps = ((ph & 1) != 0) == (w < 4);
+      if (swaps) {
+        store_dkdv(ph == 1 ? 1 : 2);
 #pragma unroll
         for (int i = 0; i < 16; ++i) { dk[0][i] = dk[1][i] = dv[0][i] = dv[1][i] = 0.0f; }
-        wk_lo = q0 + kFQ + 32 * w;
+        wk_lo += 2 * kFQ;
         key_n = wk_lo + l32;
       }
-      lds_barrier();  // phase 0's last dS^T is complete
+      lds_barrier();  // phase ph - 1's last dS^T is complete
       lds_barrier();  // the producers are done with the old rows
-      if (w < 4) load_kv();
+      if (swaps) load_kv();
       wait_vmem_all();  // (the next step's barrier makes the new rows visible to the producers)
-      while (cs < nsteps) step();
+      pend = ph == nph - 1 ? nsteps : pend + 2 * G;
+      while (cs < pend) step();
     }
     lds_barrier();  // the last dS^T is complete (the producers' final dQ)
-    // Tile 2*pr (wavefronts 4..7) has all its contributions: the rows of tiles
-    // 2*pr and 2*pr + 1.  Wavefronts 0..3 hold the tile before it (one phase:
-    // plane 1, the next tile's rows) or the tile after it: plane 0 if a later
-    // workgroup adds that tile's next rows, else complete.
-    if (w >= 4)
-      store_dkdv(2);
-    else if (nph == 1)
-      store_dkdv(1);
+    // The group holding the last phase's own key tile t0 + nph - 1: plane 0
+    // if a later workgroup adds the next tile's rows, else complete.  The
+    // other holds tile t0 + nph - 2: complete, or (one phase) tile t0 - 1,
+    // whose other part is the previous workgroup's.
+    const bool holds_last = ((nph - 1) & 1) == 0 ? w >= 4 : w < 4;
+    if (holds_last)
+      store_dkdv(q0 + nph * kFQ >= L ? 2 : 0);
     else
-      store_dkdv(q0 + 2 * kFQ >= L ? 2 : 0);
+      store_dkdv(nph == 1 ? 1 : 2);
     return;
   }
 
@@ -1180,7 +1190,7 @@ __global__ __launch_bounds__(kFThreads) void bwd_window_kernel(BwdArgs a) {
       lds_st<float>(S + kOffNdelta + p_srow, -dpart);
       if (q0 + kFQ * ph + kBM * rb + srow < L) sterm += -__expf(a.sinks[g * G + j] - lse) * dpart;
     }
-    if (rb == (ph == 0 ? nrb0 : nrb1) - 1) {  // the head's last step in this tile: this wavefront's share of dS_h
+    if (rb == (ph == nph - 1 ? nrbl : 2) - 1) {  // the head's last step in this tile: this wavefront's share of dS_h
       const float sw = wave_sum(sterm);
       if (lane == 0) lds.wsum[ph][j][pw] = sw;
       sterm = 0.0f;
@@ -1259,22 +1269,26 @@ __global__ __launch_bounds__(kFThreads) void bwd_window_kernel(BwdArgs a) {
   // dQ of step cs - 1.  Stages by index: step i uses stage i % 3.
   auto ring = [&](int i) -> FStage& { return *(FStage*)((char*)&lds.s0 + i * sizeof(FStage)); };
   int cs = 0, stg = 0;  // step, its stage
+  int pstart = 0;       // first step of the current phase
   auto pstep = [&]() {
     const int nx = stg == kStages - 1 ? 0 : stg + 1, nn = nx == kStages - 1 ? 0 : nx + 1;
     lds_barrier();  // step cs - 1's dS^T complete; its stage free
     if (cs + 1 < nsteps) stats(ring(nx), cs + 1);
     prefetch(ring(nn));
     issue_fence();
-    if (cs >= 1 && cs != nsteps0) dq_of(cs - 1);  // (the last phase-0 step's is formed at the swap)
+    if (cs != pstart) dq_of(cs - 1);  // (a later phase's first step: formed at the key swap)
     stg = nx;
     ++cs;
   };
-  while (cs < nsteps0) pstep();
-  if (nph == 2) {
-    lds_barrier();  // phase 0's last dS^T is complete
-    dq_of(nsteps0 - 1);
+  int pend = nsteps0;
+  while (cs < pend) pstep();
+  for (int ph = 1; ph < nph; ++ph) {
+    lds_barrier();  // phase ph - 1's last dS^T is complete
+    dq_of(cs - 1);
     lds_barrier();  // done with the old ks rows
-    while (cs < nsteps) pstep();
+    pstart = cs;
+    pend = ph == nph - 1 ? nsteps : pend + 2 * G;
+    while (cs < pend) pstep();
   }
   lds_barrier();  // the last step's dS^T is complete
   dq_of(nsteps - 1);
@@ -1282,20 +1296,19 @@ __global__ __launch_bounds__(kFThreads) void bwd_window_kernel(BwdArgs a) {
   // (the statistics of every step were formed before the last barrier).
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   for (int j = pt; j < G; j += 256) {
-    const float* ws0 = lds.wsum[0][j];
-    dsink_slots[j * slot_stride] = (ws0[0] + ws0[1]) + (ws0[2] + ws0[3]);
-    if (2 * pr + 1 < ntiles) {
-      const float* ws1 = lds.wsum[1][j];
-      dsink_slots[j * slot_stride + 1] = nph == 2 ? (ws1[0] + ws1[1]) + (ws1[2] + ws1[3]) : 0.0f;
+    for (int ph = 0; ph < NT && t0 + ph < ntiles; ++ph) {
+      const float* ws = lds.wsum[ph][j];
+      dsink_slots[j * slot_stride + ph] = ph < nph ? (ws[0] + ws[1]) + (ws[2] + ws[3]) : 0.0f;
     }
   }
 }
 
-// dK, dV of the key tiles that two fused workgroups share: odd tile
-// t = 2*pr + 1 of each sequence, when tile t + 1 has rows, is plane 0 + plane 1
-// (in that order).  Blocks: (sequence, pair) x 8 blocks of 16 tokens, then
-// one per query head for dS_h (as in bwd_post_kernel).
-__global__ __launch_bounds__(256) void bwd_window_post_kernel(BwdArgs a, int plane_blocks, int npairs, int parts) {
+// dK, dV of the key tiles that two fused workgroups share: the last tile
+// t = n*u + n - 1 of unit u (n query tiles per workgroup), when tile t + 1
+// has rows, is plane 0 + plane 1 (in that order).  Blocks: (sequence, unit)
+// x 8 blocks of 16 tokens, then one per query head for dS_h (as in
+// bwd_post_kernel).
+__global__ __launch_bounds__(256) void bwd_window_post_kernel(BwdArgs a, int plane_blocks, int nunits, int parts) {
   const int tid = threadIdx.x;
   if ((int)blockIdx.x >= plane_blocks) {
     __shared__ float part[kFlatThreads];
@@ -1313,10 +1326,10 @@ __global__ __launch_bounds__(256) void bwd_window_post_kernel(BwdArgs a, int pla
     return;
   }
   const int unit = blockIdx.x >> 3, sub = blockIdx.x & 7;
-  const int seq = unit / npairs, pr = unit - seq * npairs;
+  const int seq = unit / nunits, u = unit - seq * nunits;
   const int bos = a.cu_seqlens[seq];
   const int L = a.cu_seqlens[seq + 1] - bos;
-  const int t = 2 * pr + 1;
+  const int t = a.fused_tiles * (u + 1) - 1;
   if (kFQ * (t + 1) >= L) return;  // no tile after t: the fused workgroup wrote it whole
   const int ks = a.num_kv_heads * kD;
   const long base = (long)(bos + kFQ * t + 16 * sub) * ks;  // 16 tokens, contiguous
@@ -1372,6 +1385,26 @@ bool bwd_window_fusable(int dtype, int head_dim, int window, int max_seqlen, int
          hq / hkv <= kFMaxGroup;
 }
 
+int fused_tiles_per_workgroup(int max_seqlen, int num_seqs, int hkv) {
+  // One fused workgroup per compute unit: a launch of W workgroups of n
+  // query tiles each takes about ceil(W / 256) rounds of n tiles.  The n with
+  // the fewest tiles per compute unit; of equal ones the largest (fewer key
+  // tiles shared between workgroups, so less partial-sum traffic).
+  constexpr long num_cus = 256;
+  const long tiles = ((long)max_seqlen + kFQ - 1) / kFQ;
+  int best = 1;
+  long best_cost = -1;
+  for (int n = 1; n <= kFMaxTiles; ++n) {
+    const long wgs = (tiles + n - 1) / n * num_seqs * hkv;
+    const long cost = (wgs + num_cus - 1) / num_cus * n;
+    if (best_cost < 0 || cost <= best_cost) {
+      best = n;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 int dkdv_heads_per_workgroup(int total_tokens, int max_seqlen, int hq, int hkv, int window, int dtype,
                              int head_dim) {
   constexpr long num_cus = 256;
@@ -1422,19 +1455,21 @@ hipError_t launch_bwd(const BwdArgs& args, int dtype, int max_seqlen, int num_se
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return e;
   if (a.fused) {
+    if (a.fused_tiles < 1 || a.fused_tiles > kFMaxTiles) return hipErrorInvalidValue;
     // One kernel in place of the dQ and dK/dV kernels (both event slots mark
     // its end), then the shared key tiles' planes and dS.
-    const int npairs = (max_seqlen + 2 * kFQ - 1) / (2 * kFQ);
+    const int span = a.fused_tiles * kFQ;  // query rows per workgroup
+    const int nunits = (max_seqlen + span - 1) / span;
     if (T > 0) {
-      const dim3 grid(npairs * a.num_kv_heads, num_seqs);
+      const dim3 grid(nunits * a.num_kv_heads, num_seqs);
       hipLaunchKernelGGL(bwd_window_kernel, grid, dim3(kFThreads), 0, stream, a);
       if ((e = after_launch("bwd_window_kernel", grid, dim3(kFThreads), split, stream)) != hipSuccess) return e;
     }
     if ((e = mark(1)) != hipSuccess) return e;
     if ((e = mark(2)) != hipSuccess) return e;
-    const int plane_blocks = T > 0 ? npairs * num_seqs * 8 : 0;
+    const int plane_blocks = T > 0 ? nunits * num_seqs * 8 : 0;
     hipLaunchKernelGGL(bwd_window_post_kernel, dim3(plane_blocks + Hq), dim3(kFlatThreads), 0, stream, a,
-                       plane_blocks, npairs, parts);
+                       plane_blocks, nunits, parts);
     if ((e = after_launch("bwd_window_post_kernel", dim3(plane_blocks + Hq), dim3(kFlatThreads), split, stream)) !=
         hipSuccess)
       return e;

@@ -51,6 +51,7 @@ struct BwdArgs {
   int dkdv_heads;      // query heads per dK/dV workgroup (divides Hq / Hkv)
   int dkdv_planes;     // float dK/dV partial-sum planes the post kernel adds (1: dK, dV written directly)
   int fused;           // 1: the fused short-window kernel replaces the dQ and dK/dV kernels
+  int fused_tiles;     // fused kernel: 128-row query tiles per workgroup (1..4)
   int dsink_tiles;     // fused kernel: 128-row tiles per (head, sequence) in the dS partial layout
   int heads_per_tile;  // query heads of one KV head packed in a dQ workgroup (divides Hq/Hkv and 32)
   int dq_tiles;        // query tiles per (sequence, head block) of the dQ grid (set by launch_bwd)
@@ -68,6 +69,9 @@ BwdWorkspace bwd_workspace_layout(int total_tokens, int hq, int hkv, int d, int 
 // head_dim 64, a window of 1..128 keys that cuts some sequence, and at most
 // 64 query heads per KV head.
 bool bwd_window_fusable(int dtype, int head_dim, int window, int max_seqlen, int hq, int hkv);
+// Query tiles per fused workgroup for a shape (1..4), sized for the 256
+// compute units of an MI355X.
+int fused_tiles_per_workgroup(int max_seqlen, int num_seqs, int hkv);
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int max_seqlen, int num_seqs, hipStream_t s);
 // Query heads per dK/dV workgroup for a problem shape (a divisor of Hq/Hkv),

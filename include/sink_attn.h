@@ -58,7 +58,10 @@
  *
  * Tuning.  For bf16, head_dim 64 and a window of 1..128 keys (shorter than
  * max_seqlen) the backward runs one fused kernel (see sink_attn_bwd_fused;
- * SINK_ATTN_BWD_FUSED=0 selects the separate kernels instead).  Otherwise
+ * SINK_ATTN_BWD_FUSED=0 selects the separate kernels instead), each
+ * workgroup taking 1 to 4 consecutive 128-row query tiles by the shape
+ * (SINK_ATTN_FUSED_TILES=n overrides; dQ, dK, dV and dS then differ only in
+ * float summation order).  Otherwise
  * the backward's dK/dV kernel gives each workgroup one 128-key tile
  * and some of the query heads that share its KV head: all of them when the
  * problem has enough parallel work (dK, dV written once), else fewer, each

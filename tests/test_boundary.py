@@ -123,6 +123,18 @@ def test_bad_dkdv_heads_override_is_rejected(monkeypatch, value):
     assert "SINK_ATTN_DKDV_HEADS" in _lib.load().sink_attn_last_error().decode()
 
 
+@pytest.mark.parametrize("value", ["0", "5", "-1", "abc"])
+def test_bad_fused_tiles_override_is_rejected(monkeypatch, value):
+    monkeypatch.setenv("SINK_ATTN_FUSED_TILES", value)
+    lib = _lib.load()
+    p = _good_params(window=64)  # bf16, d 64, a window shorter than the sequence: the fused backward
+    assert _bwd(p) == _lib.SINK_ATTN_ERR_INVALID_ARG
+    assert "SINK_ATTN_FUSED_TILES" in lib.sink_attn_last_error().decode()
+    assert lib.sink_attn_bwd_workspace_size(ctypes.byref(p)) == 0
+    # without a window cut the fused kernel is not used and the variable is not read
+    assert lib.sink_attn_bwd_workspace_size(ctypes.byref(_good_params())) > 0
+
+
 def test_null_params():
     lib = _lib.load()
     assert _fwd(None) == _lib.SINK_ATTN_ERR_INVALID_ARG

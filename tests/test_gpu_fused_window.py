@@ -1,7 +1,8 @@
 """Short sliding windows (1..128 keys, bf16, head_dim 64): the fused backward
-kernel (one workgroup per pair of 128-row query tiles and KV group; dQ, dK, dV and the
-sink gradient from one pass) and, with SINK_ATTN_BWD_FUSED=0, the dQ and
-dK/dV kernels, each against the float64 oracle on every element.
+kernel (one workgroup per run of 1 to 4 consecutive 128-row query tiles and
+KV group; dQ, dK, dV and the sink gradient from one pass) and, with
+SINK_ATTN_BWD_FUSED=0, the dQ and dK/dV kernels, each against the float64
+oracle on every element.
 
 Shapes cover one-row and one-step tiles, a last tile of one row, windows of
 1, 63, 64, 127 and 128 keys, empty and mixed-length sequences, query heads
@@ -55,6 +56,26 @@ def test_short_window_matches_oracle(monkeypatch, path, lengths, hq, hkv, window
     check_full(gpu, _oracle_full(inp, scale, window), label)
     if sinks == "minus_inf":
         assert np.all(gpu["ds"] == 0.0)
+
+
+@pytest.mark.parametrize("tiles", ["1", "2", "3", "4"])
+@pytest.mark.parametrize("lengths,hq,hkv,window", [
+    ((1000, 257, 130), 8, 2, 128),  # 8, 3 and 2 tiles: ragged last runs, a last tile of one or two rows
+    ((640, 1), 4, 1, 100),          # 5 tiles, then a one-token sequence
+    ((900,), 16, 2, 33),
+])
+def test_fused_tiles_per_workgroup_match_oracle(monkeypatch, tiles, lengths, hq, hkv, window):
+    """Every number of query tiles per fused workgroup (SINK_ATTN_FUSED_TILES)
+    against the oracle: the key tiles shared between runs go through the two
+    float planes, the others are written whole."""
+    monkeypatch.setenv("SINK_ATTN_BWD_FUSED", "1")
+    monkeypatch.setenv("SINK_ATTN_FUSED_TILES", tiles)
+    label = f"fused tiles {tiles} L={lengths} hq={hq} hkv={hkv} W={window}"
+    say("case", label)
+    w = custom_workload(lengths, hq, hkv, 64, window, "bf16")
+    inp = make_inputs(w, seed=sum(lengths) + int(tiles))
+    gpu = run_gpu(inp, w.max_seqlen, w.softmax_scale, window)
+    check_full(gpu, _oracle_full(inp, w.softmax_scale, window), label)
 
 
 def test_fused_and_two_kernel_paths_agree(monkeypatch):
