@@ -8,10 +8,11 @@
 // One workgroup = one sequence and 32 columns of (query row, query head) per
 // wavefront (four wavefronts, or eight for long sequences): hp heads of one
 // KV group g times consecutive rows (hp = 1: rows of one head).  Keys/values
-// of g stream through a two-stage LDS ring in tiles of 64 keys (direct
-// global->LDS loads into XOR-swizzled rows, issued one tile ahead; one
-// barrier per tile; the small ring leaves room for four wavefronts per SIMD),
-// each tile loaded once for all hp heads.  Per tile a wavefront computes the
+// of g stream through a two-stage LDS ring in tiles of 64 keys, or 32 for
+// sliding windows of at most 128 keys (direct global->LDS loads into
+// XOR-swizzled rows, issued one tile ahead; one barrier per tile; the small
+// ring leaves room for four wavefronts per SIMD), each tile loaded once for
+// all hp heads.  Per tile a wavefront computes the
 // transposed score block S^T = K Q^T on the matrix cores, so each lane owns
 // one (row, head) column and its softmax statistics stay in the lane; the
 // online softmax starts from the sink (reference max m = S_h,
@@ -21,7 +22,8 @@
 // writes O = acc / l and LSE = m + ln(l) (natural log, sink included).
 //
 // A row's reference max m is only raised when the tile's exponentials at the
-// old m sum to 2^12 or more over either half of the row (32 keys); otherwise
+// old m sum to 2^12 or more over either half of the row's tile keys (the
+// 32 or 16 keys one lane of the pair holds); otherwise
 // the tile is used at the old m.  The result is the same softmax: m cancels
 // between O's numerator and l.  The common case needs no row maximum: the
 // exponentials and their half-row sums are formed first, and only a
@@ -40,7 +42,7 @@ namespace sinkattn {
 
 namespace {
 
-constexpr int kBN = 64;   // keys per LDS tile
+constexpr int kBN = 64;   // keys per LDS tile (32 for windows of at most 128 keys)
 constexpr int kD = 64;    // padded head dimension
 constexpr float kHalfSumLimit = 4096.0f;  // a half row's sum over a tile (old m) that raises m
 
@@ -48,23 +50,36 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 
+template <int kTK>
 struct __attribute__((aligned(16))) KVStage {
-  bf16 k[kBN * kD];  // K tile, swizzled [key][d]
-  bf16 v[kBN * kD];  // V tile, swizzled [key][d]
+  bf16 k[kTK * kD];  // K tile, swizzled [key][d]
+  bf16 v[kTK * kD];  // V tile, swizzled [key][d]
 };
 
 // kPaged: keys and values come from a paged cache (new query rows of a
 // sequence at the end of its cached context); otherwise they are the packed
 // tokens of the sequence itself (query row i at position i).  The arithmetic
 // per query row is the same in both, so a row gets the same bits either way.
-template <typename TIn, bool kDirect, bool kPaged, int kWaves>
+// kTK: keys per tile (64; 32 for windows of at most 128 keys, where a
+// 64-key tile would hold a dead or masked half: 5 blocks of 32 keys, 2 of
+// them masked, instead of 6 and 4 per 16-row group at window 128).  The
+// training and paged forwards pick kTK by the same rule, so their rows stay
+// bitwise equal.
+template <typename TIn, bool kDirect, bool kPaged, int kWaves, int kTK>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDirect ? 4 : 2))) void fwd_kernel(FwdArgs a) {
   constexpr int kBM = 32 * kWaves;      // (row, head) columns per workgroup
   constexpr int kThreads = 64 * kWaves;
-  constexpr int kBlk = 8 / kWaves;       // 8-row blocks of a tile each wavefront stages
+  constexpr int kBlk = kTK / 8 / kWaves;  // 8-row blocks of a tile each wavefront stages
+  constexpr int kNB = kTK / 32;           // 32-key blocks per tile
+  constexpr int kNC = kTK / 16;           // 16-key chunks per tile
+  static_assert(kBlk >= 1 && (kTK == 32 || kTK == 64), "tile shape");
+  typedef KVStage<kTK> Stage;
   // Two-stage ring; the loop is unrolled by two, so every access names its
   // stage at compile time and LDS addresses fold into instruction offsets.
-  __shared__ KVStage stage[2];
+  // (With 32-key tiles the two stages are exactly the 16 KB the epilogue
+  // stages O through.)
+  __shared__ Stage stage[2];
+  static_assert(!kDirect || sizeof(stage) >= (size_t)kWaves * 32 * kD * sizeof(bf16), "epilogue staging");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
@@ -104,7 +119,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
   const int window = a.window;
   const int kend = min(kvlen, qoff + min(L, q0 + rows));
   const int kbeg = window > 0 ? max(0, qoff + q0 - window + 1) : 0;
-  const int t0 = kbeg / kBN, t1 = (kend + kBN - 1) / kBN;  // t0 < t1 unless a paged length was bad
+  const int t0 = kbeg / kTK, t1 = (kend + kTK - 1) / kTK;  // t0 < t1 unless a paged length was bad
 
   // Row offset (in keys) of tile t within the key/value tensors: the packed
   // sequence, or the tile's page of the cache (a page holds a whole number
@@ -114,7 +129,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
   const int* __restrict__ bt = kPaged ? a.block_table + (long)seq * a.max_blocks_per_seq : nullptr;
   int pid_next = 0, k0_next = 0;  // paged: raw page id and first key of the next tile to prefetch
   auto load_page = [&](int t) {
-    k0_next = min(t, t1 - 1) * kBN;
+    k0_next = min(t, t1 - 1) * kTK;
     pid_next = bt[k0_next / a.page_size];
   };
   auto page_row = [&]() -> long {
@@ -136,14 +151,14 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
   // Prefetch key tile t (clamped to the last tile) into `st`; on the direct
   // path exactly 4 VMEM instructions per wavefront.  Rows past the keys of
   // the sequence repeat its last key (they are masked).
-  auto prefetch = [&](int t, KVStage& st) {
-    const int k0 = min(t, t1 - 1) * kBN;
+  auto prefetch = [&](int t, Stage& st) {
+    const int k0 = min(t, t1 - 1) * kTK;
     const long prow = kPaged ? page_row() : (long)k0;  // row of the tile's first key
     const int rem = kvlen - k0;                        // keys from the tile's first on
     if constexpr (kDirect) {
       const bf16* kb = (const bf16*)Kg + prow * ks;
       const bf16* vb = (const bf16*)Vg + prow * ks;
-      if (rem >= kBN) {
+      if (rem >= kTK) {
         if constexpr (kPaged) {
           // a cache is read once per KV head: non-temporal
 #pragma unroll
@@ -170,8 +185,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
         for (int i = 0; i < kBlk; ++i) lds_dma16_s(cl[i], vb, st.v + 512 * (kBlk * w + i));
       }
     } else {
-      stage_regs<kBN, TIn, kThreads>(st.k, Kg + prow * ks, 0, rem, ks, hd, tid);
-      stage_regs<kBN, TIn, kThreads>(st.v, Vg + prow * ks, 0, rem, ks, hd, tid);
+      stage_regs<kTK, TIn, kThreads>(st.k, Kg + prow * ks, 0, rem, ks, hd, tid);
+      stage_regs<kTK, TIn, kThreads>(st.v, Vg + prow * ks, 0, rem, ks, hd, tid);
     }
     if constexpr (kPaged) load_page(t + 1);
   };
@@ -219,23 +234,23 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
 
   // One key tile: consume `st`, prefetch the next tile into `nx` (the stage
   // consumed one tile earlier).
-  auto tile = [&](int t, const KVStage& st, KVStage& nx) {
+  auto tile = [&](int t, const Stage& st, Stage& nx) {
     // This wavefront's part of tile t has landed; the barrier makes every
     // part visible and ends all reads of `nx` (tile t-1).
     if constexpr (kDirect) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
     prefetch(t + 1, nx);
     issue_fence();
-    const int kb = t * kBN;
+    const int kb = t * kTK;
     if (!live || kb > wq_hi) return;                             // no rows, or all keys after all rows
-    if (window > 0 && wq_lo - (kb + kBN - 1) >= window) return;  // all keys left of window
+    if (window > 0 && wq_lo - (kb + kTK - 1) >= window) return;  // all keys left of window
 
     // S^T = K Q^T - m for two 32-key blocks (log2 domain; the accumulators
     // start from -m); register r of block blk holds key
     // kb + 32*blk + 16*(r/8) + 8*h2 + r%8 (A rows permuted).  Hidden scores
     // are -inf.
-    const bool need_mask = (kb + kBN - 1 > wq_lo) || (window > 0 && wq_hi - kb >= window);
-    f32x16 s[2];
+    const bool need_mask = (kb + kTK - 1 > wq_lo) || (window > 0 && wq_hi - kb >= window);
+    f32x16 s[kNB];
     auto scores = [&]() {
       // Built per tile (a loop-long copy would cost a wave of occupancy), by
       // 64-bit moves of a pair holding -m twice.
@@ -251,7 +266,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
       }
       const f32x16 negm = __builtin_bit_cast(f32x16, negm2);
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
+      for (int blk = 0; blk < kNB; ++blk) {
         const int kr = krow_base + 32 * blk;
         s[blk] = mfma32(frag_row(st.k, kr, 8 * h2), qf[0], negm);
 #pragma unroll
@@ -262,7 +277,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
         const int hi = qpos + 1 - kb - 8 * h2;
         const int lo = window > 0 ? hi - window : -0x7fffffff;
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
+        for (int blk = 0; blk < kNB; ++blk) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int idx = 32 * blk + 16 * (r >> 3) + (r & 7);
@@ -274,12 +289,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
     // P = exp2(S * scale * log2 e - m) as P^T fragments (chunk c covers keys
     // 16c .. 16c+15 of the tile); this half row's sum adds the rounded values,
     // two per dot product, in two chains.
-    bf16x8 pf[4];
+    bf16x8 pf[kNC];
     float ls;
     auto exponentiate = [&]() {
       float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < kNC; ++c) {
         f32x8 v;
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = fast_exp2(s[c >> 1][8 * (c & 1) + i]);
@@ -313,7 +328,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
         // this compiler's bit cast of a vector element reads element 0.)
         u16x2 mx2 = {0, 0};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < kNC; ++c) {
           const u32x4 d = __builtin_bit_cast(u32x4, pf[c]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -336,9 +351,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           mx0 = __builtin_fmaxf(__builtin_fmaxf(mx0, s[0][r]), s[0][r + 1]);
-          mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, s[1][r]), s[1][r + 1]);
+          if constexpr (kNB > 1) mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, s[kNB - 1][r]), s[kNB - 1][r + 1]);
         }
-        float mx = __builtin_fmaxf(mx0, mx1);
+        float mx = kNB > 1 ? __builtin_fmaxf(mx0, mx1) : mx0;
         mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
         const bool first = m == -__builtin_inff();
         const bool raise = exact && mx > -__builtin_inff();
@@ -352,8 +367,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
         for (int i = 0; i < 16; ++i) {
           o[0][i] *= alpha;
           o[1][i] *= alpha;
-          s[0][i] -= shift;
-          s[1][i] -= shift;
+#pragma unroll
+          for (int blk = 0; blk < kNB; ++blk) s[blk][i] -= shift;
         }
         m = raise ? (first ? mx : m + mx) : m;
         nm = (m == -__builtin_inff()) ? 0.0f : -m;
@@ -375,7 +390,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
         const short sub = (short)(kk << 7);
         const i16x2 sub2 = {sub, sub}, zero2 = {0, 0};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < kNC; ++c) {
           u32x4 d = __builtin_bit_cast(u32x4, pf[c]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -394,7 +409,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[db] = mfma32(frag_tr_swz(st.v, 16 * c, 32 * db, lane), pf[c], o[db]);
+      for (int c = 0; c < kNC; ++c) o[db] = mfma32(frag_tr_swz(st.v, 16 * c, 32 * db, lane), pf[c], o[db]);
     }
   };
   for (int t = t0; t < t1; t += 2) {
@@ -452,7 +467,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(kDi
   }
 }
 
-template <int kWaves>
+template <int kWaves, int kTK>
 hipError_t launch_fwd_waves(const FwdArgs& a, bool direct, int dtype, int max_seqlen, int num_seqs,
                             hipStream_t stream) {
   FwdArgs b = a;
@@ -462,21 +477,22 @@ hipError_t launch_fwd_waves(const FwdArgs& a, bool direct, int dtype, int max_se
   const dim3 grid(b.tiles * (a.num_q_heads / hp), num_seqs), block(64 * kWaves);
   if (a.block_table) {
     if (direct)
-      hipLaunchKernelGGL((fwd_kernel<bf16, true, true, kWaves>), grid, block, 0, stream, b);
+      hipLaunchKernelGGL((fwd_kernel<bf16, true, true, kWaves, kTK>), grid, block, 0, stream, b);
     else if (dtype == 0)
-      hipLaunchKernelGGL((fwd_kernel<bf16, false, true, kWaves>), grid, block, 0, stream, b);
+      hipLaunchKernelGGL((fwd_kernel<bf16, false, true, kWaves, kTK>), grid, block, 0, stream, b);
     else
-      hipLaunchKernelGGL((fwd_kernel<float, false, true, kWaves>), grid, block, 0, stream, b);
+      hipLaunchKernelGGL((fwd_kernel<float, false, true, kWaves, kTK>), grid, block, 0, stream, b);
   } else {
     if (direct)
-      hipLaunchKernelGGL((fwd_kernel<bf16, true, false, kWaves>), grid, block, 0, stream, b);
+      hipLaunchKernelGGL((fwd_kernel<bf16, true, false, kWaves, kTK>), grid, block, 0, stream, b);
     else if (dtype == 0)
-      hipLaunchKernelGGL((fwd_kernel<bf16, false, false, kWaves>), grid, block, 0, stream, b);
+      hipLaunchKernelGGL((fwd_kernel<bf16, false, false, kWaves, kTK>), grid, block, 0, stream, b);
     else
-      hipLaunchKernelGGL((fwd_kernel<float, false, false, kWaves>), grid, block, 0, stream, b);
+      hipLaunchKernelGGL((fwd_kernel<float, false, false, kWaves, kTK>), grid, block, 0, stream, b);
   }
-  char split[64];
-  std::snprintf(split, sizeof(split), "paged=%d pack_heads=%d waves=%d", a.block_table ? 1 : 0, hp, kWaves);
+  char split[80];
+  std::snprintf(split, sizeof(split), "paged=%d pack_heads=%d waves=%d tile_keys=%d", a.block_table ? 1 : 0, hp,
+                kWaves, kTK);
   return after_launch(direct ? "fwd_kernel<direct>" : "fwd_kernel<generic>", grid, block, split, stream);
 }
 
@@ -489,8 +505,13 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int max_seqlen, int num_seqs,
   // longer fit in L2 (3 % faster at 65536 tokens); below that, four
   // wavefronts per workgroup balance better (4 % faster at 4096).  Each
   // lane's arithmetic is the same either way.
-  if (!a.block_table && max_seqlen >= 16384) return launch_fwd_waves<8>(a, direct, dtype, max_seqlen, num_seqs, stream);
-  return launch_fwd_waves<4>(a, direct, dtype, max_seqlen, num_seqs, stream);
+  // Windows of at most 128 keys take 32-key tiles (four wavefronts), in the
+  // training and the paged forward alike, so a row's arithmetic does not
+  // depend on which of them computes it.
+  if (a.window >= 1 && a.window <= 128) return launch_fwd_waves<4, 32>(a, direct, dtype, max_seqlen, num_seqs, stream);
+  if (!a.block_table && max_seqlen >= 16384)
+    return launch_fwd_waves<8, kBN>(a, direct, dtype, max_seqlen, num_seqs, stream);
+  return launch_fwd_waves<4, kBN>(a, direct, dtype, max_seqlen, num_seqs, stream);
 }
 
 }  // namespace sinkattn
