@@ -1306,8 +1306,9 @@ __global__ __launch_bounds__(kFThreads) void bwd_window_kernel(BwdArgs a) {
 // dK, dV of the key tiles that two fused workgroups share: the last tile
 // t = n*u + n - 1 of unit u (n query tiles per workgroup), when tile t + 1
 // has rows, is plane 0 + plane 1 (in that order).  Blocks: (sequence, unit)
-// x 8 blocks of 16 tokens, then one per query head for dS_h (as in
-// bwd_post_kernel).
+// x 8 Hkv blocks, one 8-value chunk of the tile's dK or dV per thread (so
+// every load of the pass is in flight at once), then one per query head for
+// dS_h (as in bwd_post_kernel).
 __global__ __launch_bounds__(256) void bwd_window_post_kernel(BwdArgs a, int plane_blocks, int nunits, int parts) {
   const int tid = threadIdx.x;
   if ((int)blockIdx.x >= plane_blocks) {
@@ -1325,23 +1326,25 @@ __global__ __launch_bounds__(256) void bwd_window_post_kernel(BwdArgs a, int pla
     if (tid == 0) a.dsinks[h] = part[0];
     return;
   }
-  const int unit = blockIdx.x >> 3, sub = blockIdx.x & 7;
+  // A tile's dK (then dV) is kFQ * ks contiguous values: 16 ks chunks of 8
+  // each, 32 ks for both = 8 Hkv blocks of kFlatThreads chunks.
+  const int per_unit = 8 * a.num_kv_heads;
+  const int unit = blockIdx.x / per_unit, sub = blockIdx.x - unit * per_unit;
   const int seq = unit / nunits, u = unit - seq * nunits;
   const int bos = a.cu_seqlens[seq];
   const int L = a.cu_seqlens[seq + 1] - bos;
   const int t = a.fused_tiles * (u + 1) - 1;
   if (kFQ * (t + 1) >= L) return;  // no tile after t: the fused workgroup wrote it whole
   const int ks = a.num_kv_heads * kD;
-  const long base = (long)(bos + kFQ * t + 16 * sub) * ks;  // 16 tokens, contiguous
+  const long base = (long)(bos + kFQ * t) * ks;  // the tile's 128 tokens, contiguous
   const long plane = (long)a.total_tokens * ks;
-  const int chunks = 16 * ks / 8;
-  for (int c = tid; c < 2 * chunks; c += kFlatThreads) {
-    const bool is_k = c < chunks;
-    const long e = base + 8L * (is_k ? c : c - chunks);
-    const float* src = (is_k ? a.dk_part : a.dv_part) + e;
-    const f32x8 acc = load8f(src) + load8f(src + plane);
-    store8((bf16*)(is_k ? a.dk : a.dv) + e, acc);
-  }
+  const int chunks = 16 * ks;                     // per tensor
+  const int c = sub * kFlatThreads + tid;         // < 2 * chunks
+  const bool is_k = c < chunks;
+  const long e = base + 8L * (is_k ? c : c - chunks);
+  const float* src = (is_k ? a.dk_part : a.dv_part) + e;
+  const f32x8 acc = load8f(src) + load8f(src + plane);
+  store8((bf16*)(is_k ? a.dk : a.dv) + e, acc);
 }
 
 int flat_blocks(long work_items) {
@@ -1467,7 +1470,7 @@ hipError_t launch_bwd(const BwdArgs& args, int dtype, int max_seqlen, int num_se
     }
     if ((e = mark(1)) != hipSuccess) return e;
     if ((e = mark(2)) != hipSuccess) return e;
-    const int plane_blocks = T > 0 ? nunits * num_seqs * 8 : 0;
+    const int plane_blocks = T > 0 ? nunits * num_seqs * 8 * a.num_kv_heads : 0;
     hipLaunchKernelGGL(bwd_window_post_kernel, dim3(plane_blocks + Hq), dim3(kFlatThreads), 0, stream, a,
                        plane_blocks, nunits, parts);
     if ((e = after_launch("bwd_window_post_kernel", dim3(plane_blocks + Hq), dim3(kFlatThreads), split, stream)) !=
