@@ -22,6 +22,10 @@ CASES = [
     ((333, 129), (100, 2), 4, 1, 64, 48, "bf16", 64),
     ((200, 70), (7, 70), 4, 2, 40, 0, "f32", 64),
     ((190, 64), (33, 64), 4, 2, 16, 0, "bf16", 256),
+    # both sides of the 32-key / 64-key tile boundary at window 128
+    ((700, 300), (1, 120), 16, 2, 64, 128, "bf16", 64),
+    ((700, 300), (1, 120), 16, 2, 64, 129, "bf16", 128),
+    ((500, 90), (60, 1), 4, 2, 40, 32, "f32", 64),
 ]
 
 

@@ -57,6 +57,15 @@ SMALL = [
     ((257,), 4, 2, 40, 0, "f32", "normal"),
     ((200, 3), 4, 4, 64, 9, "f32", "mixed"),
     ((520,), 16, 2, 64, 0, "bf16", "normal"),
+    # windows of at most 128 keys run the forward on 32-key tiles, longer
+    # ones on 64-key tiles: both sides of that boundary and of one tile
+    ((301,), 8, 1, 64, 31, "bf16", "normal"),
+    ((301,), 8, 1, 64, 32, "bf16", "mixed"),
+    ((301,), 8, 1, 64, 33, "bf16", "normal"),
+    ((260, 77), 16, 2, 64, 127, "bf16", "normal"),
+    ((260,), 16, 2, 64, 129, "bf16", "normal"),
+    ((190,), 4, 2, 40, 128, "f32", "normal"),
+    ((190,), 4, 2, 32, 64, "bf16", "minus_inf"),
     # groups that are not a power of two (3 and 6 query heads per KV head)
     ((260, 33), 6, 2, 64, 0, "bf16", "normal"),
     ((300,), 12, 2, 64, 50, "bf16", "mixed"),
@@ -89,6 +98,15 @@ GROUPED = [
     ((129, 70), 4, 2, 16, 0, "bf16", "normal"),
     ((200, 3), 4, 2, 40, 9, "f32", "mixed"),
     ((520,), 16, 2, 64, 0, "bf16", "normal"),
+    # windows of at most 128 keys run the forward on 32-key tiles, longer
+    # ones on 64-key tiles: both sides of that boundary and of one tile
+    ((301,), 8, 1, 64, 31, "bf16", "normal"),
+    ((301,), 8, 1, 64, 32, "bf16", "mixed"),
+    ((301,), 8, 1, 64, 33, "bf16", "normal"),
+    ((260, 77), 16, 2, 64, 127, "bf16", "normal"),
+    ((260,), 16, 2, 64, 129, "bf16", "normal"),
+    ((190,), 4, 2, 40, 128, "f32", "normal"),
+    ((190,), 4, 2, 32, 64, "bf16", "minus_inf"),
 ]
 
 
