@@ -120,6 +120,32 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, torch.Tens
     return out
 
 
+def make_inputs_device(w: Workload, seed: int, device: str) -> Dict[str, torch.Tensor]:
+    """Inputs of workload ``w`` drawn on the GPU (a host draw of several
+    gigabytes takes minutes).
+
+    One ``torch.Generator(device)`` seeded with ``seed``: q, k, v, dout
+    ``randn`` float32 (drawn in chunks of tokens, cast to the workload's
+    dtype), then sinks ``randn``; cu_seqlens from the lengths.  Slices copied
+    to the host are the oracle's inputs.
+    """
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    T, hq, hkv, d = w.total_tokens, w.num_q_heads, w.num_kv_heads, w.head_dim
+    out = {}
+    for name, heads in (("q", hq), ("k", hkv), ("v", hkv), ("dout", hq)):
+        x = torch.empty((T, heads, d), dtype=tdt, device=device)
+        chunk = max(1, (1 << 26) // (heads * d))  # bound the float32 temporary
+        for r in range(0, T, chunk):
+            n = min(chunk, T - r)
+            x[r:r + n] = torch.randn((n, heads, d), generator=gen, device=device).to(tdt)
+        out[name] = x
+    out["sinks"] = torch.randn((hq,), generator=gen, device=device)
+    out["cu_seqlens"] = torch.from_numpy(w.cu_seqlens()).to(device)
+    return out
+
+
 def make_paged(inputs: Dict[str, torch.Tensor], q_lens: Sequence[int], page_size: int, seed: int,
                spare_pages: int = 3, max_blocks_extra: int = 1) -> Dict[str, torch.Tensor]:
     """Paged-cache view of packed ``inputs`` (from ``make_inputs``).

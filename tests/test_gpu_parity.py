@@ -11,9 +11,9 @@ import pytest
 import torch
 
 import oracle
-from synthetic.workloads import WORKLOADS, custom_workload, make_inputs
-from tests.parity_util import (TOL_DS, TOL_GRAD, TOL_LSE, TOL_O, check_full, max_abs, record_errors,
-                               rel_l2, run_gpu, say)
+from synthetic.workloads import WORKLOADS, custom_workload, make_inputs, make_inputs_device
+from tests.parity_util import (TOL_DS, TOL_GRAD, TOL_LSE, TOL_O, check_full, f64, max_abs,
+                               record_errors, rel_l2, run_gpu, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -396,6 +396,50 @@ def _ds_self_consistency(gpu, inp):
     dvec = np.einsum("thd,thd->ht", do, gpu["o"])
     want = -np.sum(np.exp(s[:, None] - gpu["lse"]) * dvec, axis=1)
     return rel_l2(gpu["ds"], want)
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_maximum_size_batch_against_oracle(window):
+    """The largest batch the boundary accepts at the GPT-OSS head shape:
+    T * Hq * d = 2^31 - 4096 elements (127 sequences of 4096 tokens and one
+    of 4095, 64 query heads, 8 KV heads, d = 64), where element offsets into
+    Q, O, dO and dQ come within one row of 2^31.  The last sequence's last KV
+    group (the largest offsets) against the oracle, every row and key; dS of
+    every head through the identity dS_h = -sum_i exp(S_h - LSE_i) dO_i . O_i
+    on the GPU's own O and LSE (float64 on the device)."""
+    import attention_sink_fwd_amd as sa
+
+    lengths = (4096,) * 127 + (4095,)
+    w = custom_workload(lengths, 64, 8, 64, window, "bf16", name="max_size")
+    assert w.total_tokens * 64 * 64 == 2 ** 31 - 4096
+    say("case maximum size", w.total_tokens, "tokens, window", window)
+    dev = "cuda:0"
+    d = make_inputs_device(w, seed=31 + window, device=dev)
+    o, lse = sa.sink_attn_fwd(d["q"], d["k"], d["v"], d["sinks"], d["cu_seqlens"], w.max_seqlen,
+                              w.softmax_scale, window)
+    dq, dk, dv, ds = sa.sink_attn_bwd(d["q"], d["k"], d["v"], d["sinks"], o, lse, d["dout"],
+                                      d["cu_seqlens"], w.max_seqlen, w.softmax_scale, window)
+    torch.cuda.synchronize()
+    for name, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv), ("ds", ds)):
+        assert bool(torch.isfinite(t).all()), name
+    # dS of every head from the GPU's own O and LSE, chunked over tokens.
+    want = torch.zeros(64, dtype=torch.float64, device=dev)
+    s64 = d["sinks"].double()
+    for r in range(0, w.total_tokens, 1 << 16):
+        e = min(r + (1 << 16), w.total_tokens)
+        dvec = (d["dout"][r:e].double() * o[r:e].double()).sum(-1)  # [rows, Hq]
+        want -= (torch.exp(s64[None, :] - lse[:, r:e].double().T) * dvec).sum(0)
+    e_ds = rel_l2(ds.double().cpu().numpy(), want.cpu().numpy())
+    # The last sequence, KV group 7, against the oracle.
+    b = w.total_tokens - lengths[-1]
+    host = {n: d[n][b:].cpu() for n in ("q", "k", "v", "dout")}
+    host["sinks"], host["cu_seqlens"] = d["sinks"].cpu(), torch.tensor([0, lengths[-1]], dtype=torch.int32)
+    gpu = {"o": f64(o[b:]), "lse": f64(lse[:, b:]), "dq": f64(dq[b:]), "dk": f64(dk[b:]),
+           "dv": f64(dv[b:]), "ds": f64(ds)}
+    refs = _kv_group_reference(host, w.softmax_scale, window, 7)
+    errs = _check_group(gpu, refs, 7, f"maximum size, window {window}")
+    say(f"  dS identity over all heads: {e_ds:.2e}")
+    assert e_ds <= TOL_DS
 
 
 @pytest.mark.parametrize("wid", [2, 3])
